@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and smoke().
+
+This module draws random numbers and nothing else: it holds none of the
+arithmetic of the method (no logits, softmax, attention or gradients), so
+that the CPU oracle and the HIP path can both be fed from it without sharing
+any computation.
+
+Every generator uses a CPU ``torch.Generator`` seeded explicitly, draws in a
+fixed order, and returns CPU tensors.  In bf16 mode a tensor is drawn in
+fp32 and rounded to bf16 with round-to-nearest-even (``.to(torch.bfloat16)``);
+the oracle then receives those bf16 values upcast exactly to fp64, so input
+rounding never counts as error.
+
+Workload shapes follow the long-sequence SFT / GRPO / DPO training the
+StreamBP pages describe (8B-class decoder: hidden 4096, vocab 128256, 32
+query / 8 key-value heads of width 128, MLP width 14336; and a 3584 / 152064
+variant).  No dataset or trained weight is used: the distributions stand in
+for post-norm hidden states and freshly initialised weights.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(g: torch.Generator, shape, std: float, dtype: torch.dtype) -> torch.Tensor:
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+# ---------------------------------------------------------------------------
+# LM head + cross-entropy inputs
+# ---------------------------------------------------------------------------
+@dataclass
+class LMHeadInputs:
+    H: torch.Tensor            # [T, d]   hidden states (dtype)
+    W: torch.Tensor            # [V, d]   LM-head weight, [out, in] (dtype)
+    targets: torch.Tensor      # [T]      int32, < 0 means "ignored"
+    weights: Optional[torch.Tensor]  # [T] fp32 per-token weights or None
+
+
+def lmhead_inputs(T: int, d: int, V: int, dtype: str = "bf16", seed: int = 0,
+                  h_std: float = 1.0, w_std: Optional[float] = None,
+                  n_seq: int = 1, masked_frac: float = 0.0,
+                  weighted: bool = False, ignore_frac: float = 0.0) -> LMHeadInputs:
+    """Draw order: H, W, targets, per-sequence weights, random ignore mask.
+
+    ``masked_frac`` masks the first fraction of every one of ``n_seq`` packed
+    sequences (target = -1), as a prompt would be in SFT/GRPO.  ``weighted``
+    gives each sequence one N(0,1) weight repeated over its tokens (a
+    sequence-level advantage).  ``ignore_frac`` additionally ignores a random
+    subset of tokens (edge-case tests).
+    """
+    g = _gen(seed)
+    tdt = DTYPES[dtype]
+    if w_std is None:
+        w_std = d ** -0.5
+    H = _normal(g, (T, d), h_std, tdt)
+    W = _normal(g, (V, d), w_std, tdt)
+    targets = torch.randint(0, V, (T,), generator=g, dtype=torch.int64).to(torch.int32)
+    weights = None
+    if n_seq < 1 or T % n_seq != 0:
+        raise ValueError("T must split into n_seq equal sequences")
+    L = T // n_seq
+    if weighted:
+        w_seq = torch.randn(n_seq, generator=g, dtype=torch.float32)
+        weights = w_seq.repeat_interleave(L).contiguous()
+    if masked_frac > 0.0:
+        m = int(round(L * masked_frac))
+        for s in range(n_seq):
+            targets[s * L: s * L + m] = -1
+    if ignore_frac > 0.0:
+        drop = torch.rand(T, generator=g) < ignore_frac
+        targets[drop] = -1
+    return LMHeadInputs(H, W, targets, weights)
+
+
+# ---------------------------------------------------------------------------
+# Causal GQA attention inputs, token-major [B, T, heads, dh]
+# ---------------------------------------------------------------------------
+@dataclass
+class AttnInputs:
+    Q: torch.Tensor   # [B, T, Hq, dh]
+    K: torch.Tensor   # [B, T, Hkv, dh]
+    V: torch.Tensor   # [B, T, Hkv, dh]
+    dO: torch.Tensor  # [B, T, Hq, dh]
+
+
+def attn_inputs(B: int, T: int, Hq: int, Hkv: int, dh: int, dtype: str = "bf16",
+                seed: int = 0, std: float = 1.0) -> AttnInputs:
+    """Draw order: Q, K, V, dO, each N(0, std^2)."""
+    g = _gen(seed)
+    tdt = DTYPES[dtype]
+    Q = _normal(g, (B, T, Hq, dh), std, tdt)
+    K = _normal(g, (B, T, Hkv, dh), std, tdt)
+    V = _normal(g, (B, T, Hkv, dh), std, tdt)
+    dO = _normal(g, (B, T, Hq, dh), std, tdt)
+    return AttnInputs(Q, K, V, dO)
+
+
+# ---------------------------------------------------------------------------
+# Decoder layer inputs (pre-norm: RMSNorm -> GQA attention -> RMSNorm -> SwiGLU)
+# ---------------------------------------------------------------------------
+LAYER_WEIGHT_NAMES = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W3", "W2")
+
+
+@dataclass
+class LayerInputs:
+    x: torch.Tensor     # [T, d]
+    dy: torch.Tensor    # [T, d]
+    w: dict             # name -> tensor, linear weights [out, in], gains [d]
+    Hq: int
+    Hkv: int
+    dh: int
+    F: int
+    eps: float
+
+
+def layer_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int,
+                 dtype: str = "bf16", seed: int = 0, w_std: float = 0.02,
+                 gain_std: float = 0.0, eps: float = 1e-6,
+                 x_std: float = 1.0, dy_std: float = 1.0) -> LayerInputs:
+    """Draw order: x, Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2, dy.
+
+    Gains are exactly one when ``gain_std`` is 0 (the benchmark setting) and
+    1 + N(0, gain_std^2) otherwise (to exercise the gain gradients).
+    """
+    g = _gen(seed)
+    tdt = DTYPES[dtype]
+    x = _normal(g, (T, d), x_std, tdt)
+    shapes = {"Wq": (Hq * dh, d), "Wk": (Hkv * dh, d), "Wv": (Hkv * dh, d),
+              "Wo": (d, Hq * dh), "W1": (F, d), "W3": (F, d), "W2": (d, F)}
+    w = {}
+    for name in ("Wq", "Wk", "Wv", "Wo", "W1", "W3", "W2"):
+        w[name] = _normal(g, shapes[name], w_std, tdt)
+    for name in ("g1", "g2"):
+        gg = torch.ones(d, dtype=torch.float32)
+        if gain_std > 0.0:
+            gg = gg + gain_std * torch.randn(d, generator=g, dtype=torch.float32)
+        w[name] = gg.to(tdt)
+    dy = _normal(g, (T, d), dy_std, tdt)
+    return LayerInputs(x, dy, w, Hq, Hkv, dh, F, eps)
+
+
+def to_f64(t: Optional[torch.Tensor]):
+    """Exact upcast of a CPU tensor to a float64 numpy array (None passes)."""
+    if t is None:
+        return None
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (index 0..4), seed = 1000 + index.
+# ---------------------------------------------------------------------------
+WORKLOADS = {
+    0: dict(kind="lmhead", name="lmhead_ce_f32_T256_d64_V512_D4",
+            T=256, d=64, V=512, D=4, dtype="f32"),
+    1: dict(kind="lmhead", name="lmhead_ce_bf16_T32768_d4096_V128256_D16",
+            T=32768, d=4096, V=128256, D=16, dtype="bf16", w_std=0.02),
+    2: dict(kind="attn", name="attn_bwd_bf16_B1_T16384_Hq32_Hkv8_dh128_D8",
+            B=1, T=16384, Hq=32, Hkv=8, dh=128, D=8, dtype="bf16"),
+    3: dict(kind="layer", name="layer_bwd_bf16_T65536_d4096_F14336_D16",
+            T=65536, d=4096, Hq=32, Hkv=8, dh=128, F=14336, D=16, dtype="bf16"),
+    4: dict(kind="lmhead", name="lmhead_ce_weighted_bf16_T131072x8seq_d3584_V152064_D32",
+            T=131072, d=3584, V=152064, D=32, dtype="bf16", w_std=0.02,
+            n_seq=8, masked_frac=0.25, weighted=True),
+}
+
+
+def workload_inputs(index: int, **override):
+    """Inputs of workload ``index`` (seed 1000 + index); sizes may be overridden."""
+    cfg = dict(WORKLOADS[index])
+    cfg.update(override)
+    seed = cfg.get("seed", 1000 + index)
+    kind = cfg["kind"]
+    if kind == "lmhead":
+        return lmhead_inputs(cfg["T"], cfg["d"], cfg["V"], cfg["dtype"], seed,
+                             w_std=cfg.get("w_std"), n_seq=cfg.get("n_seq", 1),
+                             masked_frac=cfg.get("masked_frac", 0.0),
+                             weighted=cfg.get("weighted", False))
+    if kind == "attn":
+        return attn_inputs(cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["dh"],
+                           cfg["dtype"], seed)
+    if kind == "layer":
+        return layer_inputs(cfg["T"], cfg["d"], cfg["Hq"], cfg["Hkv"], cfg["dh"],
+                            cfg["F"], cfg["dtype"], seed)
+    raise ValueError(kind)

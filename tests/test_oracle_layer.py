@@ -1,0 +1,128 @@
+"""Pins of the decoder-layer oracle (CPU only)."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import chunked
+
+NAMES = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W3", "W2")
+
+
+def _rand(T=6, d=8, Hq=2, Hkv=1, dh=4, Fw=12, seed=0, std=0.3):
+    rng = np.random.default_rng(seed)
+    w = {
+        "g1": 1 + 0.1 * rng.normal(size=d),
+        "Wq": rng.normal(size=(Hq * dh, d)) * std,
+        "Wk": rng.normal(size=(Hkv * dh, d)) * std,
+        "Wv": rng.normal(size=(Hkv * dh, d)) * std,
+        "Wo": rng.normal(size=(d, Hq * dh)) * std,
+        "g2": 1 + 0.1 * rng.normal(size=d),
+        "W1": rng.normal(size=(Fw, d)) * std,
+        "W3": rng.normal(size=(Fw, d)) * std,
+        "W2": rng.normal(size=(d, Fw)) * std,
+    }
+    x = rng.normal(size=(T, d))
+    dy = rng.normal(size=(T, d))
+    return x, dy, w
+
+
+def _torch_layer(x, w, Hq, Hkv, dh, eps):
+    """The same layer written with torch ops (rms_norm, silu, sdpa)."""
+    T, d = x.shape
+    h1 = F.rms_norm(x, (d,), weight=w["g1"], eps=eps)
+    q = (h1 @ w["Wq"].T).reshape(T, Hq, dh).transpose(0, 1)[None]
+    k = (h1 @ w["Wk"].T).reshape(T, Hkv, dh).transpose(0, 1)[None]
+    v = (h1 @ w["Wv"].T).reshape(T, Hkv, dh).transpose(0, 1)[None]
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=dh ** -0.5,
+                                       enable_gqa=(Hq != Hkv))
+    o = o[0].transpose(0, 1).reshape(T, Hq * dh)
+    a = x + o @ w["Wo"].T
+    n2 = F.rms_norm(a, (d,), weight=w["g2"], eps=eps)
+    m = F.silu(n2 @ w["W1"].T) * (n2 @ w["W3"].T)
+    return a + m @ w["W2"].T
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2)])
+def test_against_torch_autograd(Hq, Hkv):
+    T, d, dh, Fw, eps = 11, 16, 4, 24, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=Hq + 3 * Hkv)
+    xt = torch.tensor(x, requires_grad=True)
+    wt = {k: torch.tensor(v, requires_grad=True) for k, v in w.items()}
+    yt = _torch_layer(xt, wt, Hq, Hkv, dh, eps)
+    yt.backward(torch.tensor(dy))
+    dx, gr, y = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for k in NAMES:
+        np.testing.assert_allclose(gr[k], wt[k].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=k)
+
+
+def test_finite_differences():
+    T, d, Hq, Hkv, dh, Fw, eps = 6, 8, 2, 1, 4, 12, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=1)
+    dx, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps)
+    h = 1e-6
+
+    def f(xx, ww):
+        return float((oracle.layer_fwd(xx, ww, Hq, Hkv, dh, eps)[0] * dy).sum())
+
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (f(xp, w) - f(xm, w)) / (2 * h)
+    assert np.abs(fd - dx).max() <= 1e-7 * max(1.0, np.abs(dx).max())
+    for k in NAMES:
+        A = w[k]
+        fd = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            wp = dict(w)
+            wm = dict(w)
+            wp[k] = A.copy()
+            wm[k] = A.copy()
+            wp[k][idx] += h
+            wm[k][idx] -= h
+            fd[idx] = (f(x, wp) - f(x, wm)) / (2 * h)
+        assert np.abs(fd - gr[k]).max() <= 1e-7 * max(1.0, np.abs(gr[k]).max()), k
+
+
+def test_zero_output_projections():
+    # Wo = W2 = 0: y = x, so dx = dy; only dWo and dW2 are non-zero
+    T, d, Hq, Hkv, dh, Fw, eps = 7, 8, 2, 1, 4, 12, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=2)
+    w["Wo"] = np.zeros_like(w["Wo"])
+    w["W2"] = np.zeros_like(w["W2"])
+    dx, gr, y = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps)
+    np.testing.assert_array_equal(y, x)
+    np.testing.assert_array_equal(dx, dy)
+    for k in ("Wq", "Wk", "Wv", "W1", "W3", "g1", "g2"):
+        assert np.abs(gr[k]).max() == 0.0, k
+    # dWo = dy^T o and dW2 = dy^T m with o, m from an independent forward
+    _, cache = oracle.layer_fwd(x, w, Hq, Hkv, dh, eps)
+    np.testing.assert_allclose(gr["Wo"], dy.T @ cache["o"], atol=1e-13)
+    np.testing.assert_allclose(gr["W2"], dy.T @ cache["m"], atol=1e-13)
+
+
+def test_rmsnorm_scale_invariance():
+    # eps = 0: RMSNorm(c x) = RMSNorm(x), so the gradient is orthogonal to x
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(9, 16))
+    g = 1 + 0.1 * rng.normal(size=16)
+    dy = rng.normal(size=(9, 16))
+    dx, _ = oracle.rmsnorm_bwd(x, g, dy, 0.0)
+    assert np.abs((dx * x).sum(axis=1)).max() < 1e-13
+
+
+@pytest.mark.parametrize("D", [1, 2, 4, 7])
+def test_chunked_equals_unchunked(D):
+    T, d, Hq, Hkv, dh, Fw, eps = 7, 8, 4, 2, 4, 12, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=10 + D)
+    dx, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps)
+    dx2, gr2 = chunked.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D)
+    assert np.abs(dx - dx2).max() < 1e-12
+    for k in NAMES:
+        assert np.abs(gr[k] - gr2[k]).max() < 1e-12, k

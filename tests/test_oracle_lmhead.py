@@ -1,0 +1,162 @@
+"""Pins of the LM-head + cross-entropy oracle (CPU only).
+
+Each test checks the oracle against something other than itself: hand-worked
+closed forms, central finite differences of its own loss, torch's independent
+fp64 cross-entropy autograd, invariants and special cases fixed by the
+mathematics, and the chunked evaluation (D-invariance).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import chunked
+from helpers import ev, load_golden
+
+
+def _rand(T=7, d=5, V=11, seed=0, masked=True, weighted=True):
+    rng = np.random.default_rng(seed)
+    H = rng.normal(size=(T, d))
+    W = rng.normal(size=(V, d)) * 0.7
+    y = rng.integers(0, V, size=T)
+    if masked:
+        y[[1, 4]] = -1
+    w = rng.normal(size=T) if weighted else None
+    return H, W, y, w
+
+
+@pytest.mark.parametrize("case", [c["name"] for c in load_golden("lmhead_ce_hand.json")["cases"]])
+def test_hand_worked_golden(case):
+    g = load_golden("lmhead_ce_hand.json")
+    c = [c for c in g["cases"] if c["name"] == case][0]
+    H, W = ev(g["H"]), ev(g["W"])
+    w = None if c["weights"] is None else np.array(c["weights"])
+    L, dH, dW, tl, _ = oracle.lmhead_ce(H, W, np.array(c["targets"]), w, c["reduction"])
+    assert abs(L - ev(c["loss"])) < 1e-14
+    np.testing.assert_allclose(tl, ev(c["token_loss"]), atol=1e-14)
+    np.testing.assert_allclose(dH, ev(c["dH"]), atol=1e-14)
+    np.testing.assert_allclose(dW, ev(c["dW"]), atol=1e-14)
+
+
+@pytest.mark.parametrize("masked,weighted,reduction", [
+    (False, False, "mean_valid"), (True, False, "mean_valid"),
+    (True, True, "mean_valid"), (True, True, "sum")])
+def test_finite_differences(masked, weighted, reduction):
+    H, W, y, w = _rand(masked=masked, weighted=weighted)
+    L, dH, dW, _, _ = oracle.lmhead_ce(H, W, y, w, reduction)
+    h = 1e-6
+
+    def loss(Hx, Wx):
+        return oracle.lmhead_ce(Hx, Wx, y, w, reduction)[0]
+
+    for A, G, which in ((H, dH, 0), (W, dW, 1)):
+        fd = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            Ap, Am = A.copy(), A.copy()
+            Ap[idx] += h
+            Am[idx] -= h
+            args_p = (Ap, W) if which == 0 else (H, Ap)
+            args_m = (Am, W) if which == 0 else (H, Am)
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.abs(fd - G).max() <= 1e-7 * max(1.0, np.abs(G).max())
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_against_torch_autograd(weighted):
+    H, W, y, w = _rand(T=23, d=9, V=31, seed=3, weighted=weighted)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    yt = torch.tensor(y)
+    logits = Ht @ Wt.T
+    per_tok = F.cross_entropy(logits, yt.clamp_min(0), reduction="none")
+    valid = (yt >= 0).to(torch.float64)
+    wt = torch.ones(len(y), dtype=torch.float64) if w is None else torch.tensor(w)
+    N = valid.sum()
+    Lt = (per_tok * valid * wt).sum() / N
+    Lt.backward()
+    L, dH, dW, tl, lse = oracle.lmhead_ce(H, W, y, w)
+    assert abs(L - Lt.item()) < 1e-12
+    np.testing.assert_allclose(dH, Ht.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(tl, (per_tok * valid).detach().numpy(), atol=1e-12)
+    ref_lse = torch.logsumexp(logits, 1).detach().numpy()
+    v = y >= 0
+    np.testing.assert_allclose(lse[v], ref_lse[v], rtol=1e-13)
+    assert np.isnan(lse[~v]).all()
+
+
+def test_invariants():
+    H, W, y, w = _rand(T=17, d=6, V=13, seed=5)
+    _, dH, dW, _, _ = oracle.lmhead_ce(H, W, y, w)
+    # rows of (softmax - onehot) sum to zero, so the vocab sum of dW vanishes
+    assert np.abs(dW.sum(axis=0)).max() < 1e-14
+    # ignored tokens contribute nothing to dH
+    assert (dH[y < 0] == 0.0).all()
+
+
+def test_zero_weight_matrix_closed_form():
+    # W = 0: every softmax is uniform, L = ln V (mean of unweighted CE),
+    # dH = dZ W = 0, dW = sum_t (c_t/N)(1/V - e_{y_t}) h_t^T.
+    T, d, V = 9, 4, 6
+    rng = np.random.default_rng(11)
+    H = rng.normal(size=(T, d))
+    W = np.zeros((V, d))
+    y = rng.integers(0, V, size=T)
+    L, dH, dW, _, _ = oracle.lmhead_ce(H, W, y)
+    assert abs(L - math.log(V)) < 1e-14
+    assert (dH == 0).all()
+    ref = np.zeros((V, d))
+    for t in range(T):
+        for v in range(V):
+            ref[v] += (1.0 / T) * ((1.0 / V) - (1.0 if v == y[t] else 0.0)) * H[t]
+    np.testing.assert_allclose(dW, ref, atol=1e-15)
+
+
+def test_all_ignored_gives_zeros():
+    H, W, y, w = _rand()
+    y[:] = -1
+    L, dH, dW, tl, lse = oracle.lmhead_ce(H, W, y, w)
+    assert L == 0.0 and (dH == 0).all() and (dW == 0).all() and (tl == 0).all()
+
+
+def test_row_blocking_matches_unblocked():
+    H, W, y, w = _rand(T=37, d=6, V=19, seed=7)
+    a = oracle.lmhead_ce(H, W, y, w)
+    b = oracle.lmhead_ce(H, W, y, w, row_block=5)
+    assert abs(a[0] - b[0]) < 1e-13
+    for x, z in zip(a[1:4], b[1:4]):
+        assert np.abs(x - z).max() < 1e-13
+
+
+def test_sampled_rows_match_full():
+    H, W, y, w = _rand(T=29, d=6, V=19, seed=8)
+    _, dH, _, tl, lse = oracle.lmhead_ce(H, W, y, w)
+    rows = np.array([0, 1, 4, 13, 28])
+    N = int((y >= 0).sum())
+    dHr, tlr, lser = oracle.lmhead_ce_rows(H, W, y, w, rows, N)
+    np.testing.assert_allclose(dHr, dH[rows], atol=1e-15)
+    np.testing.assert_allclose(tlr, tl[rows], atol=1e-15)
+    np.testing.assert_array_equal(np.isnan(lser), np.isnan(lse[rows]))
+
+
+@pytest.mark.parametrize("T,D", [(13, 1), (13, 2), (13, 3), (13, 13), (64, 5)])
+def test_chunked_equals_unchunked(T, D):
+    H, W, y, w = _rand(T=T, d=6, V=17, seed=T + D)
+    L, dH, dW, _, _ = oracle.lmhead_ce(H, W, y, w)
+    L2, dH2, dW2 = chunked.lmhead_ce(H, W, y, w, D)
+    assert abs(L - L2) < 1e-12
+    assert np.abs(dH - dH2).max() < 1e-12
+    assert np.abs(dW - dW2).max() < 1e-12
+
+
+def test_chunk_table_rule():
+    # size = T // D, the last chunk takes the remainder
+    assert chunked.chunk_table(10, 3) == [(0, 3), (3, 6), (6, 10)]
+    assert chunked.chunk_table(5, 5) == [(i, i + 1) for i in range(5)]
+    assert chunked.chunk_table(7, 1) == [(0, 7)]
+    for bad in ((5, 0), (5, 6)):
+        with pytest.raises(ValueError):
+            chunked.chunk_table(*bad)
