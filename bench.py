@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the StreamBP hot path on one MI355X.
+
+Default workload: the chunked LM head + cross-entropy forward/backward at
+T=32768, d=4096, V=128256, D=16 in bf16 (fp32 accumulation), synthetic
+N(0,1) hidden states and N(0, 0.02^2) weights with uniform targets.  A
+"step" is one full call of the path on that batch (logits GEMM, softmax-CE
+row kernels, dH and dW GEMMs for every chunk, loss reduction), inputs
+resident in HBM.
+
+Prints ONE JSON line: tokens/s, ms per step, peak HBM bytes of the call,
+the fraction of bf16 MFMA peak over the whole step, the roofline of the
+dominant kernel (timed live with hipEvents on the launch stream through the
+library's kernel timer), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "backward tokens/sec + peak HBM bytes vs seq len T; % of bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", type=int, default=1)
+    p.add_argument("--D", type=int, default=None, help="override the chunk count")
+    p.add_argument("--T", type=int, default=None, help="override the sequence length")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=None)
+    return p.parse_args()
+
+
+def lmhead_setup(cfg, dev):
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    inp = synthetic.workload_inputs(cfg["index"], T=cfg["T"])
+    H, W, tg = inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev)
+    w = None if inp.weights is None else inp.weights.to(dev)
+    T, d, V, D = cfg["T"], cfg["d"], cfg["V"], cfg["D"]
+    dW = torch.empty(V, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(sbp.lmhead_ce_workspace_size(T, d, V, D, H.dtype), dtype=torch.uint8,
+                     device=dev)
+    red = "mean_valid"
+
+    def step():
+        return sbp.lmhead_ce(H, W, tg, w, D=D, reduction=red, dW=dW, workspace=ws)
+
+    y = inp.targets
+    n_valid = int((y >= 0).sum())
+    # algorithmic flops: 3 GEMMs of 2*N*V*d over the rows of chunks that hold a
+    # valid token (fully masked chunks are skipped)
+    rows = 0
+    for s, e in sbp.chunk_table(T, D):
+        if (y[s:e] >= 0).any():
+            rows += e - s
+    flops = 6.0 * rows * V * d
+    return step, flops, inp, n_valid
+
+
+def cpu_baseline_lmhead(inp, cfg, sample):
+    """The oracle, untouched, on the first `sample` tokens of the same input."""
+    import numpy as np
+    import oracle
+    import synthetic
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    H = synthetic.to_f64(inp.H[:sample])
+    W = synthetic.to_f64(inp.W)
+    y = inp.targets[:sample].numpy()
+    wts = None if inp.weights is None else synthetic.to_f64(inp.weights[:sample])
+    t0 = time.perf_counter()
+    oracle.lmhead_ce(H, W, y, wts)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample} of {cfg['T']} tokens, full V={cfg['V']} and d={cfg['d']} "
+                      f"(fp64 NumPy, unchunked); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; multi-GPU data parallelism is not built)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    sbp.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    idx = args.workload
+    cfg = dict(synthetic.WORKLOADS[idx])
+    cfg["index"] = idx
+    if args.D:
+        cfg["D"] = args.D
+    if args.T:
+        cfg["T"] = args.T
+    if cfg["kind"] != "lmhead":
+        print("only the LM-head workloads are wired into bench.py so far", file=sys.stderr)
+        sys.exit(2)
+    step, flops, inp, n_valid = lmhead_setup(cfg, dev)
+    dtype = cfg["dtype"]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_mem = torch.cuda.memory_allocated(dev)
+
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with sbp.profile() as prof:
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_gpu = e0.elapsed_time(e1) / args.steps
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms = max(ms_gpu, ms_wall)
+    peak = torch.cuda.max_memory_allocated(dev)
+    T = cfg["T"]
+    value = T / (ms / 1e3)
+
+    # dominant kernel and its roofline (live hipEvent timing inside the call)
+    dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
+    name, k = dom
+    if k["flops"] > 0:
+        ach = k["flops"] / (k["ms"] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dtype],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4), "traffic": None,
+                "kernel": name, "avg_launch_ms": round(k["ms"] / k["launches"], 4),
+                "flops_per_launch": k["flops"] / k["launches"]}
+    else:
+        ach = k["bytes"] / (k["ms"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": name,
+                "avg_launch_ms": round(k["ms"] / k["launches"], 4),
+                "bytes_per_launch": k["bytes"] / k["launches"]}
+    kernels = {n: {"launches": v["launches"] // args.steps,
+                   "ms_per_step": round(v["ms"] / args.steps, 3),
+                   "tflops": round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1) if v["flops"] else None,
+                   "gbs": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1) if not v["flops"] else None}
+               for n, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "T": T, "d": cfg["d"], "V": cfg["V"], "D": cfg["D"],
+                   "valid_tokens": n_valid},
+        "peak_hbm_bytes": int(peak),
+        "peak_hbm_bytes_call": int(peak - base_mem),
+        "mfma_frac_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or (256 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
+        out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

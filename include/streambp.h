@@ -1,0 +1,220 @@
+/*
+ * libstreambp -- sequence-chunked exact backward (StreamBP) for MI355X (gfx950).
+ *
+ * The method (StreamBP pages: the skill page "StreamBP: Memory-Efficient
+ * Backpropagation", sections "Core Concept", "Architecture Overview" and
+ * "Implementation"; the arXiv abstract quoted on the tomesphere and mlsanity
+ * pages): the chain rule of a layer is split linearly along the sequence into
+ * D chunks.  Each chunk's activations are (re)computed and back-propagated on
+ * their own, weight gradients are summed over the chunks, and the result is
+ * the exact gradient of the unchunked objective.  Causal attention makes a
+ * query chunk depend only on its key prefix.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.   Every array argument is a DEVICE pointer (HIP device memory of
+ *             the current device), except `desc`, `weights` and `grads`
+ *             structs and `bytes` out-params, which are HOST pointers.  All
+ *             device pointers must be 16-byte aligned.  Arrays are dense and
+ *             row-major with the shapes given below; weights are stored
+ *             [out, in] (y = x W^T).
+ * Ownership.  The caller owns every buffer, including the workspace `ws`
+ *             (size from the matching *_workspace_size call).  The library
+ *             allocates no device memory, keeps no pointer after a call
+ *             returns, and holds no state between calls besides the
+ *             thread-local error text and the optional profiler.
+ * Streams.    `stream` is a hipStream_t passed as void* (NULL = the legacy
+ *             default stream).  Every call only enqueues work on `stream`
+ *             and returns; no host synchronisation.  Outputs are valid once
+ *             the stream reaches that point.  Two calls that share a
+ *             workspace must be ordered on one stream.
+ * Chunks.     D chunks of a length-T sequence (skill page, "Implementation",
+ *             the sequence decomposition): size = T / D (integer division);
+ *             chunk i is [i*size, (i+1)*size), the last chunk ends at T.
+ *             1 <= D <= T is required.  Results do not depend on D beyond
+ *             floating-point summation order.
+ * Precision.  dtype SBP_F32: every tensor fp32.  SBP_BF16: activations,
+ *             weights and activation gradients (dH, dQ, dx) bf16; products
+ *             accumulate in fp32; weight gradients, dK/dV and gain gradients
+ *             are always fp32.
+ * Accumulate. accumulate = 1 adds into the fp32 gradient outputs (dW, dK,
+ *             dV, the layer's weight and gain gradients) -- gradient
+ *             accumulation over micro-batches, which the skill page's
+ *             "Practical Guidance" calls orthogonal to StreamBP;
+ *             accumulate = 0 overwrites them.  Activation gradients (dH, dQ,
+ *             dx) are always overwritten.
+ * Errors.     Arguments are checked before anything is enqueued; a bad
+ *             argument returns SBP_ERR_INVALID_ARG / SBP_ERR_UNSUPPORTED /
+ *             SBP_ERR_WORKSPACE with a message in sbp_last_error() (per host
+ *             thread) and touches no output.  A failed kernel launch returns
+ *             SBP_ERR_HIP; outputs are then unspecified.  No C++ exception
+ *             crosses this interface.
+ */
+#ifndef STREAMBP_H
+#define STREAMBP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SBP_OK = 0,
+  SBP_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, D out of range */
+  SBP_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype, alignment of a size) */
+  SBP_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_workspace_size result */
+  SBP_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} sbp_status;
+
+typedef enum { SBP_F32 = 0, SBP_BF16 = 1 } sbp_dtype;
+
+typedef enum {
+  SBP_MEAN_VALID = 0, /* divide by N = number of tokens with target >= 0 */
+  SBP_SUM = 1         /* N = 1 */
+} sbp_reduction;
+
+/* ------------------------------------------------------------------------
+ * 1. LM head + softmax cross-entropy, forward and backward.
+ *
+ * Passage: skill page, "Implementation" -- the logits-gradient routine
+ * (per-token cross-entropy; softmax with one subtracted at the target) and
+ * the linear-layer chunk gradient (weight gradient from activations and
+ * upstream gradient, input gradient from upstream gradient and weight);
+ * "Core Concept" / arXiv abstract: the memory of the logits is what
+ * StreamBP removes.  Per chunk the [T_c, V] logits are formed, consumed and
+ * dropped; the full [T, V] logits never exist.
+ *
+ *   Z = H W^T,  l_t = logsumexp(Z_t) - Z_{t,y_t},  c_t = w_t [y_t >= 0]
+ *   loss = (1/N) sum_t c_t l_t          (N: see sbp_reduction; N = 0 -> 0)
+ *   dZ_t = (c_t/N) (softmax(Z_t) - e_{y_t}),  dH = dZ W,  dW (+)= dZ^T H
+ *
+ * H        [T, d]   dtype       hidden states
+ * W        [V, d]   dtype       LM-head weight
+ * targets  [T]      int32       target ids in [0, V); < 0 = ignored token
+ *                               (ids >= V are a caller error, not checked)
+ * weights  [T]      fp32 or NULL  per-token weights w_t (GRPO advantage, DPO
+ *                               sequence weight); NULL = all ones
+ * loss     [1]      fp32 out    the loss above
+ * token_loss [T]    fp32 out or NULL  unweighted per-token l_t (0 if ignored)
+ * dH       [T, d]   dtype out   (ignored tokens give zero rows)
+ * dW       [V, d]   fp32 out    accumulate semantics as above
+ * Requires d % 8 == 0 (bf16) or d % 4 == 0 (f32), V >= 1, T >= 1.
+ * Chunks with no valid token are skipped on the device (their dH rows are
+ * zero-filled).
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_lmhead_ce_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,
+                                        int32_t dtype, size_t* bytes);
+
+sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* targets,
+                                 const float* weights, int64_t T, int64_t d, int64_t V,
+                                 int32_t D, int32_t dtype, int32_t reduction,
+                                 int32_t accumulate, float* loss, float* token_loss,
+                                 void* dH, float* dW, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * 2. Causal GQA attention backward, chunked over queries.
+ *
+ * Passage: skill page, "Architecture Overview" (causal structure
+ * exploitation) and "Practical Guidance" (masks across chunk boundaries;
+ * causal masking); arXiv abstract: the causal structure lowers the FLOPs.
+ * Query chunk c = [s_c, e_c) reads keys/values [0, e_c) only; key blocks
+ * that lie entirely above the diagonal are never visited.  Chunks run in
+ * reverse order; dK/dV are accumulated in fp32 across chunks and across the
+ * G = Hq/Hkv query heads of a group (query head h uses kv head h / G).
+ *
+ *   S = scale Q K^T (key j visible to query i iff j <= i), P = softmax(S),
+ *   O = P V, dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO O)),
+ *   dQ = scale dS K, dK = scale dS^T Q
+ *
+ * Q, dO  [B, T, Hq, dh]  dtype     K, V  [B, T, Hkv, dh]  dtype
+ * O      [B, T, Hq, dh]  dtype or NULL   forward output; with `lse`, skips
+ * lse    [B, T, Hq]      fp32 or NULL    the forward recomputation (both or
+ *                                        neither; natural-log log-sum-exp of
+ *                                        the scaled scores)
+ * dQ     [B, T, Hq, dh]  dtype out
+ * dK, dV [B, T, Hkv, dh] fp32 out  (accumulate semantics)
+ * Supported: dh in {64, 128}; Hq % Hkv == 0.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_attn_bwd_workspace_size(int64_t B, int64_t T, int32_t Hq, int32_t Hkv,
+                                       int32_t dh, int32_t D, int32_t dtype, size_t* bytes);
+
+sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const void* V, const void* dO,
+                                const void* O, const float* lse, int64_t B, int64_t T,
+                                int32_t Hq, int32_t Hkv, int32_t dh, float scale, int32_t D,
+                                int32_t dtype, int32_t accumulate, void* dQ, float* dK,
+                                float* dV, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 3. One pre-norm decoder layer, streamed backward.
+ *
+ * Passage: skill page, "Implementation" -- the streaming layer backward
+ * (per chunk: run the layer forward on the chunk, back-propagate the chunk's
+ * upstream gradient, add the weight gradients, keep the chunk's input
+ * gradient) and "Architecture Overview" (layer-wise application).  Layer:
+ *
+ *   h1 = RMSNorm(x; g1); q,k,v = h1 Wq^T, h1 Wk^T, h1 Wv^T
+ *   o = causal GQA attention (scale 1/sqrt(dh)); a = x + o Wo^T
+ *   n2 = RMSNorm(a; g2); m = silu(n2 W1^T) * (n2 W3^T); y = a + m W2^T
+ *   RMSNorm(x; g) = g x / sqrt(mean(x^2) + eps)
+ *
+ * Keys and values of all T tokens are formed once (the causal prefix); then
+ * chunks run in reverse order, each recomputing its own forward, so the MLP
+ * activations exist for one chunk at a time.
+ *
+ * x, dy   [T, d] dtype;  dx [T, d] dtype out
+ * weights (host struct of device pointers, dtype): g1, g2 [d];
+ *   Wq [Hq*dh, d]; Wk, Wv [Hkv*dh, d]; Wo [d, Hq*dh]; W1, W3 [F, d]; W2 [d, F]
+ * grads   (host struct of device pointers, fp32, same shapes; accumulate
+ *          semantics)
+ * Supported: dh in {64, 128}; Hq % Hkv == 0; d % 8 == 0; F % 8 == 0.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t T, d;
+  int32_t Hq, Hkv, dh;
+  int64_t F;
+  float eps;
+  int32_t dtype;
+} sbp_layer_desc;
+
+typedef struct {
+  const void *g1, *Wq, *Wk, *Wv, *Wo, *g2, *W1, *W3, *W2;
+} sbp_layer_weights;
+
+typedef struct {
+  float *g1, *Wq, *Wk, *Wv, *Wo, *g2, *W1, *W3, *W2;
+} sbp_layer_grads;
+
+sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D, size_t* bytes);
+
+sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, const void* dy,
+                         const sbp_layer_weights* weights, int32_t D, int32_t accumulate,
+                         void* dx, sbp_layer_grads* grads, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * ---------------------------------------------------------------------- */
+const char* sbp_status_string(int32_t status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* sbp_last_error(void);
+int32_t sbp_version(void);
+
+/* Kernel timer, for benchmarking.  While enabled, every kernel the library
+ * enqueues is bracketed by hipEvents on its stream (events come from a pool
+ * created by sbp_profile_begin; no device memory is allocated).
+ * sbp_profile_end waits for those events and folds them into per-kernel
+ * totals; sbp_profile_entry then reads entry i (0 <= i < count) as kernel
+ * name, launch count, total milliseconds and the algorithmic flop and byte
+ * counts of those launches.  Profiling is process-wide and not thread-safe. */
+sbp_status sbp_profile_begin(int32_t max_launches);
+sbp_status sbp_profile_end(int32_t* count);
+sbp_status sbp_profile_entry(int32_t i, const char** name, int64_t* launches,
+                             double* total_ms, double* flops, double* bytes);
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMBP_H */

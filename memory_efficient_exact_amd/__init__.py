@@ -1,0 +1,208 @@
+"""libstreambp Python binding: argument marshalling over the C ABI.
+
+Every step of the computation runs in the HIP kernels of libstreambp
+(``csrc/``); this module only checks tensor shapes/dtypes, allocates the
+outputs and the workspace with torch, and passes raw device pointers and the
+current HIP stream.  There is no CPU or PyTorch fallback: if the library is
+not built, or a tensor is not on the GPU, the call raises.
+
+Names follow ``include/streambp.h``:
+
+* ``lmhead_ce``      -> ``sbp_lmhead_ce_fwd_bwd``
+* ``attn_bwd``       -> ``sbp_attn_bwd_chunked``
+* ``layer_bwd``      -> ``sbp_layer_bwd``
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from contextlib import contextmanager
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, LayerDesc,
+                   LayerGrads, LayerWeights, StreamBPError, check, load)
+
+__all__ = ["lmhead_ce", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
+           "attn_bwd_workspace_size", "layer_bwd_workspace_size", "profile", "load",
+           "StreamBPError", "chunk_table"]
+
+_DT = {torch.float32: SBP_F32, torch.bfloat16: SBP_BF16}
+_RED = {"mean_valid": SBP_MEAN_VALID, "sum": SBP_SUM}
+
+
+def chunk_table(T: int, D: int):
+    """The chunk boundaries the library uses: size = T // D, last chunk to T."""
+    if not 1 <= D <= T:
+        raise ValueError("need 1 <= D <= T")
+    s = T // D
+    return [(i * s, (i + 1) * s if i < D - 1 else T) for i in range(D)]
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+def lmhead_ce_workspace_size(T, d, V, D, dtype=torch.bfloat16) -> int:
+    out = C.c_size_t(0)
+    check(load().sbp_lmhead_ce_workspace_size(T, d, V, D, _DT[dtype], C.byref(out)))
+    return out.value
+
+
+def lmhead_ce(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+              weights: Optional[torch.Tensor] = None, D: int = 1,
+              reduction: str = "mean_valid", dW: Optional[torch.Tensor] = None,
+              accumulate: bool = False, token_loss: bool = False,
+              workspace: Optional[torch.Tensor] = None):
+    """Chunked LM head + cross-entropy.  Returns ``(loss, dH, dW, token_loss)``.
+
+    ``loss`` is a 1-element fp32 tensor; ``token_loss`` is None unless asked.
+    ``dW`` may be passed in (fp32 [V, d]) to accumulate into it.
+    """
+    lib = load()
+    _dev(H, W, targets, weights, dW)
+    T, d = H.shape
+    V = W.shape[0]
+    if W.shape[1] != d or W.dtype != H.dtype or targets.shape != (T,) or targets.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    if weights is not None and (weights.shape != (T,) or weights.dtype != torch.float32):
+        raise ValueError("weights must be fp32 [T]")
+    dt = _dtype(H)
+    dev = H.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    if dW is None:
+        dW = torch.empty(V, d, dtype=torch.float32, device=dev)
+    elif dW.shape != (V, d) or dW.dtype != torch.float32:
+        raise ValueError("dW must be fp32 [V, d]")
+    tl = torch.empty(T, dtype=torch.float32, device=dev) if token_loss else None
+    nb = lmhead_ce_workspace_size(T, d, V, D, H.dtype)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
+    check(lib.sbp_lmhead_ce_fwd_bwd(_ptr(H), _ptr(W), _ptr(targets), _ptr(weights), T, d, V, D,
+                                    dt, _RED[reduction], int(accumulate), _ptr(loss), _ptr(tl),
+                                    _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, dH, dW, tl
+
+
+# ----------------------------------------------------------------------------
+def attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, dtype=torch.bfloat16) -> int:
+    out = C.c_size_t(0)
+    check(load().sbp_attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, _DT[dtype], C.byref(out)))
+    return out.value
+
+
+def attn_bwd(Q, K, V, dO, D: int = 1, scale: Optional[float] = None, O=None, lse=None,
+             dK: Optional[torch.Tensor] = None, dV: Optional[torch.Tensor] = None,
+             accumulate: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Chunked causal GQA attention backward.  Returns ``(dQ, dK, dV)``;
+    dK/dV are fp32.  Layout [B, T, heads, dh]."""
+    lib = load()
+    _dev(Q, K, V, dO, O, lse, dK, dV)
+    B, T, Hq, dh = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, T, Hkv, dh) or V.shape != K.shape or dO.shape != Q.shape:
+        raise ValueError("shape mismatch")
+    if not (Q.dtype == K.dtype == V.dtype == dO.dtype):
+        raise ValueError("dtype mismatch")
+    dt = _dtype(Q)
+    dev = Q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    dQ = torch.empty_like(Q)
+    if dK is None:
+        dK = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
+    if dV is None:
+        dV = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
+    nb = attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
+    check(lib.sbp_attn_bwd_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(O), _ptr(lse), B, T,
+                                   Hq, Hkv, dh, float(scale), D, dt, int(accumulate), _ptr(dQ),
+                                   _ptr(dK), _ptr(dV), _ptr(ws), ws.numel(), _stream(dev)))
+    return dQ, dK, dV
+
+
+# ----------------------------------------------------------------------------
+def _desc(T, d, Hq, Hkv, dh, F, eps, dtype) -> LayerDesc:
+    return LayerDesc(T, d, Hq, Hkv, dh, F, eps, _DT[dtype])
+
+
+def layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6) -> int:
+    out = C.c_size_t(0)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype)
+    check(load().sbp_layer_bwd_workspace_size(C.byref(desc), D, C.byref(out)))
+    return out.value
+
+
+def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
+              eps: float = 1e-6, D: int = 1, grads: Optional[Dict[str, torch.Tensor]] = None,
+              accumulate: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Streamed backward of one pre-norm decoder layer.  Returns ``(dx, grads)``
+    with fp32 weight/gain gradients keyed like ``weights``."""
+    lib = load()
+    _dev(x, dy, *weights.values())
+    T, d = x.shape
+    F = weights["W1"].shape[0]
+    dev = x.device
+    dt = x.dtype
+    if grads is None:
+        grads = {n: torch.empty(weights[n].shape, dtype=torch.float32, device=dev) for n in LAYER_NAMES}
+    _dev(*grads.values())
+    for n in LAYER_NAMES:
+        if weights[n].dtype != dt or grads[n].dtype != torch.float32 or grads[n].shape != weights[n].shape:
+            raise ValueError(f"bad weight/grad {n}")
+    dx = torch.empty_like(x)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt)
+    wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
+    gst = LayerGrads(*[grads[n].data_ptr() for n in LAYER_NAMES])
+    nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
+    check(lib.sbp_layer_bwd(C.byref(desc), _ptr(x), _ptr(dy), C.byref(wst), D, int(accumulate),
+                            _ptr(dx), C.byref(gst), _ptr(ws), ws.numel(), _stream(dev)))
+    return dx, grads
+
+
+# ----------------------------------------------------------------------------
+@contextmanager
+def profile(max_launches: int = 65536):
+    """Per-kernel timing of every library launch inside the block.
+
+    Yields a dict that, after the block, maps kernel name ->
+    ``{"launches", "ms", "flops", "bytes"}`` (totals over the block)."""
+    lib = load()
+    res: Dict[str, dict] = {}
+    check(lib.sbp_profile_begin(max_launches))
+    try:
+        yield res
+    finally:
+        n = C.c_int32(0)
+        check(lib.sbp_profile_end(C.byref(n)))
+        for i in range(n.value):
+            name = C.c_char_p()
+            L, ms, fl, by = C.c_int64(), C.c_double(), C.c_double(), C.c_double()
+            check(lib.sbp_profile_entry(i, C.byref(name), C.byref(L), C.byref(ms), C.byref(fl),
+                                        C.byref(by)))
+            res[name.value.decode()] = {"launches": L.value, "ms": ms.value, "flops": fl.value,
+                                        "bytes": by.value}

@@ -1,0 +1,67 @@
+// Internal kernel launchers of libstreambp (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace sbp {
+
+// ---------------------------------------------------------------- GEMM ----
+enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4 };
+enum { GEMM_TILE_128 = 0, GEMM_TILE_256 = 1 };
+
+struct GemmParams {
+  const void* A = nullptr;  // [M, K] row-major, K contiguous, pitch lda elements
+  const void* B = nullptr;  // [N, K] row-major, pitch ldb
+  void* C = nullptr;        // [M, N] pitch ldc (fp32 for F32/F32_ACC/PARTIAL, else dtype)
+  const void* R = nullptr;  // residual [M, N] pitch ldr (EPI_OUT_RESID)
+  int64_t lda = 0, ldb = 0, ldc = 0, ldr = 0;
+  int M = 0, N = 0, K = 0;  // K % 8 == 0 (bf16) / K % 4 == 0 (fp32); lda/ldb likewise
+  float alpha = 1.f;
+  int beta = 0;                    // EPI_F32_ACC: C = acc + beta * C
+  const int* beta_zero = nullptr;  // EPI_F32_ACC: device flag, non-zero forces beta = 0
+  const int* active = nullptr;     // device flag, 0 -> the whole launch is a no-op
+  int k_split = 1;                 // EPI_PARTIAL: number of K ranges
+  int k_per_split = 0;             // multiple of the K step (0 = even split)
+  int64_t split_stride = 0;        // EPI_PARTIAL: elements between partial outputs
+  int m_fastest = 1;               // tile order inside an XCD's range
+  int tiles_m = 0, tiles_n = 0;    // filled by the launcher
+};
+
+int gemm_k_granule(int dtype);
+sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, const char* name);
+
+// ------------------------------------------------------- LM head + CE ----
+struct LmPrep {   // device-side scalars written by lm_prep
+  int* n_valid;       // [1]
+  float* inv_norm;    // [1]  1/N (mean_valid, N>0), 1 (sum), 0 (N == 0)
+  int* chunk_active;  // [D]
+  int* beta_zero;     // [D]  1 for the chunk whose dW GEMM must overwrite
+  int* none_active;   // [1]  1 if no chunk has a valid token
+};
+sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int reduction, int accumulate,
+                   const LmPrep& pr, hipStream_t st);
+// Per-row log-sum-exp and per-token loss for rows [s, s+Tc) of one chunk.
+sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
+                    int64_t s, int64_t Tc, int64_t V, float* lse, float* loss_part,
+                    float* token_loss, hipStream_t st);
+// dZ (dtype) [Tc, ldg] and dZ^T (dtype) [Vp, ldgt] for one chunk; zero pads.
+sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* targets,
+                   const float* weights, const float* inv_norm, const float* lse, int64_t s,
+                   int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,
+                   int64_t ldgt, int64_t Tcp, const int* active, hipStream_t st);
+sbp_status loss_reduce(const float* loss_part, int64_t T, const float* inv_norm, float* loss,
+                       hipStream_t st);
+
+// ------------------------------------------------------------ helpers ----
+// dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rp; c < C.
+sbp_status transpose_pad(int dtype, const void* src, int64_t lds_, int64_t R, int64_t C,
+                         void* dst, int64_t ldd, int64_t Rp, const int* active, hipStream_t st);
+// out[m][n] = sum_s part[s][m][n] (or 0 where *active == 0), cast to dtype.
+sbp_status splitk_reduce(int dtype, const float* part, int64_t split_stride, int S, int64_t M,
+                         int64_t N, int64_t ldp, void* out, int64_t ldo, const int* active,
+                         hipStream_t st);
+// Fill n floats with 0 when *when != 0 (unconditionally when `when` is null).
+sbp_status fill_zero_f32(float* p, int64_t n, const int* when, hipStream_t st);
+sbp_status fill_zero_bytes(void* p, int64_t nbytes, hipStream_t st);
+
+}  // namespace sbp

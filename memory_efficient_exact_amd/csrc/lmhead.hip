@@ -1,0 +1,188 @@
+// sbp_lmhead_ce_fwd_bwd: chunked LM head + softmax cross-entropy.
+//
+// Per chunk c = [s, e) (skill page "Implementation": the sequence
+// decomposition, the logits-gradient routine and the linear-layer chunk
+// gradient), with every GEMM in the NT form of gemm.hip:
+//   Z_c   = H_c W^T                fp32 [T_c, V]          (gemm, EPI_F32)
+//   lse, l_t, c_t l_t              per row                 (ce_stats)
+//   dZ_c, dZ_c^T                   dtype, zero-padded      (ce_grad)
+//   H_c^T                          dtype [d, T_c]          (transpose_pad)
+//   dH_c  = dZ_c W = dZ_c (W^T)^T  split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
+//   dW   += dZ_c^T H_c             fp32 read-modify-write  (gemm EPI_F32_ACC)
+// W^T is formed once per call.  Peak workspace is O(T_c V + V d), not O(T V).
+#include "common.h"
+#include "kernels.h"
+
+namespace sbp {
+namespace {
+
+struct LmWs {
+  float* Z;
+  void* dZ;
+  void* dZt;
+  void* Wt;
+  void* Ht;
+  float* part;
+  float* lse;
+  float* loss_part;
+  LmPrep prep;
+};
+
+struct LmShape {
+  int64_t T, d, V;
+  int32_t D;
+  int dtype;
+  int64_t Tcm, Tcp, Vp;
+  int S;  // split count of the dH GEMM
+  size_t esz;
+};
+
+LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
+  LmShape s;
+  s.T = T; s.d = d; s.V = V; s.D = D; s.dtype = dtype;
+  s.esz = dtype == SBP_BF16 ? 2 : 4;
+  s.Tcm = max_chunk_len(T, D);
+  s.Tcp = round_up(s.Tcm, 64);
+  s.Vp = round_up(V, 64);
+  // dH GEMM: few output tiles, long K = V.  Split K so that the launch has
+  // ~1024 blocks (4 per CU); a function of the shape only.
+  const int64_t tiles = cdiv(s.Tcm, 128) * cdiv(d, 128);
+  int64_t S = cdiv(1024, tiles);
+  S = std::max<int64_t>(1, std::min<int64_t>(S, 16));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, s.Vp / 512));
+  s.S = (int)S;
+  return s;
+}
+
+size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
+  WsPlan P;
+  P.base = base;
+  LmWs x;
+  x.Z = (float*)P.take(sizeof(float) * s.Tcm * s.Vp);
+  x.dZ = P.take(s.esz * s.Tcm * s.Vp);
+  x.dZt = P.take(s.esz * s.Vp * s.Tcp);
+  x.Wt = P.take(s.esz * s.d * s.Vp);
+  x.Ht = P.take(s.esz * s.d * s.Tcp);
+  x.part = (float*)P.take(sizeof(float) * (size_t)s.S * s.Tcm * s.d);
+  x.lse = (float*)P.take(sizeof(float) * s.Tcm);
+  x.loss_part = (float*)P.take(sizeof(float) * s.T);
+  x.prep.n_valid = (int*)P.take(sizeof(int));
+  x.prep.inv_norm = (float*)P.take(sizeof(float));
+  x.prep.none_active = (int*)P.take(sizeof(int));
+  x.prep.chunk_active = (int*)P.take(sizeof(int) * s.D);
+  x.prep.beta_zero = (int*)P.take(sizeof(int) * s.D);
+  if (w) *w = x;
+  return round_up((int64_t)P.off, 256);
+}
+
+inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+sbp_status lm_check_sizes(int64_t T, int64_t d, int64_t V, int32_t D, int32_t dtype) {
+  if (dtype != SBP_F32 && dtype != SBP_BF16) return set_error(SBP_ERR_INVALID_ARG, "dtype %d is not SBP_F32 or SBP_BF16", dtype);
+  if (T < 1 || d < 1 || V < 1) return set_error(SBP_ERR_INVALID_ARG, "T, d, V must be >= 1 (got %lld, %lld, %lld)", (long long)T, (long long)d, (long long)V);
+  if (D < 1 || D > T) return set_error(SBP_ERR_INVALID_ARG, "need 1 <= D <= T (D=%d, T=%lld)", D, (long long)T);
+  const int64_t vec = dtype == SBP_BF16 ? 8 : 4;
+  if (d % vec) return set_error(SBP_ERR_UNSUPPORTED, "d=%lld must be a multiple of %lld for this dtype", (long long)d, (long long)vec);
+  if (T > (1ll << 30) || V > (1ll << 30) || d > (1ll << 20)) return set_error(SBP_ERR_UNSUPPORTED, "size out of supported range");
+  return SBP_OK;
+}
+
+}  // namespace
+}  // namespace sbp
+
+using namespace sbp;
+
+extern "C" sbp_status sbp_lmhead_ce_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,
+                                                   int32_t dtype, size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = lm_check_sizes(T, d, V, D, dtype);
+  if (st != SBP_OK) return st;
+  *bytes = lm_plan(lm_shape(T, d, V, D, dtype), nullptr, nullptr);
+  return SBP_OK;
+}
+
+extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* targets,
+                                            const float* weights, int64_t T, int64_t d, int64_t V,
+                                            int32_t D, int32_t dtype, int32_t reduction,
+                                            int32_t accumulate, float* loss, float* token_loss,
+                                            void* dH, float* dW, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  clear_error();
+  sbp_status st = lm_check_sizes(T, d, V, D, dtype);
+  if (st != SBP_OK) return st;
+  if (reduction != SBP_MEAN_VALID && reduction != SBP_SUM)
+    return set_error(SBP_ERR_INVALID_ARG, "reduction %d is not SBP_MEAN_VALID or SBP_SUM", reduction);
+  if (!H || !W || !targets || !loss || !dH || !dW)
+    return set_error(SBP_ERR_INVALID_ARG, "H, W, targets, loss, dH and dW must be non-NULL");
+  if (misaligned(H) || misaligned(W) || misaligned(targets) || misaligned(loss) || misaligned(dH) ||
+      misaligned(dW) || misaligned(weights) || misaligned(token_loss) || misaligned(ws))
+    return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const LmShape s = lm_shape(T, d, V, D, dtype);
+  const size_t need = lm_plan(s, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  LmWs w;
+  lm_plan(s, (char*)ws, &w);
+  hipStream_t str = (hipStream_t)stream;
+  const char* Hb = (const char*)H;
+
+#define SBP_TRY(x)                   \
+  do {                               \
+    sbp_status _s = (x);             \
+    if (_s != SBP_OK) return _s;     \
+  } while (0)
+
+  SBP_TRY(lm_prep(targets, T, D, reduction, accumulate, w.prep, str));
+  // W^T [d, Vp], zero columns V..Vp (they meet the zero pad of dZ in the dH GEMM)
+  SBP_TRY(transpose_pad(dtype, W, d, V, d, w.Wt, s.Vp, s.Vp, nullptr, str));
+  for (int32_t c = 0; c < D; ++c) {
+    int64_t s0, e0;
+    chunk_bounds(T, D, c, &s0, &e0);
+    const int64_t Tc = e0 - s0;
+    const int64_t Tcp = round_up(Tc, 64);
+    const int* act = w.prep.chunk_active + c;
+
+    GemmParams g1;
+    g1.A = Hb + s0 * d * s.esz; g1.lda = d;
+    g1.B = W; g1.ldb = d;
+    g1.C = w.Z; g1.ldc = s.Vp;
+    g1.M = (int)Tc; g1.N = (int)V; g1.K = (int)d;
+    g1.active = act;
+    g1.m_fastest = 1;
+    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_128, str, "gemm_logits"));
+
+    SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
+    SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
+                    w.dZ, s.Vp, w.dZt, Tcp, Tcp, act, str));
+    SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, w.Ht, Tcp, Tcp, act, str));
+
+    GemmParams g2;
+    g2.A = w.dZ; g2.lda = s.Vp;
+    g2.B = w.Wt; g2.ldb = s.Vp;
+    g2.C = w.part; g2.ldc = d;
+    g2.M = (int)Tc; g2.N = (int)d; g2.K = (int)s.Vp;
+    g2.k_split = s.S;
+    g2.split_stride = s.Tcm * d;
+    g2.active = act;
+    g2.m_fastest = 1;
+    SBP_TRY(gemm_nt(dtype, EPI_PARTIAL, g2, GEMM_TILE_128, str, "gemm_dH"));
+    SBP_TRY(splitk_reduce(dtype, w.part, s.Tcm * d, s.S, Tc, d, d, (char*)dH + s0 * d * s.esz, d,
+                          act, str));
+
+    GemmParams g3;
+    g3.A = w.dZt; g3.lda = Tcp;
+    g3.B = w.Ht; g3.ldb = Tcp;
+    g3.C = dW; g3.ldc = d;
+    g3.M = (int)V; g3.N = (int)d; g3.K = (int)Tcp;
+    g3.beta = 1;
+    g3.beta_zero = w.prep.beta_zero + c;
+    g3.active = act;
+    g3.m_fastest = 0;
+    SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_128, str, "gemm_dW"));
+  }
+  if (!accumulate) SBP_TRY(fill_zero_f32(dW, V * d, w.prep.none_active, str));
+  SBP_TRY(loss_reduce(w.loss_part, T, w.prep.inv_norm, loss, str));
+#undef SBP_TRY
+  return SBP_OK;
+}

@@ -1,0 +1,161 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments before launching anything (CPU only: no call here reaches a kernel;
+device pointers are fake addresses that validation never dereferences)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import memory_efficient_exact_amd as sbp
+from memory_efficient_exact_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streambp.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+MIS = 0x10004   # misaligned
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sbp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = sbp.load()
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in _lib.SIGNATURES, s
+    assert lib.sbp_version() >= 100
+
+
+def test_status_strings():
+    lib = sbp.load()
+    assert lib.sbp_status_string(0) == b"SBP_OK"
+    assert lib.sbp_status_string(3) == b"SBP_ERR_WORKSPACE"
+
+
+def _ws(fn, *args):
+    out = C.c_size_t(0)
+    st = fn(*args, C.byref(out))
+    return st, out.value
+
+
+def test_lmhead_workspace_is_chunk_sized():
+    lib = sbp.load()
+    # logits workspace shrinks ~ 1/D (O(T_c V), never O(T V))
+    st1, w1 = _ws(lib.sbp_lmhead_ce_workspace_size, 32768, 4096, 128256, 1, 1)
+    st16, w16 = _ws(lib.sbp_lmhead_ce_workspace_size, 32768, 4096, 128256, 16, 1)
+    assert st1 == st16 == 0
+    full_logits_fp32 = 32768 * 128256 * 4
+    assert w16 < full_logits_fp32 / 4
+    assert w1 > full_logits_fp32
+
+
+@pytest.mark.parametrize("T,d,V,D,dt,code", [
+    (10, 8, 10, 0, 1, _lib.SBP_ERR_INVALID_ARG),
+    (10, 8, 10, 11, 1, _lib.SBP_ERR_INVALID_ARG),
+    (0, 8, 10, 1, 1, _lib.SBP_ERR_INVALID_ARG),
+    (10, 8, 10, 2, 7, _lib.SBP_ERR_INVALID_ARG),
+    (10, 12, 10, 2, 1, _lib.SBP_ERR_UNSUPPORTED),  # d % 8 for bf16
+    (10, 12, 10, 2, 0, _lib.SBP_OK),               # d % 4 is enough for fp32
+])
+def test_lmhead_size_checks(T, d, V, D, dt, code):
+    st, _ = _ws(sbp.load().sbp_lmhead_ce_workspace_size, T, d, V, D, dt)
+    assert st == code
+    if code:
+        assert sbp.load().sbp_last_error()
+
+
+def _lm_call(**kw):
+    a = dict(H=FAKE, W=FAKE, tg=FAKE, w=None, T=64, d=16, V=32, D=2, dt=1, red=0, acc=0,
+             loss=FAKE, tl=None, dH=FAKE, dW=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+    a.update(kw)
+    return sbp.load().sbp_lmhead_ce_fwd_bwd(a["H"], a["W"], a["tg"], a["w"], a["T"], a["d"],
+                                            a["V"], a["D"], a["dt"], a["red"], a["acc"],
+                                            a["loss"], a["tl"], a["dH"], a["dW"], a["ws"],
+                                            a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(dW=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(H=MIS), _lib.SBP_ERR_INVALID_ARG),
+    (dict(tl=MIS), _lib.SBP_ERR_INVALID_ARG),
+    (dict(red=5), _lib.SBP_ERR_INVALID_ARG),
+    (dict(D=65), _lib.SBP_ERR_INVALID_ARG),
+    (dict(wsb=16), _lib.SBP_ERR_WORKSPACE),
+    (dict(ws=None), _lib.SBP_ERR_WORKSPACE),
+])
+def test_lmhead_argument_errors(kw, code):
+    assert _lm_call(**kw) == code
+    assert sbp.load().sbp_last_error()
+
+
+def _attn_call(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dO=FAKE, O=None, lse=None, B=1, T=64, Hq=4, Hkv=2,
+             dh=64, scale=0.125, D=2, dt=1, acc=0, dQ=FAKE, dK=FAKE, dV=FAKE, ws=FAKE,
+             wsb=1 << 40, st=None)
+    a.update(kw)
+    return sbp.load().sbp_attn_bwd_chunked(a["Q"], a["K"], a["V"], a["dO"], a["O"], a["lse"],
+                                           a["B"], a["T"], a["Hq"], a["Hkv"], a["dh"], a["scale"],
+                                           a["D"], a["dt"], a["acc"], a["dQ"], a["dK"], a["dV"],
+                                           a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), _lib.SBP_ERR_INVALID_ARG),
+    (dict(dh=96), _lib.SBP_ERR_UNSUPPORTED),
+    (dict(D=0), _lib.SBP_ERR_INVALID_ARG),
+    (dict(D=65), _lib.SBP_ERR_INVALID_ARG),
+    (dict(O=FAKE), _lib.SBP_ERR_INVALID_ARG),      # O without lse
+    (dict(dK=MIS), _lib.SBP_ERR_INVALID_ARG),
+    (dict(dQ=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.SBP_ERR_INVALID_ARG),
+    (dict(wsb=0), _lib.SBP_ERR_WORKSPACE),
+])
+def test_attn_argument_errors(kw, code):
+    assert _attn_call(**kw) == code
+
+
+def _layer_call(desc_kw=None, D=2, **kw):
+    d = dict(T=64, d=64, Hq=4, Hkv=2, dh=64, F=128, eps=1e-6, dtype=1)
+    d.update(desc_kw or {})
+    desc = _lib.LayerDesc(d["T"], d["d"], d["Hq"], d["Hkv"], d["dh"], d["F"], d["eps"], d["dtype"])
+    w = _lib.LayerWeights(*[FAKE] * 9)
+    g = _lib.LayerGrads(*[FAKE] * 9)
+    for k, v in kw.get("wset", {}).items():
+        setattr(w, k, v)
+    a = dict(x=FAKE, dy=FAKE, dx=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update({k: v for k, v in kw.items() if k != "wset"})
+    return sbp.load().sbp_layer_bwd(C.byref(desc), a["x"], a["dy"], C.byref(w), D, 0, a["dx"],
+                                    C.byref(g), a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("desc_kw,D,kw,code", [
+    (dict(Hq=3), 2, {}, _lib.SBP_ERR_INVALID_ARG),
+    (dict(dh=32), 2, {}, _lib.SBP_ERR_UNSUPPORTED),
+    (dict(F=100), 2, {}, _lib.SBP_ERR_UNSUPPORTED),
+    ({}, 0, {}, _lib.SBP_ERR_INVALID_ARG),
+    ({}, 2, dict(wset={"W2": None}), _lib.SBP_ERR_INVALID_ARG),
+    ({}, 2, dict(wset={"Wq": MIS}), _lib.SBP_ERR_INVALID_ARG),
+    ({}, 2, dict(wsb=1), _lib.SBP_ERR_WORKSPACE),
+])
+def test_layer_argument_errors(desc_kw, D, kw, code):
+    assert _layer_call(desc_kw, D, **kw) == code
+
+
+def test_layer_workspace_is_chunk_sized():
+    lib = sbp.load()
+    sizes = []
+    for D in (1, 16):
+        desc = _lib.LayerDesc(65536, 4096, 32, 8, 128, 14336, 1e-6, 1)
+        out = C.c_size_t(0)
+        assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), D, C.byref(out)) == 0
+        sizes.append(out.value)
+    # MLP activations are per chunk: D = 16 needs far less than D = 1
+    assert sizes[1] < sizes[0] / 3

@@ -1,0 +1,159 @@
+"""GPU parity of sbp_lmhead_ce_fwd_bwd against the fp64 oracle.
+
+Normwise error max|gpu - ref| / max|ref| per output; fp32 mode <= 1e-4,
+bf16 mode <= 2e-2 (fp32 accumulation).  The loss is compared against
+max(|L|, (1/N) sum_t |c_t| l_t) because signed weights can cancel L.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import memory_efficient_exact_amd as sbp
+import oracle
+import synthetic
+from helpers import normwise
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _run(inp, D, reduction="mean_valid", accumulate=False, dW=None):
+    dev = torch.device("cuda:0")
+    H, W, tg = inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev)
+    w = None if inp.weights is None else inp.weights.to(dev)
+    loss, dH, dWo, tl = sbp.lmhead_ce(H, W, tg, w, D=D, reduction=reduction,
+                                      accumulate=accumulate, dW=dW, token_loss=True)
+    torch.cuda.synchronize()
+    return loss, dH, dWo, tl
+
+
+def _check(inp, D, dtype, reduction="mean_valid"):
+    loss, dH, dW, tl = _run(inp, D, reduction)
+    L, rH, rW, rtl, _ = oracle.lmhead_ce(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                         inp.targets.numpy(), synthetic.to_f64(inp.weights),
+                                         reduction)
+    tol = TOL[dtype]
+    y = inp.targets.numpy()
+    valid = y >= 0
+    N = max(1, int(valid.sum())) if reduction == "mean_valid" else 1
+    c = np.where(valid, 1.0 if inp.weights is None else inp.weights.numpy().astype(np.float64), 0.0)
+    den = max(abs(L), float(np.abs(c * rtl).sum()) / N, 1e-30)
+    e_loss = abs(loss.item() - L) / den
+    e_dH = normwise(dH.float().cpu().numpy(), rH)
+    e_dW = normwise(dW.cpu().numpy(), rW)
+    e_tl = normwise(tl.cpu().numpy(), rtl)
+    assert e_loss <= tol, (e_loss, loss.item(), L)
+    assert e_dH <= tol, e_dH
+    assert e_dW <= tol, e_dW
+    assert e_tl <= tol, e_tl
+    # ignored tokens give exactly zero dH rows
+    if (~valid).any():
+        assert (dH[torch.from_numpy(~valid).cuda()] == 0).all()
+    return dict(loss=e_loss, dH=e_dH, dW=e_dW, tl=e_tl)
+
+
+# ---- the small fp32 workload at its exact size, D swept ------------------
+@pytest.mark.parametrize("D", [4, 1, 2, 3, 256])
+def test_fp32_workload0_D_sweep(D):
+    inp = synthetic.workload_inputs(0)
+    _check(inp, D, "f32")
+
+
+# ---- ragged shapes spanning several tiles --------------------------------
+@pytest.mark.parametrize("dtype,T,d,V,D", [
+    ("f32", 333, 68, 1000, 3),
+    ("f32", 1000, 128, 777, 7),
+    ("bf16", 1000, 256, 5000, 3),
+    ("bf16", 517, 136, 2063, 1),
+    ("bf16", 2048, 512, 8192, 8),
+    ("bf16", 300, 64, 130, 300),   # D = T: one token per chunk
+])
+def test_ragged_parity(dtype, T, d, V, D):
+    inp = synthetic.lmhead_inputs(T, d, V, dtype, seed=T + d + V + D,
+                                  w_std=0.02 if dtype == "bf16" else None, ignore_frac=0.1)
+    _check(inp, D, dtype)
+
+
+def test_weighted_masked_packed_skips_chunks():
+    # the weighted-token workload's structure at a small size: 8 packed
+    # sequences, first quarter of each masked, per-sequence N(0,1) weights;
+    # D = 32 makes every fourth chunk fully masked (skipped on the device)
+    inp = synthetic.lmhead_inputs(8 * 128, 128, 3000, "bf16", seed=5, w_std=0.02, n_seq=8,
+                                  masked_frac=0.25, weighted=True)
+    _check(inp, 32, "bf16")
+
+
+def test_sum_reduction():
+    inp = synthetic.lmhead_inputs(400, 64, 900, "f32", seed=9, weighted=True, ignore_frac=0.2)
+    _check(inp, 5, "f32", reduction="sum")
+
+
+def test_all_tokens_ignored():
+    inp = synthetic.lmhead_inputs(256, 64, 512, "bf16", seed=3, w_std=0.02)
+    inp.targets[:] = -1
+    dW0 = torch.full((512, 64), 7.0, device="cuda:0")
+    loss, dH, dW, tl = _run(inp, 4, dW=dW0.clone())
+    assert loss.item() == 0.0 and (dH == 0).all() and (dW == 0).all() and (tl == 0).all()
+    loss, dH, dW, tl = _run(inp, 4, accumulate=True, dW=dW0.clone())
+    assert (dW == 7.0).all()
+
+
+def test_accumulate_adds_into_dW():
+    inp = synthetic.lmhead_inputs(512, 128, 1024, "f32", seed=4)
+    _, _, dW1, _ = _run(inp, 4)
+    _, _, dW2, _ = _run(inp, 2, accumulate=True, dW=dW1.clone())
+    assert normwise(dW2.cpu().numpy(), 2 * dW1.cpu().numpy()) < 1e-5
+
+
+def test_gpu_D_invariance_bf16():
+    inp = synthetic.lmhead_inputs(4096, 512, 4096, "bf16", seed=8, w_std=0.02)
+    outs = [_run(inp, D) for D in (1, 2, 16)]
+    base = outs[0]
+    for o in outs[1:]:
+        assert abs(o[0].item() - base[0].item()) <= 1e-5 * abs(base[0].item())
+        assert normwise(o[1].float().cpu().numpy(), base[1].float().cpu().numpy()) < 1e-2
+        assert normwise(o[2].cpu().numpy(), base[2].cpu().numpy()) < 1e-4
+
+
+# ---- full-size workloads: sampled rows + size-free identities ------------
+def _full_size(index, rows):
+    cfg = synthetic.WORKLOADS[index]
+    inp = synthetic.workload_inputs(index)
+    loss, dH, dW, tl = _run(inp, cfg["D"])
+    y = inp.targets.numpy()
+    N = int((y >= 0).sum())
+    rows = np.asarray(rows)
+    rH, rtl, _ = oracle.lmhead_ce_rows(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W), y,
+                                       synthetic.to_f64(inp.weights), rows, N)
+    e_dH = normwise(dH[torch.from_numpy(rows).cuda()].float().cpu().numpy(), rH)
+    e_tl = normwise(tl[torch.from_numpy(rows).cuda()].cpu().numpy(), rtl)
+    assert e_dH <= 2e-2, e_dH
+    assert e_tl <= 2e-2, e_tl
+    # sum_v (softmax - onehot) = 0 for every token, so the vocab sum of dW is 0
+    col = dW.double().sum(0).abs().max().item()
+    assert col <= 1e-3 * dW.abs().max().item() * math.sqrt(dW.shape[0]), col
+    # <dW, W> = sum_tv dZ_tv Z_tv = <dH, H>
+    a = (dW.double() * inp.W.to("cuda:0").double()).sum().item()
+    b = (dH.double() * inp.H.to("cuda:0").double()).sum().item()
+    assert abs(a - b) <= 2e-2 * max(abs(a), abs(b)), (a, b)
+    # loss from the per-token losses (rows checked above) and the weights
+    c = np.where(y >= 0, 1.0 if inp.weights is None else inp.weights.numpy(), 0.0)
+    L = float((c * tl.double().cpu().numpy()).sum()) / N
+    assert abs(loss.item() - L) <= 1e-4 * max(abs(L), 1e-3)
+    return inp
+
+
+def test_full_size_bf16_T32768_V128256():
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([[0, 1, 2047, 2048, 32767], rng.integers(0, 32768, 27)])
+    _full_size(1, rows)
+
+
+def test_full_size_weighted_T131072_V152064():
+    rng = np.random.default_rng(1)
+    rows = np.concatenate([[0, 4095, 4096, 16383, 16384 + 4096, 131071],
+                           rng.integers(0, 131072, 26)])
+    _full_size(4, rows)
