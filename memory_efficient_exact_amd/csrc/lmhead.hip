@@ -42,11 +42,11 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   s.T = T; s.d = d; s.V = V; s.D = D; s.dtype = dtype;
   s.esz = dtype == SBP_BF16 ? 2 : 4;
   s.Tcm = max_chunk_len(T, D);
-  s.Tcp = round_up(s.Tcm, 64);
-  s.Vp = round_up(V, 64);
+  s.Tcp = round_up(s.Tcm, 128);  // K granule of the bf16 GEMM
+  s.Vp = round_up(V, 128);
   // dH GEMM: few output tiles, long K = V.  Split K so that the launch has
   // ~1024 blocks (4 per CU); a function of the shape only.
-  const int64_t tiles = cdiv(s.Tcm, 128) * cdiv(d, 128);
+  const int64_t tiles = cdiv(s.Tcm, 256) * cdiv(d, 256);
   int64_t S = cdiv(1024, tiles);
   S = std::max<int64_t>(1, std::min<int64_t>(S, 16));
   S = std::min<int64_t>(S, std::max<int64_t>(1, s.Vp / 512));
@@ -140,7 +140,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     int64_t s0, e0;
     chunk_bounds(T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
-    const int64_t Tcp = round_up(Tc, 64);
+    const int64_t Tcp = round_up(Tc, 128);
     const int* act = w.prep.chunk_active + c;
 
     GemmParams g1;
@@ -150,7 +150,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g1.M = (int)Tc; g1.N = (int)V; g1.K = (int)d;
     g1.active = act;
     g1.m_fastest = 1;
-    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_128, str, "gemm_logits"));
+    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_256, str, "gemm_logits"));
 
     SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
     SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
@@ -166,7 +166,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g2.split_stride = s.Tcm * d;
     g2.active = act;
     g2.m_fastest = 1;
-    SBP_TRY(gemm_nt(dtype, EPI_PARTIAL, g2, GEMM_TILE_128, str, "gemm_dH"));
+    SBP_TRY(gemm_nt(dtype, EPI_PARTIAL, g2, GEMM_TILE_256, str, "gemm_dH"));
     SBP_TRY(splitk_reduce(dtype, w.part, s.Tcm * d, s.S, Tc, d, d, (char*)dH + s0 * d * s.esz, d,
                           act, str));
 
@@ -179,7 +179,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g3.beta_zero = w.prep.beta_zero + c;
     g3.active = act;
     g3.m_fastest = 0;
-    SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_128, str, "gemm_dW"));
+    SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_256, str, "gemm_dW"));
   }
   if (!accumulate) SBP_TRY(fill_zero_f32(dW, V * d, w.prep.none_active, str));
   SBP_TRY(loss_reduce(w.loss_part, T, w.prep.inv_norm, loss, str));
