@@ -72,16 +72,62 @@ def lmhead_setup(cfg, dev):
     return step, flops, inp, n_valid
 
 
+def attn_setup(cfg, dev):
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    inp = synthetic.workload_inputs(cfg["index"], T=cfg["T"])
+    Q, K, V, dO = (x.to(dev) for x in (inp.Q, inp.K, inp.V, inp.dO))
+    B, T, Hq, Hkv, dh, D = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["dh"], cfg["D"]
+    dK = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
+    dV = torch.empty_like(dK)
+    ws = torch.empty(sbp.attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        return sbp.attn_bwd(Q, K, V, dO, D=D, dK=dK, dV=dV, workspace=ws)
+
+    # algorithmic work: 7 causal units of 2*Hq*dh*T(T+1)/2*B (forward
+    # recompute 2, backward 5)
+    unit = 2.0 * Hq * dh * T * (T + 1) / 2 * B
+    return step, 7.0 * unit, inp
+
+
+def cpu_baseline_attn(inp, cfg, sample_heads=1):
+    """The oracle, untouched, on one q head's share of the same input."""
+    import math
+    import oracle
+    import synthetic
+    G = cfg["Hq"] // cfg["Hkv"]
+    Q = synthetic.to_f64(inp.Q[:, :, :sample_heads])
+    K = synthetic.to_f64(inp.K[:, :, :1])
+    V = synthetic.to_f64(inp.V[:, :, :1])
+    dO = synthetic.to_f64(inp.dO[:, :, :sample_heads])
+    t0 = time.perf_counter()
+    oracle.attn_bwd(Q, K, V, dO, 1.0 / math.sqrt(cfg["dh"]))
+    dt = time.perf_counter() - t0
+    scale = cfg["Hq"] / sample_heads
+    tokens = cfg["B"] * cfg["T"]
+    return {"value": tokens / (dt * scale), "unit": "tokens/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{sample_heads} of {cfg['Hq']} q heads (1 kv head), full T={cfg['T']}; "
+                      f"{dt:.1f} s, scaled by {scale:g} to all heads"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
 def cpu_baseline_lmhead(inp, cfg, sample):
     """The oracle, untouched, on the first `sample` tokens of the same input."""
     import numpy as np
     import oracle
     import synthetic
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = _blas_threads()
     H = synthetic.to_f64(inp.H[:sample])
     W = synthetic.to_f64(inp.W)
     y = inp.targets[:sample].numpy()
@@ -117,10 +163,14 @@ def main():
         cfg["D"] = args.D
     if args.T:
         cfg["T"] = args.T
-    if cfg["kind"] != "lmhead":
-        print("only the LM-head workloads are wired into bench.py so far", file=sys.stderr)
+    n_valid = None
+    if cfg["kind"] == "lmhead":
+        step, flops, inp, n_valid = lmhead_setup(cfg, dev)
+    elif cfg["kind"] == "attn":
+        step, flops, inp = attn_setup(cfg, dev)
+    else:
+        print("the decoder-layer workload is not wired into bench.py yet", file=sys.stderr)
         sys.exit(2)
-    step, flops, inp, n_valid = lmhead_setup(cfg, dev)
     dtype = cfg["dtype"]
 
     for _ in range(args.warmup):
@@ -146,7 +196,8 @@ def main():
     ms = max(ms_gpu, ms_wall)
     peak = torch.cuda.max_memory_allocated(dev)
     T = cfg["T"]
-    value = T / (ms / 1e3)
+    tokens = T * cfg.get("B", 1)
+    value = tokens / (ms / 1e3)
 
     # dominant kernel and its roofline (live hipEvent timing inside the call)
     dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
@@ -182,8 +233,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": cfg["name"], "T": T, "d": cfg["d"], "V": cfg["V"], "D": cfg["D"],
-                   "valid_tokens": n_valid},
+        "config": {k: v for k, v in cfg.items() if k not in ("kind", "name", "index", "dtype")}
+                  | {"workload": cfg["name"]} | ({"valid_tokens": n_valid} if n_valid else {}),
         "peak_hbm_bytes": int(peak),
         "peak_hbm_bytes_call": int(peak - base_mem),
         "mfma_frac_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
@@ -191,8 +242,11 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or (256 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
-        out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
+        if cfg["kind"] == "lmhead":
+            sample = args.cpu_sample or (256 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
+            out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
+        elif cfg["kind"] == "attn":
+            out["cpu_baseline"] = cpu_baseline_attn(inp, cfg)
     print(json.dumps(out), flush=True)
 
 

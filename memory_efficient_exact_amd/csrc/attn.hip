@@ -1,8 +1,549 @@
 // sbp_attn_bwd_chunked: causal GQA attention backward, chunked over queries.
+//
+// StreamBP skill page, "Architecture Overview" (causal structure
+// exploitation) and "Practical Guidance" (masks across chunk boundaries,
+// causal masking): query chunk c = [s, e) reads keys/values [0, e) only, and
+// inside it no key block above the diagonal is visited.  Per chunk, in
+// reverse order:
+//   attn_fwd_kernel   per (128-query tile, q head): S^T = K Q^T over the
+//                     causal prefix, online softmax per query, O^T += V^T P^T;
+//                     writes LSE and Delta = rowsum(dO * O) (and O if asked).
+//   attn_dkdv_kernel  per (128-key tile, kv head): for every q head of the
+//                     group and every query tile of the chunk that sees the
+//                     keys: S = Q K^T, P, dP = dO V^T, dS = P (dP - Delta),
+//                     dV += P^T dO, dK += dS^T Q; fp32 read-modify-write.
+//   attn_dq_kernel    per (128-query tile, q head): S^T, dP^T over key tiles
+//                     up to the diagonal, dQ += dS K.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64): the A operand of
+// lane l holds row l%32 and 8 consecutive k of group l/32; B likewise by
+// column; the 32x32 fp32 result has lane l holding column l%32 and rows
+// 8*(e/4) + 4*(l/32) + e%4, e = 0..15.  Because that result column is the
+// lane, a score block computed in one orientation is already, element by
+// element, the A (or B) operand of the next product in the other
+// orientation: elements 8i..8i+7 of a lane form the k16 step i, whose k
+// index e maps to the block row above.  The matching operand of that product
+// (dO, Q, K or V with the contraction over its rows) is read transposed from
+// LDS with ds_read_b64_tr_b16: within each 16-lane group, lane i returns
+// element i%4 of the 8-byte chunks fetched by lanes i/4 + 4m (m = 0..3), so
+// 16 lanes that fetch 4 rows x 16 columns receive one column each, 4 rows
+// deep.  LDS tiles are rows of dh bf16 with 16-byte chunk c of row r stored
+// at c ^ f(r), f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps both the
+// 16-byte row reads (8 rows) and the transposed reads (4 rows x 32 bytes)
+// free of bank conflicts.
 #include "common.h"
 #include "kernels.h"
 
 namespace sbp {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define SBP_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Byte offset of element (r, col) in a swizzled [rows][DH] bf16 LDS tile.
+template <int DH>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  const int c = col >> 3;
+  return r * (DH * 2) + ((c ^ swz(r)) << 4) + ((col & 7) << 1);
+}
+
+// Copy rows [0, 64) of a [rows][DH] bf16 tile from global (row pitch ld
+// elements, rows >= nvalid zero-filled) into a swizzled LDS tile.
+template <int DH>
+__device__ __forceinline__ void load_tile64(char* lds, const bf16_t* __restrict__ src, int64_t ld,
+                                            int nvalid, int tid) {
+  constexpr int CPR = DH / 8;  // 16-byte chunks per row
+  constexpr int TOTAL = 64 * CPR;
+#pragma unroll
+  for (int i = tid; i < TOTAL; i += 256) {
+    const int r = i / CPR, c = i % CPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nvalid) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + c * 8);
+    *reinterpret_cast<uint4*>(lds + r * (DH * 2) + ((c ^ swz(r)) << 4)) = v;
+  }
+}
+
+// 16-byte row read: row rbase + l%32, k16 step ks (columns 16ks + 8(l/32) ..).
+template <int DH>
+__device__ __forceinline__ uint4 lds_row_frag(const char* lds, int rbase, int ks, int lane) {
+  const int r = rbase + (lane & 31);
+  const int c = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const uint4*>(lds + r * (DH * 2) + ((c ^ swz(r)) << 4));
+}
+
+// Transposed read: 8 bf16 of column cbase + l%32 at rows
+// rbase + 4(l/32) + {0..3} and rbase + 8 + 4(l/32) + {0..3}.
+template <int DH>
+__device__ __forceinline__ uint4 lds_tr_frag(const char* lds, int rbase, int cbase, int lane) {
+  const int G = (lane >> 4) & 3, j = lane & 15;
+  const int r = rbase + 4 * (G >> 1) + (j >> 2);
+  const int col = cbase + (G & 1) * 16 + 4 * (j & 3);
+  const SBP_LDS char* base = (const SBP_LDS char*)lds;
+  i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(base + tile_off<DH>(r, col)));
+  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(base + tile_off<DH>(r + 8, col)));
+  uint4 u;
+  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return u;
+}
+
+// Elements 8i..8i+7 of a result block as a bf16 operand (k16 step i).
+__device__ __forceinline__ uint4 pack_frag(const f32x16_t& a, int i) {
+  uint4 u;
+  u.x = (uint32_t)f2bf(a[8 * i + 0]) | ((uint32_t)f2bf(a[8 * i + 1]) << 16);
+  u.y = (uint32_t)f2bf(a[8 * i + 2]) | ((uint32_t)f2bf(a[8 * i + 3]) << 16);
+  u.z = (uint32_t)f2bf(a[8 * i + 4]) | ((uint32_t)f2bf(a[8 * i + 5]) << 16);
+  u.w = (uint32_t)f2bf(a[8 * i + 6]) | ((uint32_t)f2bf(a[8 * i + 7]) << 16);
+  return u;
+}
+
+__device__ __forceinline__ f32x16_t mma(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Row of element e of a result block for this lane.
+__device__ __forceinline__ int crow(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// 16-byte global fragment of a [rows][DH] matrix (row pitch ld): row r,
+// k16 step ks, group g: columns 16 ks + 8 g .. +8; zero past nrows.
+template <int DH>
+__device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t ld, int r, int nrows,
+                                          int ks, int g) {
+  if (r >= nrows) return make_uint4(0, 0, 0, 0);
+  return *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + ks * 16 + g * 8);
+}
+
+struct AttnArgs {
+  const bf16_t* Q;   // [B, T, Hq, dh]
+  const bf16_t* K;   // [B, T, Hkv, dh]
+  const bf16_t* V;
+  const bf16_t* dO;  // [B, T, Hq, dh] (may be null for the forward)
+  bf16_t* O;         // forward output (optional) [B, T, Hq, dh]
+  bf16_t* dQ;        // [B, T, Hq, dh]
+  float* dK;         // [B, T, Hkv, dh]
+  float* dV;
+  // per-row statistics of the chunk: element (b, h, t) at
+  // base + b*sb + h*sh + (t - s)*st   (t absolute, s = chunk start)
+  float* lse;
+  int64_t lse_sb, lse_sh, lse_st;
+  float* delta;
+  int64_t dl_sb, dl_sh, dl_st;
+  int T, Hq, Hkv, G;
+  int s, e;          // chunk [s, e)
+  float scale;
+  int beta;          // dK/dV: 1 = add into, 0 = overwrite
+};
+
+// ---------------------------------------------------------------------------
+// Forward statistics.  Block: 4 waves, 128 queries (32 per wave), one q head.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int NB = DH / 32;   // 32-wide dh blocks
+  constexpr int KS = DH / 16;   // k16 steps over dh
+  __shared__ __attribute__((aligned(16))) char kt[2][64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char vt[2][64 * DH * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const int q0 = a.s + blockIdx.x * 128;            // first query of the block
+  const int qw = q0 + wave * 32;                    // first query of the wave
+  const int qcol = qw + (lane & 31);                // this lane's query
+  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
+  const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+
+  // Q^T as the B operand of S^T = K Q^T: column = query, k = dh
+  uint4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = glb_frag<DH>(Qb, ldq, qcol, a.e, ks, lane >> 5);
+
+  f32x16_t ot[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) ot[i] = f32x16_t{};
+  float m = -INFINITY, l = 0.f;
+  const float c2 = a.scale * kLog2e;
+
+  const int kend = min(q0 + 128, a.e);              // keys [0, kend)
+  const int ntiles = (kend + 63) / 64;
+  load_tile64<DH>(kt[0], Kb, ldk, kend, tid);
+  load_tile64<DH>(vt[0], Vb, ldk, kend, tid);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int k0 = t * 64;
+    if (t + 1 < ntiles) {
+      load_tile64<DH>(kt[cur ^ 1], Kb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
+      load_tile64<DH>(vt[cur ^ 1], Vb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
+    }
+    if (k0 <= qw + 31) {  // some key of the tile is visible to this wave
+      f32x16_t st[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          st[kb] = mma(lds_row_frag<DH>(kt[cur], kb * 32, ks, lane), qf[ks], st[kb]);
+      }
+      // scale, mask (key > query), online softmax along the keys (rows)
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + crow(e, lane);
+          const float v = (key <= qcol) ? st[kb][e] * c2 : -INFINITY;
+          st[kb][e] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m, mt);
+      const float alpha = exp2f(m - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(st[kb][e] - mn);
+          st[kb][e] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l = l * alpha + ls;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) ot[i] *= alpha;
+      // O^T[dh, q] += V^T[dh, key] P^T[key, q]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 pb = pack_frag(st[kb], i);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            ot[nb] = mma(lds_tr_frag<DH>(vt[cur], kb * 32 + 16 * i, nb * 32, lane), pb, ot[nb]);
+        }
+    }
+    __syncthreads();
+  }
+  if (qcol >= a.e) return;
+  const float inv = 1.f / l;
+  const float lse = (m + log2f(l)) * kLn2;
+  const int64_t row = (int64_t)b * a.T + qcol;
+  // Delta = sum_dh dO * O, O from the fp32 accumulator; O written if asked
+  float dsum = 0.f;
+  const bf16_t* dorow = a.dO ? a.dO + row * ldq + (int64_t)h * DH : nullptr;
+  bf16_t* orow = a.O ? a.O + row * ldq + (int64_t)h * DH : nullptr;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = nb * 32 + 8 * q4 + 4 * (lane >> 5);  // rows of elements 4q4 .. 4q4+3
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = ot[nb][4 * q4 + j] * inv;
+      if (dorow) {
+        const uint2 u = *reinterpret_cast<const uint2*>(dorow + d0);
+        dsum += o[0] * bf2f((bf16_t)(u.x & 0xffff)) + o[1] * bf2f((bf16_t)(u.x >> 16)) +
+                o[2] * bf2f((bf16_t)(u.y & 0xffff)) + o[3] * bf2f((bf16_t)(u.y >> 16));
+      }
+      if (orow) {
+        uint2 w;
+        w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+        w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + d0) = w;
+      }
+    }
+  dsum += __shfl_xor(dsum, 32, 64);
+  if (lane < 32) {
+    a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(qcol - a.s) * a.lse_st] = lse;
+    if (a.dO) a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(qcol - a.s) * a.dl_st] = dsum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO * O) from a given O (dtype), one wave per (row, head).
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_t* __restrict__ O) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over Tc * Hq rows of batch row b
+  const int Tc = a.e - a.s;
+  if (idx >= (int64_t)Tc * a.Hq) return;
+  const int b = blockIdx.y;
+  const int h = (int)(idx % a.Hq);
+  const int t = a.s + (int)(idx / a.Hq);
+  const int64_t off = (((int64_t)b * a.T + t) * a.Hq + h) * DH;
+  float s = 0.f;
+  for (int d = lane; d < DH; d += 64) s += bf2f(a.dO[off + d]) * bf2f(O[off + d]);
+  s = wave_sum(s);
+  if (lane == 0) a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(t - a.s) * a.dl_st] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Block: 4 waves, 128 keys (32 per wave), one kv head; loops over
+// the G q heads of the group and the 64-query tiles of the chunk.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  __shared__ __attribute__((aligned(16))) char qt[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char ot[64 * DH * 2];  // dO tile
+  __shared__ float s_lse[64], s_dl[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kv = blockIdx.y, b = blockIdx.z;
+  const int kbase = blockIdx.x * 128;
+  const int kw = kbase + wave * 32;
+  const int kcol = kw + (lane & 31);  // this lane's key (result column)
+  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
+  const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  // K, V of this wave's keys as B operands (column = key, k = dh)
+  uint4 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = glb_frag<DH>(Kb, ldk, kcol, a.T, ks, lane >> 5);
+    vf[ks] = glb_frag<DH>(Vb, ldk, kcol, a.T, ks, lane >> 5);
+  }
+  f32x16_t dk[NB], dv[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    dk[i] = f32x16_t{};
+    dv[i] = f32x16_t{};
+  }
+  const float c2 = a.scale * kLog2e;
+  // query tiles that see any key of the block: queries >= kbase
+  const int qstart = max(a.s, kbase & ~63);
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int h = kv * a.G + hh;
+    const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+    const bf16_t* Ob = a.dO + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+    const float* lrow = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh;
+    const float* drow = a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh;
+    for (int q0 = qstart; q0 < a.e; q0 += 64) {
+      __syncthreads();
+      load_tile64<DH>(qt, Qb + (int64_t)q0 * ldq, ldq, a.e - q0, tid);
+      load_tile64<DH>(ot, Ob + (int64_t)q0 * ldq, ldq, a.e - q0, tid);
+      if (tid < 64) {
+        const int q = q0 + tid;
+        const bool ok = q < a.e;
+        s_lse[tid] = ok ? lrow[(int64_t)(q - a.s) * a.lse_st] * kLog2e : INFINITY;
+        s_dl[tid] = ok ? drow[(int64_t)(q - a.s) * a.dl_st] : 0.f;
+      }
+      __syncthreads();
+      if (q0 + 63 < kw) continue;  // every query of the tile precedes this wave's keys
+      // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two row blocks
+      f32x16_t sp[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sp[qb] = f32x16_t{};
+        dp[qb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sp[qb] = mma(lds_row_frag<DH>(qt, qb * 32, ks, lane), kf[ks], sp[qb]);
+          dp[qb] = mma(lds_row_frag<DH>(ot, qb * 32, ks, lane), vf[ks], dp[qb]);
+        }
+      }
+      // P = exp(s S - LSE) (0 where key > query), dS = P (dP - Delta)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = qb * 32 + crow(e, lane);
+          const float p = (kcol <= q0 + r) ? exp2f(sp[qb][e] * c2 - s_lse[r]) : 0.f;
+          sp[qb][e] = p;
+          dp[qb][e] = p * (dp[qb][e] - s_dl[r]);
+        }
+      // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 pa = pack_frag(sp[qb], i);
+          const uint4 da = pack_frag(dp[qb], i);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            dv[nb] = mma(pa, lds_tr_frag<DH>(ot, qb * 32 + 16 * i, nb * 32, lane), dv[nb]);
+            dk[nb] = mma(da, lds_tr_frag<DH>(qt, qb * 32 + 16 * i, nb * 32, lane), dk[nb]);
+          }
+        }
+    }
+  }
+  // result blocks [32 keys x 32 dh]: lane = dh column, rows = keys
+  float* dKb = a.dK + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  float* dVb = a.dV + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kw + crow(e, lane);
+      if (key >= a.T) continue;
+      const int64_t off = (int64_t)key * ldk + nb * 32 + (lane & 31);
+      const float gk = a.scale * dk[nb][e], gv = dv[nb][e];
+      if (a.beta) {
+        dKb[off] += gk;
+        dVb[off] += gv;
+      } else {
+        dKb[off] = gk;
+        dVb[off] = gv;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Block: 4 waves, 128 queries (32 per wave), one q head; key tiles of
+// 64 up to the diagonal.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  __shared__ __attribute__((aligned(16))) char kt[2][64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char vt[2][64 * DH * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const int q0 = a.s + blockIdx.x * 128;
+  const int qw = q0 + wave * 32;
+  const int qcol = qw + (lane & 31);
+  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
+  const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  const bf16_t* Ob = a.dO + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  uint4 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = glb_frag<DH>(Qb, ldq, qcol, a.e, ks, lane >> 5);
+    of[ks] = glb_frag<DH>(Ob, ldq, qcol, a.e, ks, lane >> 5);
+  }
+  const bool qok = qcol < a.e;
+  const float c2 = a.scale * kLog2e;
+  const float lse2 = qok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(qcol - a.s) * a.lse_st] * kLog2e : INFINITY;
+  const float dl = qok ? a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(qcol - a.s) * a.dl_st] : 0.f;
+  f32x16_t dq[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) dq[i] = f32x16_t{};
+
+  const int kend = min(q0 + 128, a.e);
+  const int ntiles = (kend + 63) / 64;
+  load_tile64<DH>(kt[0], Kb, ldk, kend, tid);
+  load_tile64<DH>(vt[0], Vb, ldk, kend, tid);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int k0 = t * 64;
+    if (t + 1 < ntiles) {
+      load_tile64<DH>(kt[cur ^ 1], Kb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
+      load_tile64<DH>(vt[cur ^ 1], Vb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
+    }
+    if (k0 <= qw + 31) {
+      f32x16_t st[2], dpt[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = f32x16_t{};
+        dpt[kb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          st[kb] = mma(lds_row_frag<DH>(kt[cur], kb * 32, ks, lane), qf[ks], st[kb]);
+          dpt[kb] = mma(lds_row_frag<DH>(vt[cur], kb * 32, ks, lane), of[ks], dpt[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + crow(e, lane);
+          const float p = (key <= qcol) ? exp2f(st[kb][e] * c2 - lse2) : 0.f;
+          dpt[kb][e] = p * (dpt[kb][e] - dl);
+        }
+      // dQ[q, dh] += dS[q, key] K[key, dh]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 da = pack_frag(dpt[kb], i);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dq[nb] = mma(da, lds_tr_frag<DH>(kt[cur], kb * 32 + 16 * i, nb * 32, lane), dq[nb]);
+        }
+    }
+    __syncthreads();
+  }
+  // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries
+  bf16_t* dQb = a.dQ + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int q = qw + crow(e, lane);
+      if (q >= a.e) continue;
+      dQb[(int64_t)q * ldq + nb * 32 + (lane & 31)] = f2bf(a.scale * dq[nb][e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers (shared with the decoder layer).
+// ---------------------------------------------------------------------------
+static double attn_pairs(int s, int e) {
+  // (query, key) pairs with key <= query for queries [s, e)
+  return 0.5 * ((double)e * (e + 1) - (double)s * (s + 1));
+}
+
+sbp_status attn_fwd(const AttnArgs& a, int dh, int B, hipStream_t st) {
+  const int Tc = a.e - a.s;
+  dim3 grid((unsigned)cdiv(Tc, 128), (unsigned)a.Hq, (unsigned)B);
+  ProfScope prof("attn_fwd", st, 4.0 * dh * a.Hq * B * attn_pairs(a.s, a.e), 0.0);
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(256), 0, st, a);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+sbp_status attn_delta(const AttnArgs& a, const void* O, int dh, int B, hipStream_t st) {
+  const int Tc = a.e - a.s;
+  const int64_t rows = (int64_t)Tc * a.Hq;
+  dim3 grid((unsigned)cdiv(rows, 4), (unsigned)B);
+  ProfScope prof("attn_delta", st, 0.0, 4.0 * rows * B * dh);
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_delta_kernel<128>, grid, dim3(256), 0, st, a, (const bf16_t*)O);
+  else
+    hipLaunchKernelGGL(attn_delta_kernel<64>, grid, dim3(256), 0, st, a, (const bf16_t*)O);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st) {
+  const double pairs = attn_pairs(a.s, a.e) * a.Hq * B;
+  {
+    dim3 grid((unsigned)cdiv(a.e, 128), (unsigned)a.Hkv, (unsigned)B);
+    ProfScope prof("attn_dkdv", st, 8.0 * dh * pairs, 0.0);
+    if (dh == 128)
+      hipLaunchKernelGGL(attn_dkdv_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_dkdv_kernel<64>, grid, dim3(256), 0, st, a);
+    SBP_LAUNCH_CHECK();
+  }
+  {
+    dim3 grid((unsigned)cdiv(a.e - a.s, 128), (unsigned)a.Hq, (unsigned)B);
+    ProfScope prof("attn_dq", st, 6.0 * dh * pairs, 0.0);
+    if (dh == 128)
+      hipLaunchKernelGGL(attn_dq_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_dq_kernel<64>, grid, dim3(256), 0, st, a);
+    SBP_LAUNCH_CHECK();
+  }
+  return SBP_OK;
+}
+
 namespace {
 
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
@@ -14,16 +555,17 @@ sbp_status attn_check(int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
   if (D < 1 || D > T) return set_error(SBP_ERR_INVALID_ARG, "need 1 <= D <= T (D=%d, T=%lld)", D, (long long)T);
   if (Hq % Hkv) return set_error(SBP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (dh != 64 && dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", dh);
-  if (B * T > (1ll << 30)) return set_error(SBP_ERR_UNSUPPORTED, "B*T out of supported range");
+  if (dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "attention backward is implemented for bf16 only");
+  if (T > (1ll << 30) || B > 65535 || Hq > 65535) return set_error(SBP_ERR_UNSUPPORTED, "size out of supported range");
   return SBP_OK;
 }
 
 size_t attn_ws(int64_t B, int64_t T, int32_t Hq, int32_t dh, int32_t D, int32_t dtype) {
-  // per query chunk: O_c (dtype), LSE_c and Delta_c (fp32)
+  (void)dh;
+  (void)dtype;
+  // per query chunk: LSE_c and Delta_c, fp32 [B, Hq, T_c]
   const int64_t Tcm = max_chunk_len(T, D);
-  const size_t esz = dtype == SBP_BF16 ? 2 : 4;
   WsPlan P;
-  P.take(esz * B * Tcm * Hq * dh);
   P.take(sizeof(float) * B * Tcm * Hq);
   P.take(sizeof(float) * B * Tcm * Hq);
   return round_up((int64_t)P.off, 256);
@@ -65,7 +607,36 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
   const size_t need = attn_ws(B, T, Hq, dh, D, dtype);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-  (void)accumulate;
-  (void)stream;
-  return set_error(SBP_ERR_UNSUPPORTED, "attention backward kernels are not built in this version");
+  hipStream_t str = (hipStream_t)stream;
+  const int64_t Tcm = max_chunk_len(T, D);
+  WsPlan P;
+  P.base = (char*)ws;
+  float* w_lse = (float*)P.take(sizeof(float) * B * Tcm * Hq);
+  float* w_dl = (float*)P.take(sizeof(float) * B * Tcm * Hq);
+  for (int32_t c = D - 1; c >= 0; --c) {
+    int64_t s0, e0;
+    chunk_bounds(T, D, c, &s0, &e0);
+    AttnArgs a;
+    a.Q = (const bf16_t*)Q; a.K = (const bf16_t*)K; a.V = (const bf16_t*)V;
+    a.dO = (const bf16_t*)dO; a.O = nullptr; a.dQ = (bf16_t*)dQ; a.dK = dK; a.dV = dV;
+    a.T = (int)T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.s = (int)s0; a.e = (int)e0;
+    a.scale = scale;
+    // the last chunk (processed first) reaches every key: it overwrites
+    a.beta = (accumulate || c != D - 1) ? 1 : 0;
+    a.delta = w_dl; a.dl_sb = (int64_t)Hq * Tcm; a.dl_sh = Tcm; a.dl_st = 1;
+    if (lse) {
+      // caller's statistics [B, T, Hq], offset to the chunk start
+      a.lse = const_cast<float*>(lse) + s0 * Hq;
+      a.lse_sb = T * Hq; a.lse_sh = 1; a.lse_st = Hq;
+      st = attn_delta(a, O, dh, (int)B, str);
+    } else {
+      a.lse = w_lse; a.lse_sb = (int64_t)Hq * Tcm; a.lse_sh = Tcm; a.lse_st = 1;
+      st = attn_fwd(a, dh, (int)B, str);
+    }
+    if (st != SBP_OK) return st;
+    st = attn_bwd_chunk(a, dh, (int)B, str);
+    if (st != SBP_OK) return st;
+  }
+  return SBP_OK;
 }

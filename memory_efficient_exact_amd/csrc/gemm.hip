@@ -403,6 +403,230 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_256_kernel(GemmParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 4-stage ring variant: the same 256 x 256 tile and 32x32x16 MFMA, but K is
+// staged 32 wide (32 KB per stage) in four distinct LDS arrays, so three
+// stages (96 KB) are in flight while one is consumed.  Rows are 4 x 16-byte
+// chunks; chunk c of row r sits at c ^ ((r >> 1) & 3).  Each wave fetches
+// 128 rows of one operand with 8 DMA instructions per stage (16 rows each).
+// ---------------------------------------------------------------------------
+struct RingFrag {
+  uint4 a[4], b[4];
+};
+
+// Fragments of k16 step ks (0 or 1) of a 32-wide stage in LDS tile L.
+__device__ __forceinline__ void ring_load(const uint4* __restrict__ L, int ks, int wm, int wn, int lane,
+                                          RingFrag& f) {
+  constexpr int BM = 256, WT = 128;
+  const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * WT + i * 32 + (lane & 31);
+    f.a[i] = L[r * 4 + (ch ^ ((r >> 1) & 3))];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = BM + wn * WT + i * 32 + (lane & 31);
+    f.b[i] = L[r * 4 + (ch ^ ((r >> 1) & 3))];
+  }
+}
+
+__device__ __forceinline__ void ring_mma(const RingFrag& f, f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, f.a[fm]), __builtin_bit_cast(bf16x8_t, f.b[fn]), acc[fm][fn],
+          0, 0, 0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, BK = 32, WT = 128;
+  __shared__ uint4 L0[(BM + BN) * 4];
+  __shared__ uint4 L1[(BM + BN) * 4];
+  __shared__ uint4 L2[(BM + BN) * 4];
+  __shared__ uint4 L3[(BM + BN) * 4];
+  if (p.active && *p.active == 0) return;
+  int tm, tn, split;
+  tile_coords(p, tm, tn, split);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb = split * p.k_per_split;
+  const int ke = min(p.K, kb + p.k_per_split);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int opnd = wave >> 1;
+  const int rbase = (wave & 1) * 128;
+  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
+  const int64_t ld = opnd ? p.ldb : p.lda;
+  const int lim = opnd ? p.N : p.M;
+  const int r0 = (opnd ? n0 : m0) + rbase + (lane >> 2);
+  const int lds_row0 = opnd * BM + rbase;
+
+  auto issue = [&](uint4* L, int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int gr = r0 + j * 16;
+      gr = gr < lim ? gr : lim - 1;
+      const bf16_t* g = X + (int64_t)gr * ld + k0 + chunk * 8;
+      __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
+                                       (SBP_AS3 void*)&L[(lds_row0 + j * 16) * 4], 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  // every K range is a multiple of 4 * BK (checked by the launcher)
+  const int nk = ke > kb ? (ke - kb) / BK : 0;
+  // nk is 0 or a multiple of 4; stage t lives in buffer t % 4.  Software
+  // pipeline, per stage t:
+  //   read k16 step 1 of stage t            (MFMAs of step 0 cover it)
+  //   MFMAs of step 0 of stage t
+  //   wait for stage t+1's DMA, bare barrier (everyone's stage t+1 landed;
+  //     everyone finished reading stage t-1, whose buffer takes stage t+3)
+  //   issue stage t+3
+  //   read k16 step 0 of stage t+1          (MFMAs of step 1 cover it)
+  //   MFMAs of step 1 of stage t
+  // The refill is unconditional -- past the end it re-fetches the last
+  // stage into a buffer nobody reads -- so every step has the same wait
+  // count.  sched_barrier(0) keeps the fragment reads ahead of the MFMAs.
+  // Waits use the builtin (gfx9 encoding, vmcnt in bits 3:0 and 15:14) so
+  // the compiler's own wait insertion knows which stages have landed.
+  RingFrag f0, f1;
+  if (nk > 0) {
+    issue(L0, kb);
+    issue(L1, kb + BK);
+    issue(L2, kb + 2 * BK);
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    ring_load(L0, 0, wm, wn, lane, f0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+  auto step = [&](const uint4* Lc, const uint4* Lnext, uint4* Lrefill, int t) {
+    ring_load(Lc, 1, wm, wn, lane, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_mma(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): stage t+1 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(Lrefill, kb + min(t + 3, nk - 1) * BK);
+    ring_load(Lnext, 0, wm, wn, lane, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_mma(f1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // lgkmcnt(0): the next stage's step-0 fragments, read 16 MFMAs ago, have
+    // landed; stating it keeps the compiler from waiting on the step-1 reads
+    // it issues next before starting the step-0 MFMAs.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  };
+  for (int it = 0; it < nk; it += 4) {
+    step(L0, L1, L3, it);
+    step(L1, L2, L0, it + 1);
+    step(L2, L3, L1, it + 2);
+    step(L3, L0, L2, it + 3);
+  }
+
+  // Epilogue through LDS (L0|L1 and L2|L3 are adjacent 64 KB halves of the
+  // static LDS block only by accident of layout, so each wave uses one 32 KB
+  // array on its own): 32 rows x 128 columns per pass, 4 passes.
+  __syncthreads();
+  float* W = reinterpret_cast<float*>(wave == 0 ? L0 : wave == 1 ? L1 : wave == 2 ? L2 : L3);
+  float beta = (float)p.beta;
+  if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
+  const bool vec_ok = (p.ldc % 4 == 0) && (EPI != EPI_OUT_RESID || p.ldr % 4 == 0);
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int lr = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        W[lr * 128 + fn * 32 + (lane & 31)] = acc[fm][fn][e];
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int lr = it * 2 + (lane >> 5);
+      const int lc = (lane & 31) * 4;
+      const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + lc]);
+      float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
+      const int row = m0 + wm * WT + fm * 32 + lr;
+      const int col = n0 + wn * WT + lc;
+      if (row >= p.M || col >= p.N) continue;
+      const int64_t off = (int64_t)row * p.ldc + col;
+      if (vec_ok && col + 4 <= p.N) {
+        if constexpr (EPI == EPI_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_F32_ACC) {
+          float4* c = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off);
+          if (beta != 0.f) {
+            const float4 o = *c;
+            *c = make_float4(v[0] + beta * o.x, v[1] + beta * o.y, v[2] + beta * o.z, v[3] + beta * o.w);
+          } else {
+            *c = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+          if constexpr (EPI == EPI_OUT_RESID) {
+            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.R) + (int64_t)row * p.ldr + col);
+            v[0] += bf2f((bf16_t)(r.x & 0xffff)); v[1] += bf2f((bf16_t)(r.x >> 16));
+            v[2] += bf2f((bf16_t)(r.y & 0xffff)); v[3] += bf2f((bf16_t)(r.y >> 16));
+          }
+          uint2 u;
+          u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (col + j >= p.N) break;
+          if constexpr (EPI == EPI_F32) {
+            reinterpret_cast<float*>(p.C)[off + j] = v[j];
+          } else if constexpr (EPI == EPI_PARTIAL) {
+            reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
+          } else if constexpr (EPI == EPI_F32_ACC) {
+            float* c = reinterpret_cast<float*>(p.C) + off + j;
+            *c = (beta != 0.f) ? (v[j] + beta * *c) : v[j];
+          } else if constexpr (EPI == EPI_OUT) {
+            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j]);
+          } else {
+            const float r = Elem<bf16_t>::load(reinterpret_cast<const bf16_t*>(p.R), (int64_t)row * p.ldr + col + j);
+            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j] + r);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+static void launch_bf16_ring(int epi, GemmParams p, hipStream_t st) {
+  p.tiles_m = (int)cdiv(p.M, 256);
+  p.tiles_n = (int)cdiv(p.N, 256);
+  const int grid = p.tiles_m * p.tiles_n * p.k_split;
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32>, dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_F32_ACC: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32_ACC>, dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_OUT: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT>, dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_OUT_RESID: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT_RESID>, dim3(grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_PARTIAL>, dim3(grid), dim3(256), 0, st, p); break;
+  }
+}
+
 static void launch_bf16_256(int epi, GemmParams p, hipStream_t st) {
   p.tiles_m = (int)cdiv(p.M, 256);
   p.tiles_n = (int)cdiv(p.N, 256);
@@ -443,7 +667,10 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
                        (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : 4.0 * p.k_split);
   ProfScope prof(name, st, flops, bytes);
   if (dtype == SBP_BF16) {
-    if (tile == GEMM_TILE_256 && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
+    if (tile == GEMM_TILE_RING && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
+        p.ldb % 8 == 0)
+      launch_bf16_ring(epi, p, st);
+    else if (tile == GEMM_TILE_256 && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
         p.ldb % 8 == 0)
       launch_bf16_256(epi, p, st);
     else if (tile == GEMM_TILE_256_REG)

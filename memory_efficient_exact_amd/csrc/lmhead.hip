@@ -150,7 +150,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g1.M = (int)Tc; g1.N = (int)V; g1.K = (int)d;
     g1.active = act;
     g1.m_fastest = 1;
-    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_256, str, "gemm_logits"));
+    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
 
     SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
     SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
@@ -166,7 +166,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g2.split_stride = s.Tcm * d;
     g2.active = act;
     g2.m_fastest = 1;
-    SBP_TRY(gemm_nt(dtype, EPI_PARTIAL, g2, GEMM_TILE_256, str, "gemm_dH"));
+    SBP_TRY(gemm_nt(dtype, EPI_PARTIAL, g2, GEMM_TILE_RING, str, "gemm_dH"));
     SBP_TRY(splitk_reduce(dtype, w.part, s.Tcm * d, s.S, Tc, d, d, (char*)dH + s0 * d * s.esz, d,
                           act, str));
 
@@ -179,7 +179,7 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g3.beta_zero = w.prep.beta_zero + c;
     g3.active = act;
     g3.m_fastest = 0;
-    SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_256, str, "gemm_dW"));
+    SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_RING, str, "gemm_dW"));
   }
   if (!accumulate) SBP_TRY(fill_zero_f32(dW, V * d, w.prep.none_active, str));
   SBP_TRY(loss_reduce(w.loss_part, T, w.prep.inv_norm, loss, str));
