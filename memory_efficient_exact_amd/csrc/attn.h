@@ -1,0 +1,44 @@
+// Internal interface of the attention kernels (shared by the attention
+// entry point and the decoder layer).
+#pragma once
+
+#include "common.h"
+
+namespace sbp {
+
+struct AttnArgs {
+  // Query-side arrays (Q, dO, O, dQ) hold rows t - qoff of batch row b at
+  // p + b * q_bs + (t - qoff) * ld + head * dh: the whole sequence
+  // (qoff = 0, q_bs = T * ld) or just the current chunk (qoff = s).
+  const bf16_t* Q;   // [B, T, Hq, dh]
+  const bf16_t* K;   // [B, T, Hkv, dh]
+  const bf16_t* V;
+  const bf16_t* dO;  // [B, T, Hq, dh] (may be null for the forward)
+  bf16_t* O;         // forward output (optional) [B, T, Hq, dh]
+  bf16_t* dQ;        // [B, T, Hq, dh]
+  float* dK;         // [B, T, Hkv, dh]
+  float* dV;
+  // per-row statistics of the chunk: element (b, h, t) at
+  // base + b*sb + h*sh + (t - s)*st   (t absolute, s = chunk start)
+  float* lse;
+  int64_t lse_sb, lse_sh, lse_st;
+  float* delta;
+  int64_t dl_sb, dl_sh, dl_st;
+  int64_t ldq;       // row pitch of Q, dO, O
+  int64_t lddq;      // row pitch of dQ
+  int64_t q_bs;      // batch stride of the query-side arrays
+  int qoff;
+  int T, Hq, Hkv, G;
+  int s, e;          // chunk [s, e)
+  float scale;
+  int beta;          // dK/dV: 1 = add into, 0 = overwrite
+};
+
+// Per query chunk [a.s, a.e): forward statistics (LSE always; Delta when
+// a.dO is set; O when a.O is set), Delta from a given O, and the backward
+// (dK/dV accumulate into fp32, dQ overwritten).
+sbp_status attn_fwd(const AttnArgs& a, int dh, int B, hipStream_t st);
+sbp_status attn_delta(const AttnArgs& a, const void* O, int dh, int B, hipStream_t st);
+sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st);
+
+}  // namespace sbp

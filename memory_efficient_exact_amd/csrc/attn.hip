@@ -31,6 +31,7 @@
 // at c ^ f(r), f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps both the
 // 16-byte row reads (8 rows) and the transposed reads (4 rows x 32 bytes)
 // free of bank conflicts.
+#include "attn.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -121,27 +122,6 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
   return *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + ks * 16 + g * 8);
 }
 
-struct AttnArgs {
-  const bf16_t* Q;   // [B, T, Hq, dh]
-  const bf16_t* K;   // [B, T, Hkv, dh]
-  const bf16_t* V;
-  const bf16_t* dO;  // [B, T, Hq, dh] (may be null for the forward)
-  bf16_t* O;         // forward output (optional) [B, T, Hq, dh]
-  bf16_t* dQ;        // [B, T, Hq, dh]
-  float* dK;         // [B, T, Hkv, dh]
-  float* dV;
-  // per-row statistics of the chunk: element (b, h, t) at
-  // base + b*sb + h*sh + (t - s)*st   (t absolute, s = chunk start)
-  float* lse;
-  int64_t lse_sb, lse_sh, lse_st;
-  float* delta;
-  int64_t dl_sb, dl_sh, dl_st;
-  int T, Hq, Hkv, G;
-  int s, e;          // chunk [s, e)
-  float scale;
-  int beta;          // dK/dV: 1 = add into, 0 = overwrite
-};
-
 // ---------------------------------------------------------------------------
 // Forward statistics.  Block: 4 waves, 128 queries (32 per wave), one q head.
 // ---------------------------------------------------------------------------
@@ -156,15 +136,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   const int q0 = a.s + blockIdx.x * 128;            // first query of the block
   const int qw = q0 + wave * 32;                    // first query of the wave
   const int qcol = qw + (lane & 31);                // this lane's query
-  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
-  const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
+  const bf16_t* Qb = a.Q + (int64_t)b * a.q_bs + (int64_t)h * DH;  // row t at (t - qoff)
   const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  const int qrel = qcol - a.qoff, qend = a.e - a.qoff;
 
   // Q^T as the B operand of S^T = K Q^T: column = query, k = dh
   uint4 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = glb_frag<DH>(Qb, ldq, qcol, a.e, ks, lane >> 5);
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = glb_frag<DH>(Qb, ldq, qrel, qend, ks, lane >> 5);
 
   f32x16_t ot[NB];
 #pragma unroll
@@ -237,11 +218,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   if (qcol >= a.e) return;
   const float inv = 1.f / l;
   const float lse = (m + log2f(l)) * kLn2;
-  const int64_t row = (int64_t)b * a.T + qcol;
+  const int64_t row = (int64_t)b * a.q_bs + (int64_t)qrel * ldq + (int64_t)h * DH;
   // Delta = sum_dh dO * O, O from the fp32 accumulator; O written if asked
   float dsum = 0.f;
-  const bf16_t* dorow = a.dO ? a.dO + row * ldq + (int64_t)h * DH : nullptr;
-  bf16_t* orow = a.O ? a.O + row * ldq + (int64_t)h * DH : nullptr;
+  const bf16_t* dorow = a.dO ? a.dO + row : nullptr;
+  bf16_t* orow = a.O ? a.O + row : nullptr;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -281,7 +262,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
   const int b = blockIdx.y;
   const int h = (int)(idx % a.Hq);
   const int t = a.s + (int)(idx / a.Hq);
-  const int64_t off = (((int64_t)b * a.T + t) * a.Hq + h) * DH;
+  const int64_t off = (int64_t)b * a.q_bs + (int64_t)(t - a.qoff) * a.ldq + (int64_t)h * DH;
   float s = 0.f;
   for (int d = lane; d < DH; d += 64) s += bf2f(a.dO[off + d]) * bf2f(O[off + d]);
   s = wave_sum(s);
@@ -303,7 +284,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   const int kbase = blockIdx.x * 128;
   const int kw = kbase + wave * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
-  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
+  const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
   const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   // K, V of this wave's keys as B operands (column = key, k = dh)
@@ -324,14 +305,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   const int qstart = max(a.s, kbase & ~63);
   for (int hh = 0; hh < a.G; ++hh) {
     const int h = kv * a.G + hh;
-    const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
-    const bf16_t* Ob = a.dO + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+    const bf16_t* Qb = a.Q + (int64_t)b * a.q_bs + (int64_t)h * DH;   // row t at (t - qoff)
+    const bf16_t* Ob = a.dO + (int64_t)b * a.q_bs + (int64_t)h * DH;
     const float* lrow = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh;
     const float* drow = a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh;
     for (int q0 = qstart; q0 < a.e; q0 += 64) {
       __syncthreads();
-      load_tile64<DH>(qt, Qb + (int64_t)q0 * ldq, ldq, a.e - q0, tid);
-      load_tile64<DH>(ot, Ob + (int64_t)q0 * ldq, ldq, a.e - q0, tid);
+      load_tile64<DH>(qt, Qb + (int64_t)(q0 - a.qoff) * ldq, ldq, a.e - q0, tid);
+      load_tile64<DH>(ot, Ob + (int64_t)(q0 - a.qoff) * ldq, ldq, a.e - q0, tid);
       if (tid < 64) {
         const int q = q0 + tid;
         const bool ok = q < a.e;
@@ -412,16 +393,17 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   const int q0 = a.s + blockIdx.x * 128;
   const int qw = q0 + wave * 32;
   const int qcol = qw + (lane & 31);
-  const int64_t ldq = (int64_t)a.Hq * DH, ldk = (int64_t)a.Hkv * DH;
-  const bf16_t* Qb = a.Q + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
-  const bf16_t* Ob = a.dO + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
+  const bf16_t* Qb = a.Q + (int64_t)b * a.q_bs + (int64_t)h * DH;   // row t at (t - qoff)
+  const bf16_t* Ob = a.dO + (int64_t)b * a.q_bs + (int64_t)h * DH;
   const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  const int qrel = qcol - a.qoff, qend = a.e - a.qoff;
   uint4 qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = glb_frag<DH>(Qb, ldq, qcol, a.e, ks, lane >> 5);
-    of[ks] = glb_frag<DH>(Ob, ldq, qcol, a.e, ks, lane >> 5);
+    qf[ks] = glb_frag<DH>(Qb, ldq, qrel, qend, ks, lane >> 5);
+    of[ks] = glb_frag<DH>(Ob, ldq, qrel, qend, ks, lane >> 5);
   }
   const bool qok = qcol < a.e;
   const float c2 = a.scale * kLog2e;
@@ -477,14 +459,14 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
     __syncthreads();
   }
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries
-  bf16_t* dQb = a.dQ + ((int64_t)b * a.T) * ldq + (int64_t)h * DH;
+  bf16_t* dQb = a.dQ + (int64_t)b * a.q_bs / ldq * a.lddq + (int64_t)h * DH;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int q = qw + crow(e, lane);
       if (q >= a.e) continue;
-      dQb[(int64_t)q * ldq + nb * 32 + (lane & 31)] = f2bf(a.scale * dq[nb][e]);
+      dQb[(int64_t)(q - a.qoff) * a.lddq + nb * 32 + (lane & 31)] = f2bf(a.scale * dq[nb][e]);
     }
 }
 
@@ -619,6 +601,7 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
     AttnArgs a;
     a.Q = (const bf16_t*)Q; a.K = (const bf16_t*)K; a.V = (const bf16_t*)V;
     a.dO = (const bf16_t*)dO; a.O = nullptr; a.dQ = (bf16_t*)dQ; a.dK = dK; a.dV = dV;
+    a.ldq = (int64_t)Hq * dh; a.lddq = a.ldq; a.q_bs = T * a.ldq; a.qoff = 0;
     a.T = (int)T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.s = (int)s0; a.e = (int)e0;
     a.scale = scale;

@@ -64,4 +64,18 @@ sbp_status splitk_reduce(int dtype, const float* part, int64_t split_stride, int
 sbp_status fill_zero_f32(float* p, int64_t n, const int* when, hipStream_t st);
 sbp_status fill_zero_bytes(void* p, int64_t nbytes, hipStream_t st);
 
+// ------------------------------------------------------- decoder layer ----
+sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, int64_t d,
+                       float eps, void* out, int64_t ldo, float* rinv, hipStream_t st);
+sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* dn, int64_t ldn,
+                       const float* rinv, const void* resid, int64_t ldr, int64_t rows, int64_t d,
+                       void* out, int64_t ldo, hipStream_t st);
+sbp_status gain_grad(const float* dn, int64_t ldn, const void* x, int64_t ldx, const float* rinv,
+                     int64_t rows, int64_t d, float* dg, int beta, hipStream_t st);
+sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStream_t st);
+sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, void* dudg,
+                      hipStream_t st);
+sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t cols, void* dst,
+                        int64_t ldd, hipStream_t st);
+
 }  // namespace sbp

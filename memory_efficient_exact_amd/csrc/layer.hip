@@ -1,4 +1,28 @@
 // sbp_layer_bwd: streamed backward of one pre-norm decoder layer.
+//
+// StreamBP skill page, "Implementation" (the streaming layer backward: per
+// chunk, run the layer forward on the chunk, back-propagate the chunk's
+// upstream gradient, add the weight gradients, keep the chunk's input
+// gradient) and "Architecture Overview" (layer-wise application, causal
+// structure).  Layer (no bias, no rotary embedding):
+//   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T
+//   o = causal GQA attention; a = x + o Wo^T
+//   n2 = RMSNorm(a; g2); [u | g] = n2 [W1; W3]^T; m = silu(u) g; y = a + m W2^T
+//
+// Pass F: h1 and k, v for every token, chunk by chunk (the causal prefix
+// every later query chunk reads).  Pass B, chunks c = D-1 .. 0:
+//   recompute h1, q, attention forward (o, LSE) over keys [0, e), a, n2,
+//   u, g, m;  dW2 += dy^T m;  dm = dy W2;  du, dg;  dW1 += du^T n2,
+//   dW3 += dg^T n2;  dn2 = [du | dg] [W1; W3];  da = dy + RMSNorm2'(dn2),
+//   dg2 +=;  dWo += da^T o;  do = da Wo;  attention backward over the prefix
+//   (dK, dV of keys [0, e) accumulate in fp32; after chunk c, rows [s, e) are
+//   final because later chunks already added theirs and earlier chunks never
+//   reach them);  dWq, dWk, dWv += [dq | dK_c | dV_c]^T h1;
+//   dh1 = [dq | dK_c | dV_c] [Wq; Wk; Wv];  dx = da + RMSNorm1'(dh1), dg1 +=.
+// Every product is an NT GEMM (gemm.hip): the weight transposes are formed
+// once per call, the chunk-time transposes (operands contracted over the
+// chunk's tokens) per chunk, zero-padded to the GEMM's K granule.
+#include "attn.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -6,6 +30,75 @@ namespace sbp {
 namespace {
 
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+struct LayerShape {
+  int64_t T, d, F, qd, kd, qkvd;
+  int Hq, Hkv, dh;
+  int32_t D;
+  int64_t Tcm, Tcp;
+  float eps;
+};
+
+LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
+  LayerShape s;
+  s.T = L->T; s.d = L->d; s.F = L->F;
+  s.Hq = L->Hq; s.Hkv = L->Hkv; s.dh = L->dh;
+  s.qd = (int64_t)L->Hq * L->dh;
+  s.kd = (int64_t)L->Hkv * L->dh;
+  s.qkvd = s.qd + 2 * s.kd;
+  s.D = D;
+  s.Tcm = max_chunk_len(L->T, D);
+  s.Tcp = round_up(s.Tcm, 128);
+  s.eps = L->eps;
+  return s;
+}
+
+struct LayerWs {
+  bf16_t *Kall, *Vall;
+  float *dKacc, *dVacc;
+  bf16_t *W2T, *W13T, *WoT, *WqkvT;
+  bf16_t *h1, *q, *o, *a, *n2, *ug, *mdm, *dudg, *da, *dov, *dqkv;
+  float *dn, *rinv1, *rinv2, *lse, *delta;
+  bf16_t *TA, *TB;
+};
+
+size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
+  WsPlan P;
+  P.base = base;
+  LayerWs x;
+  const size_t b2 = sizeof(bf16_t), f4 = sizeof(float);
+  x.Kall = (bf16_t*)P.take(b2 * s.T * s.kd);
+  x.Vall = (bf16_t*)P.take(b2 * s.T * s.kd);
+  x.dKacc = (float*)P.take(f4 * s.T * s.kd);
+  x.dVacc = (float*)P.take(f4 * s.T * s.kd);
+  x.W2T = (bf16_t*)P.take(b2 * s.F * s.d);
+  x.W13T = (bf16_t*)P.take(b2 * s.d * 2 * s.F);
+  x.WoT = (bf16_t*)P.take(b2 * s.qd * s.d);
+  x.WqkvT = (bf16_t*)P.take(b2 * s.d * s.qkvd);
+  const int64_t R = s.Tcm;
+  x.h1 = (bf16_t*)P.take(b2 * R * s.d);
+  x.q = (bf16_t*)P.take(b2 * R * s.qd);
+  x.o = (bf16_t*)P.take(b2 * R * s.qd);
+  x.a = (bf16_t*)P.take(b2 * R * s.d);
+  x.n2 = (bf16_t*)P.take(b2 * R * s.d);
+  x.ug = (bf16_t*)P.take(b2 * R * 2 * s.F);
+  x.mdm = (bf16_t*)P.take(b2 * R * s.F);
+  x.dudg = (bf16_t*)P.take(b2 * R * 2 * s.F);
+  x.da = (bf16_t*)P.take(b2 * R * s.d);
+  x.dov = (bf16_t*)P.take(b2 * R * s.qd);
+  x.dqkv = (bf16_t*)P.take(b2 * R * s.qkvd);
+  x.dn = (float*)P.take(f4 * R * s.d);
+  x.rinv1 = (float*)P.take(f4 * R);
+  x.rinv2 = (float*)P.take(f4 * R);
+  x.lse = (float*)P.take(f4 * R * s.Hq);
+  x.delta = (float*)P.take(f4 * R * s.Hq);
+  const int64_t maxA = std::max(std::max(s.d, 2 * s.F), s.qkvd);
+  const int64_t maxB = std::max(std::max(s.F, s.d), s.qd);
+  x.TA = (bf16_t*)P.take(b2 * maxA * s.Tcp);
+  x.TB = (bf16_t*)P.take(b2 * maxB * s.Tcp);
+  if (w) *w = x;
+  return round_up((int64_t)P.off, 256);
+}
 
 sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   if (!L) return set_error(SBP_ERR_INVALID_ARG, "desc is NULL");
@@ -17,20 +110,9 @@ sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   if (!(L->eps >= 0.f)) return set_error(SBP_ERR_INVALID_ARG, "eps must be >= 0");
   if (L->dh != 64 && L->dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", L->dh);
   if (L->d % 8 || L->F % 8) return set_error(SBP_ERR_UNSUPPORTED, "d and F must be multiples of 8");
+  if (L->dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "the decoder-layer backward is implemented for bf16 only");
+  if (L->T > (1ll << 30) || L->d > (1ll << 20) || L->F > (1ll << 24)) return set_error(SBP_ERR_UNSUPPORTED, "size out of supported range");
   return SBP_OK;
-}
-
-size_t layer_ws(const sbp_layer_desc* L, int32_t D) {
-  const int64_t T = L->T, d = L->d, F = L->F;
-  const int64_t qd = (int64_t)L->Hq * L->dh, kd = (int64_t)L->Hkv * L->dh;
-  const int64_t Tcm = max_chunk_len(T, D);
-  const size_t esz = L->dtype == SBP_BF16 ? 2 : 4;
-  WsPlan P;
-  P.take(esz * T * kd * 2);                 // K, V of every token
-  P.take(sizeof(float) * T * kd * 2);       // dK, dV accumulators
-  P.take(esz * Tcm * (3 * d + 2 * qd + 3 * F));  // chunk activations
-  P.take(sizeof(float) * Tcm * (2 * d + F));     // chunk fp32 temporaries
-  return round_up((int64_t)P.off, 256);
 }
 
 }  // namespace
@@ -44,7 +126,7 @@ extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, i
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = layer_check(desc, D);
   if (st != SBP_OK) return st;
-  *bytes = layer_ws(desc, D);
+  *bytes = layer_plan(layer_shape(desc, D), nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -64,10 +146,124 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
   }
   if (misaligned(x) || misaligned(dy) || misaligned(dx) || misaligned(ws))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  const size_t need = layer_ws(desc, D);
+  const LayerShape S = layer_shape(desc, D);
+  const size_t need = layer_plan(S, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-  (void)accumulate;
-  (void)stream;
-  return set_error(SBP_ERR_UNSUPPORTED, "decoder-layer backward is not built in this version");
+  LayerWs W;
+  layer_plan(S, (char*)ws, &W);
+  hipStream_t str = (hipStream_t)stream;
+  const int64_t d = S.d, F = S.F, qd = S.qd, kd = S.kd, qkvd = S.qkvd;
+  const bf16_t* X = (const bf16_t*)x;
+  const bf16_t* DY = (const bf16_t*)dy;
+  bf16_t* DX = (bf16_t*)dx;
+
+#define SBP_TRY(e_)                  \
+  do {                               \
+    sbp_status _s = (e_);            \
+    if (_s != SBP_OK) return _s;     \
+  } while (0)
+
+  // C[M, N] (op)= A[M, K] B[N, K]^T
+  auto gemm = [&](const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                  int64_t M, int64_t N, int64_t K, int epi, int beta, const void* R, int64_t ldr,
+                  const char* name) -> sbp_status {
+    GemmParams p;
+    p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc; p.R = R; p.ldr = ldr;
+    p.M = (int)M; p.N = (int)N; p.K = (int)K; p.beta = beta;
+    p.m_fastest = M <= N ? 1 : 0;
+    return gemm_nt(SBP_BF16, epi, p, GEMM_TILE_RING, str, name);
+  };
+  auto tr = [&](const void* src, int64_t ld_src, int64_t rows, int64_t cols, void* dst,
+                int64_t ld_dst, int64_t rows_pad) -> sbp_status {
+    return transpose_pad(SBP_BF16, src, ld_src, rows, cols, dst, ld_dst, rows_pad, nullptr, str);
+  };
+
+  // weight transposes for the products that contract over a weight's rows
+  SBP_TRY(tr(w->W2, F, d, F, W.W2T, d, d));                       // W2 [d, F] -> [F, d]
+  SBP_TRY(tr(w->W1, d, F, d, W.W13T, 2 * F, F));                   // W1 [F, d] -> cols 0..F
+  SBP_TRY(tr(w->W3, d, F, d, W.W13T + F, 2 * F, F));               // W3 -> cols F..2F
+  SBP_TRY(tr(w->Wo, qd, d, qd, W.WoT, d, d));                      // Wo [d, qd] -> [qd, d]
+  SBP_TRY(tr(w->Wq, d, qd, d, W.WqkvT, qkvd, qd));                 // Wq [qd, d] -> cols 0..qd
+  SBP_TRY(tr(w->Wk, d, kd, d, W.WqkvT + qd, qkvd, kd));
+  SBP_TRY(tr(w->Wv, d, kd, d, W.WqkvT + qd + kd, qkvd, kd));
+
+  // pass F: keys and values of every token
+  for (int32_t c = 0; c < D; ++c) {
+    int64_t s0, e0;
+    chunk_bounds(S.T, D, c, &s0, &e0);
+    const int64_t Tc = e0 - s0;
+    SBP_TRY(rmsnorm_fwd(X + s0 * d, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
+    SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    SBP_TRY(gemm(W.h1, d, w->Wv, d, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+  }
+
+  const float scale = 1.0f / sqrtf((float)S.dh);
+  for (int32_t c = D - 1; c >= 0; --c) {
+    int64_t s0, e0;
+    chunk_bounds(S.T, D, c, &s0, &e0);
+    const int64_t Tc = e0 - s0;
+    const int64_t Tp = round_up(Tc, 128);
+    const int wb = (c == D - 1) ? (accumulate ? 1 : 0) : 1;  // weight-gradient beta
+    const bf16_t* xc = X + s0 * d;
+    const bf16_t* dyc = DY + s0 * d;
+
+    // ---- recompute the chunk's forward ----
+    SBP_TRY(rmsnorm_fwd(xc, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
+    SBP_TRY(gemm(W.h1, d, w->Wq, d, W.q, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    AttnArgs at;
+    at.Q = W.q; at.K = W.Kall; at.V = W.Vall; at.dO = nullptr; at.O = W.o;
+    at.dQ = W.dqkv; at.dK = W.dKacc; at.dV = W.dVacc;
+    at.lse = W.lse; at.lse_sb = 0; at.lse_sh = S.Tcm; at.lse_st = 1;
+    at.delta = W.delta; at.dl_sb = 0; at.dl_sh = S.Tcm; at.dl_st = 1;
+    at.ldq = qd; at.lddq = qkvd; at.q_bs = 0; at.qoff = (int)s0;
+    at.T = (int)S.T; at.Hq = S.Hq; at.Hkv = S.Hkv; at.G = S.Hq / S.Hkv;
+    at.s = (int)s0; at.e = (int)e0; at.scale = scale;
+    at.beta = (c == D - 1) ? 0 : 1;  // dK/dV accumulators start at the last chunk
+    SBP_TRY(attn_fwd(at, S.dh, 1, str));
+    SBP_TRY(gemm(W.o, qd, w->Wo, qd, W.a, d, Tc, d, qd, EPI_OUT_RESID, 0, xc, d, "gemm_layer_fwd"));
+    SBP_TRY(rmsnorm_fwd(W.a, d, w->g2, Tc, d, S.eps, W.n2, d, W.rinv2, str));
+    SBP_TRY(gemm(W.n2, d, w->W1, d, W.ug, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    SBP_TRY(gemm(W.n2, d, w->W3, d, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    SBP_TRY(swiglu_fwd(W.ug, Tc, F, W.mdm, str));
+
+    // ---- MLP backward ----
+    SBP_TRY(tr(dyc, d, Tc, d, W.TA, Tp, Tp));            // dy^T [d, Tp]
+    SBP_TRY(tr(W.mdm, F, Tc, F, W.TB, Tp, Tp));          // m^T  [F, Tp]
+    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->W2, F, d, F, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(dyc, d, W.W2T, d, W.mdm, F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));  // dm
+    SBP_TRY(swiglu_bwd(W.mdm, W.ug, Tc, F, W.dudg, str));
+    SBP_TRY(tr(W.dudg, 2 * F, Tc, 2 * F, W.TA, Tp, Tp)); // [du | dg]^T [2F, Tp]
+    SBP_TRY(tr(W.n2, d, Tc, d, W.TB, Tp, Tp));           // n2^T [d, Tp]
+    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->W1, d, F, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.TA + F * Tp, Tp, W.TB, Tp, g->W3, d, F, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.dudg, 2 * F, W.W13T, 2 * F, W.dn, d, Tc, d, 2 * F, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
+    SBP_TRY(rmsnorm_bwd(W.a, d, w->g2, W.dn, d, W.rinv2, dyc, d, Tc, d, W.da, d, str));
+    SBP_TRY(gain_grad(W.dn, d, W.a, d, W.rinv2, Tc, d, g->g2, wb, str));
+
+    // ---- output projection ----
+    SBP_TRY(tr(W.da, d, Tc, d, W.TA, Tp, Tp));           // da^T [d, Tp]
+    SBP_TRY(tr(W.o, qd, Tc, qd, W.TB, Tp, Tp));          // o^T  [qd, Tp]
+    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->Wo, qd, d, qd, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.da, d, W.WoT, d, W.dov, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));
+
+    // ---- attention over the causal key prefix ----
+    at.dO = W.dov;
+    SBP_TRY(attn_delta(at, W.o, S.dh, 1, str));
+    SBP_TRY(attn_bwd_chunk(at, S.dh, 1, str));
+    SBP_TRY(rows_to_bf16(W.dKacc + s0 * kd, kd, Tc, kd, W.dqkv + qd, qkvd, str));
+    SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
+
+    // ---- q, k, v projections and the first norm ----
+    SBP_TRY(tr(W.dqkv, qkvd, Tc, qkvd, W.TA, Tp, Tp));   // [dq | dK | dV]^T
+    SBP_TRY(tr(W.h1, d, Tc, d, W.TB, Tp, Tp));           // h1^T
+    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->Wq, d, qd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.TA + qd * Tp, Tp, W.TB, Tp, g->Wk, d, kd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.TA + (qd + kd) * Tp, Tp, W.TB, Tp, g->Wv, d, kd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm(W.dqkv, qkvd, W.WqkvT, qkvd, W.dn, d, Tc, d, qkvd, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
+    SBP_TRY(rmsnorm_bwd(xc, d, w->g1, W.dn, d, W.rinv1, W.da, d, Tc, d, DX + s0 * d, d, str));
+    SBP_TRY(gain_grad(W.dn, d, xc, d, W.rinv1, Tc, d, g->g1, wb, str));
+  }
+#undef SBP_TRY
+  return SBP_OK;
 }
