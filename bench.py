@@ -31,6 +31,28 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record of
+    this workload (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), or
+    None when there is no record or the kernel sources changed since."""
+    import glob
+    import hashlib
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("workload") != workload or kernel not in rec.get("kernels", {}):
+            continue
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != rec["source_sha"]:
+            return None
+        k = rec["kernels"][kernel]
+        return int(k["read_bytes"] + k["write_bytes"])
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -41,7 +63,24 @@ def parse():
     p.add_argument("--T", type=int, default=None, help="override the sequence length")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(dev):
+    """A plain device-to-device copy of known size: 1 GiB read + 1 GiB
+    written per launch, the reference the FETCH_SIZE / WRITE_SIZE counters of
+    the path's kernels are scaled by."""
+    import torch
+    n = 1 << 28  # fp32 elements = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "launches": 3}), flush=True)
 
 
 def lmhead_setup(cfg, dev):
@@ -91,6 +130,44 @@ def attn_setup(cfg, dev):
     # recompute 2, backward 5)
     unit = 2.0 * Hq * dh * T * (T + 1) / 2 * B
     return step, 7.0 * unit, inp
+
+
+def layer_setup(cfg, dev):
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    L = synthetic.workload_inputs(cfg["index"], T=cfg["T"])
+    x, dy = L.x.to(dev), L.dy.to(dev)
+    w = {k: v.to(dev) for k, v in L.w.items()}
+    T, d, Hq, Hkv, dh, F, D = (cfg[k] for k in ("T", "d", "Hq", "Hkv", "dh", "F", "D"))
+    grads = {k: torch.empty(v.shape, dtype=torch.float32, device=dev) for k, v in w.items()}
+    ws = torch.empty(sbp.layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, x.dtype, L.eps),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return sbp.layer_bwd(x, dy, w, Hq, Hkv, dh, L.eps, D=D, grads=grads, workspace=ws)
+
+    # algorithmic work: 6 P T for the linear maps (forward recompute 2, backward
+    # 4; P = number of projection weights) plus 7 causal attention units
+    P = (Hq * dh) * d + 2 * (Hkv * dh) * d + d * (Hq * dh) + 3 * F * d
+    unit = 2.0 * Hq * dh * T * (T + 1) / 2
+    return step, 6.0 * P * T + 7.0 * unit, L
+
+
+def cpu_baseline_layer(L, cfg, sample):
+    """The oracle, untouched, on the first `sample` tokens of the same input."""
+    import oracle
+    import synthetic
+    w = {k: synthetic.to_f64(v) for k, v in L.w.items()}
+    x = synthetic.to_f64(L.x[:sample])
+    dy = synthetic.to_f64(L.dy[:sample])
+    t0 = time.perf_counter()
+    oracle.layer_bwd(x, dy, w, L.Hq, L.Hkv, L.dh, L.eps)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {sample} of {cfg['T']} tokens with the full weights (fp64 NumPy, "
+                      f"unchunked); {dt:.1f} s; attention cost per token grows with T, so this "
+                      f"overstates the oracle's rate at full T"}
 
 
 def cpu_baseline_attn(inp, cfg, sample_heads=1):
@@ -155,6 +232,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
 
     idx = args.workload
     cfg = dict(synthetic.WORKLOADS[idx])
@@ -169,8 +249,7 @@ def main():
     elif cfg["kind"] == "attn":
         step, flops, inp = attn_setup(cfg, dev)
     else:
-        print("the decoder-layer workload is not wired into bench.py yet", file=sys.stderr)
-        sys.exit(2)
+        step, flops, inp = layer_setup(cfg, dev)
     dtype = cfg["dtype"]
 
     for _ in range(args.warmup):
@@ -205,13 +284,15 @@ def main():
     if k["flops"] > 0:
         ach = k["flops"] / (k["ms"] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dtype],
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4),
+                "traffic": measured_traffic(cfg["name"], name),
                 "kernel": name, "avg_launch_ms": round(k["ms"] / k["launches"], 4),
                 "flops_per_launch": k["flops"] / k["launches"]}
     else:
         ach = k["bytes"] / (k["ms"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": name,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg["name"], name),
+                "kernel": name,
                 "avg_launch_ms": round(k["ms"] / k["launches"], 4),
                 "bytes_per_launch": k["bytes"] / k["launches"]}
     kernels = {n: {"launches": v["launches"] // args.steps,
@@ -247,6 +328,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
         elif cfg["kind"] == "attn":
             out["cpu_baseline"] = cpu_baseline_attn(inp, cfg)
+        else:
+            out["cpu_baseline"] = cpu_baseline_layer(inp, cfg, args.cpu_sample or 256)
     print(json.dumps(out), flush=True)
 
 
