@@ -404,17 +404,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_256_kernel(GemmParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// 4-stage ring variant: the same 256 x 256 tile and 32x32x16 MFMA, but K is
-// staged 32 wide (32 KB per stage) in four distinct LDS arrays, so three
-// stages (96 KB) are in flight while one is consumed.  Rows are 4 x 16-byte
-// chunks; chunk c of row r sits at c ^ ((r >> 1) & 3).  Each wave fetches
-// 128 rows of one operand with 8 DMA instructions per stage (16 rows each).
+// Pipelined variant (the default for bf16): the same 256 x 256 tile and
+// 32x32x16 MFMA with two 64-wide K stages (64 KB each) in two distinct LDS
+// arrays.  Every DMA instruction fetches 8 rows x 128 bytes -- whole cache
+// lines; fetching half lines (16 rows x 64 bytes) was measured on the box to
+// move ~40% less data per second.  Rows are 8 x 16-byte chunks, chunk c of
+// row r at c ^ (r & 7).  Per stage t (4 k16 steps):
+//   read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
+//   MFMAs step 2 | wait for stage t+1, bare barrier | fetch stage t+2 into
+//   stage t's buffer | read step 0 of stage t+1 | MFMAs step 3
+// so fragment reads always run under 16 MFMAs, and the barrier only waits
+// for stage t+1 (issued one stage earlier), never for t+2.
 // ---------------------------------------------------------------------------
 struct RingFrag {
   uint4 a[4], b[4];
 };
 
-// Fragments of k16 step ks (0 or 1) of a 32-wide stage in LDS tile L.
+// Fragments of k16 step ks (0..3) of a 64-wide stage in LDS tile L.
 __device__ __forceinline__ void ring_load(const uint4* __restrict__ L, int ks, int wm, int wn, int lane,
                                           RingFrag& f) {
   constexpr int BM = 256, WT = 128;
@@ -422,12 +428,12 @@ __device__ __forceinline__ void ring_load(const uint4* __restrict__ L, int ks, i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wm * WT + i * 32 + (lane & 31);
-    f.a[i] = L[r * 4 + (ch ^ ((r >> 1) & 3))];
+    f.a[i] = L[r * 8 + (ch ^ (r & 7))];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = BM + wn * WT + i * 32 + (lane & 31);
-    f.b[i] = L[r * 4 + (ch ^ ((r >> 1) & 3))];
+    f.b[i] = L[r * 8 + (ch ^ (r & 7))];
   }
 }
 
@@ -443,11 +449,9 @@ __device__ __forceinline__ void ring_mma(const RingFrag& f, f32x16_t (&acc)[4][4
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, BK = 32, WT = 128;
-  __shared__ uint4 L0[(BM + BN) * 4];
-  __shared__ uint4 L1[(BM + BN) * 4];
-  __shared__ uint4 L2[(BM + BN) * 4];
-  __shared__ uint4 L3[(BM + BN) * 4];
+  constexpr int BM = 256, BN = 256, BK = 64, WT = 128;
+  __shared__ uint4 L0[(BM + BN) * 8];
+  __shared__ uint4 L1[(BM + BN) * 8];
   if (p.active && *p.active == 0) return;
   int tm, tn, split;
   tile_coords(p, tm, tn, split);
@@ -457,24 +461,26 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // DMA role: waves 0-1 fetch the A panel, 2-3 the B panel, 128 rows each
   const int opnd = wave >> 1;
   const int rbase = (wave & 1) * 128;
-  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const int chunk = (lane & 7) ^ (lane >> 3);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
   const int64_t ld = opnd ? p.ldb : p.lda;
   const int lim = opnd ? p.N : p.M;
-  const int r0 = (opnd ? n0 : m0) + rbase + (lane >> 2);
+  const int r0 = (opnd ? n0 : m0) + rbase + (lane >> 3);
   const int lds_row0 = opnd * BM + rbase;
 
+  auto issue_one = [&](uint4* L, int k0, int j) {
+    int gr = r0 + j * 8;
+    gr = gr < lim ? gr : lim - 1;
+    const bf16_t* g = X + (int64_t)gr * ld + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
+                                     (SBP_AS3 void*)&L[(lds_row0 + j * 8) * 8], 16, 0, 0);
+  };
   auto issue = [&](uint4* L, int k0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int gr = r0 + j * 16;
-      gr = gr < lim ? gr : lim - 1;
-      const bf16_t* g = X + (int64_t)gr * ld + k0 + chunk * 8;
-      __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
-                                       (SBP_AS3 void*)&L[(lds_row0 + j * 16) * 4], 16, 0, 0);
-    }
+    for (int j = 0; j < 16; ++j) issue_one(L, k0, j);
   };
 
   f32x16_t acc[4][4];
@@ -483,65 +489,73 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  // every K range is a multiple of 4 * BK (checked by the launcher)
+  // nk is 0 or even.  The refill past the end re-fetches the last stage into
+  // a buffer nobody reads, so every step has the same shape.  Waits use the
+  // builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+  // 11:8) so the compiler's own wait insertion knows what has landed.
   const int nk = ke > kb ? (ke - kb) / BK : 0;
-  // nk is 0 or a multiple of 4; stage t lives in buffer t % 4.  Software
-  // pipeline, per stage t:
-  //   read k16 step 1 of stage t            (MFMAs of step 0 cover it)
-  //   MFMAs of step 0 of stage t
-  //   wait for stage t+1's DMA, bare barrier (everyone's stage t+1 landed;
-  //     everyone finished reading stage t-1, whose buffer takes stage t+3)
-  //   issue stage t+3
-  //   read k16 step 0 of stage t+1          (MFMAs of step 1 cover it)
-  //   MFMAs of step 1 of stage t
-  // The refill is unconditional -- past the end it re-fetches the last
-  // stage into a buffer nobody reads -- so every step has the same wait
-  // count.  sched_barrier(0) keeps the fragment reads ahead of the MFMAs.
-  // Waits use the builtin (gfx9 encoding, vmcnt in bits 3:0 and 15:14) so
-  // the compiler's own wait insertion knows which stages have landed.
   RingFrag f0, f1;
   if (nk > 0) {
     issue(L0, kb);
-    issue(L1, kb + BK);
-    issue(L2, kb + 2 * BK);
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 landed
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stage 0 landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    issue(L1, kb + BK);
     ring_load(L0, 0, wm, wn, lane, f0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
-  auto step = [&](const uint4* Lc, const uint4* Lnext, uint4* Lrefill, int t) {
+  auto step = [&](const uint4* Lc, const uint4* Ln, uint4* Lrefill, int t) {
+    // lgkmcnt(0) after each MFMA group: the reads issued before it have long
+    // landed, and saying so keeps at most 8 reads outstanding (the counter
+    // cannot express waits with more than 15 in flight).
     ring_load(Lc, 1, wm, wn, lane, f1);
     __builtin_amdgcn_sched_barrier(0);
     ring_mma(f0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): stage t+1 landed
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(Lrefill, kb + min(t + 3, nk - 1) * BK);
-    ring_load(Lnext, 0, wm, wn, lane, f0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    ring_load(Lc, 2, wm, wn, lane, f0);
     __builtin_amdgcn_sched_barrier(0);
     ring_mma(f1, acc);
     __builtin_amdgcn_sched_barrier(0);
-    // lgkmcnt(0): the next stage's step-0 fragments, read 16 MFMAs ago, have
-    // landed; stating it keeps the compiler from waiting on the step-1 reads
-    // it issues next before starting the step-0 MFMAs.
     __builtin_amdgcn_s_waitcnt(0xC07F);
+    ring_load(Lc, 3, wm, wn, lane, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_mma(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stage t+1 landed, step 3 read
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // the next stage's first fragments, then the refill DMA spread over the
+    // 16 MFMAs of step 3 (4 DMA instructions per 4 MFMAs) so that the wave
+    // never stalls issuing a burst of DMAs while the matrix unit idles
+    ring_load(Ln, 0, wm, wn, lane, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kr = kb + min(t + 2, nk - 1) * BK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 4 * q; j < 4 * q + 4; ++j) issue_one(Lrefill, kr, j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+        acc[q][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, f1.a[q]), __builtin_bit_cast(bf16x8_t, f1.b[fn]), acc[q][fn],
+            0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   };
-  for (int it = 0; it < nk; it += 4) {
-    step(L0, L1, L3, it);
-    step(L1, L2, L0, it + 1);
-    step(L2, L3, L1, it + 2);
-    step(L3, L0, L2, it + 3);
+  for (int it = 0; it < nk; it += 2) {
+    step(L0, L1, L0, it);
+    step(L1, L0, L1, it + 1);
   }
 
-  // Epilogue through LDS (L0|L1 and L2|L3 are adjacent 64 KB halves of the
-  // static LDS block only by accident of layout, so each wave uses one 32 KB
-  // array on its own): 32 rows x 128 columns per pass, 4 passes.
+  // Epilogue through LDS: each wave parks 32 rows x 128 columns of fp32 (16 KB)
+  // in its own quarter of L0|L1, then writes row-contiguous 4-wide vectors.
   __syncthreads();
-  float* W = reinterpret_cast<float*>(wave == 0 ? L0 : wave == 1 ? L1 : wave == 2 ? L2 : L3);
+  float* W = reinterpret_cast<float*>((wave < 2 ? L0 : L1)) + (wave & 1) * (32 * 128);
   float beta = (float)p.beta;
   if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
   const bool vec_ok = (p.ldc % 4 == 0) && (EPI != EPI_OUT_RESID || p.ldr % 4 == 0);
