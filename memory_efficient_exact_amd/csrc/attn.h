@@ -38,7 +38,14 @@ struct AttnArgs {
 // a.dO is set; O when a.O is set), Delta from a given O, and the backward
 // (dK/dV accumulate into fp32, dQ overwritten).
 sbp_status attn_fwd(const AttnArgs& a, int dh, int B, hipStream_t st);
-sbp_status attn_delta(const AttnArgs& a, const void* O, int dh, int B, hipStream_t st);
+// Delta from a given O; when lse_src is set also copies LSE (element (b, t, h)
+// at lse_src + b * lsb + t * lst + h) into the statistics layout of a.lse.
+sbp_status attn_delta(const AttnArgs& a, const void* O, const float* lse_src, int64_t lsb,
+                      int64_t lst, int dh, int B, hipStream_t st);
+
+// Row pitch (floats) of per-chunk LSE / Delta rows: the chunk length padded
+// so that a 64-row fetch starting at any 64-aligned row stays in bounds.
+inline int64_t attn_stats_pitch(int64_t Tcm) { return round_up(Tcm, 64) + 64; }
 sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st);
 
 }  // namespace sbp

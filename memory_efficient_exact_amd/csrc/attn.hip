@@ -53,20 +53,32 @@ __device__ __forceinline__ int tile_off(int r, int col) {
   return r * (DH * 2) + ((c ^ swz(r)) << 4) + ((col & 7) << 1);
 }
 
-// Copy rows [0, 64) of a [rows][DH] bf16 tile from global (row pitch ld
-// elements, rows >= nvalid zero-filled) into a swizzled LDS tile.
+#define SBP_AS1 __attribute__((address_space(1)))
+
+// DMA rows [0, 64) of a [rows][DH] bf16 tile (global row pitch ld elements)
+// into a swizzled LDS tile: each 1 KB global_load_lds covers 1024 / (2 DH)
+// rows, lane i filling 16-byte slot i, so the swizzle is applied to the
+// global address (lane i fetches logical chunk (i % CPR) ^ f(row)).  Rows at
+// or past nvalid fetch row nvalid - 1 instead (finite data the callers mask).
 template <int DH>
-__device__ __forceinline__ void load_tile64(char* lds, const bf16_t* __restrict__ src, int64_t ld,
-                                            int nvalid, int tid) {
-  constexpr int CPR = DH / 8;  // 16-byte chunks per row
-  constexpr int TOTAL = 64 * CPR;
+__device__ __forceinline__ void dma_tile64(char* lds, const bf16_t* __restrict__ src, int64_t ld,
+                                           int nvalid, int wave, int lane) {
+  constexpr int ROWB = DH * 2, RPI = 1024 / ROWB, NI = 64 / RPI, CPR = DH / 8;
+  const int rr = lane / CPR, pc = lane % CPR;
 #pragma unroll
-  for (int i = tid; i < TOTAL; i += 256) {
-    const int r = i / CPR, c = i % CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nvalid) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + c * 8);
-    *reinterpret_cast<uint4*>(lds + r * (DH * 2) + ((c ^ swz(r)) << 4)) = v;
+  for (int i = wave; i < NI; i += 4) {
+    const int r = i * RPI + rr;
+    const int c = pc ^ swz(r);
+    const int gr = r < nvalid ? r : nvalid - 1;
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + (int64_t)gr * ld + c * 8),
+                                     (SBP_LDS void*)(lds + i * 1024), 16, 0, 0);
   }
+}
+
+// DMA 64 consecutive fp32 (16-byte aligned, in bounds) with lanes 0..15.
+__device__ __forceinline__ void dma_f32x64(float* lds, const float* __restrict__ src, int lane) {
+  if (lane < 16)
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + lane * 4), (SBP_LDS void*)lds, 16, 0, 0);
 }
 
 // 16-byte row read: row rbase + l%32, k16 step ks (columns 16ks + 8(l/32) ..).
@@ -124,13 +136,70 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
 
 // ---------------------------------------------------------------------------
 // Forward statistics.  Block: 4 waves, 128 queries (32 per wave), one q head.
+// Key/value tiles of 64 rows are double-buffered in two distinct LDS arrays
+// (so the compiler can tell the DMA into one from the reads of the other):
+// tile t+1 is fetched while tile t is used.
 // ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void fwd_tile(const char* kt, const char* vt, int k0, int qcol, int lane,
+                                         float c2, const uint4 (&qf)[DH / 16], float& m, float& l,
+                                         f32x16_t (&ot)[DH / 32]) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  f32x16_t st[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    st[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) st[kb] = mma(lds_row_frag<DH>(kt, kb * 32, ks, lane), qf[ks], st[kb]);
+  }
+  // scale, mask (key > query), online softmax along the keys (rows)
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + kb * 32 + crow(e, lane);
+      const float v = (key <= qcol) ? st[kb][e] * c2 : -INFINITY;
+      st[kb][e] = v;
+      mt = fmaxf(mt, v);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m, mt);
+  const float alpha = exp2f(m - mn);
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2f(st[kb][e] - mn);
+      st[kb][e] = p;
+      ls += p;
+    }
+  ls += __shfl_xor(ls, 32, 64);
+  l = l * alpha + ls;
+  m = mn;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) ot[i] *= alpha;
+  // O^T[dh, q] += V^T[dh, key] P^T[key, q]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 pb = pack_frag(st[kb], i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        ot[nb] = mma(lds_tr_frag<DH>(vt, kb * 32 + 16 * i, nb * 32, lane), pb, ot[nb]);
+    }
+}
+
 template <int DH>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NB = DH / 32;   // 32-wide dh blocks
   constexpr int KS = DH / 16;   // k16 steps over dh
-  __shared__ __attribute__((aligned(16))) char kt[2][64 * DH * 2];
-  __shared__ __attribute__((aligned(16))) char vt[2][64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char K0[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char V0[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
   const int q0 = a.s + blockIdx.x * 128;            // first query of the block
@@ -155,66 +224,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
 
   const int kend = min(q0 + 128, a.e);              // keys [0, kend)
   const int ntiles = (kend + 63) / 64;
-  load_tile64<DH>(kt[0], Kb, ldk, kend, tid);
-  load_tile64<DH>(vt[0], Vb, ldk, kend, tid);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
+  auto issue = [&](char* kd, char* vd, int t) {
     const int k0 = t * 64;
-    if (t + 1 < ntiles) {
-      load_tile64<DH>(kt[cur ^ 1], Kb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
-      load_tile64<DH>(vt[cur ^ 1], Vb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
-    }
-    if (k0 <= qw + 31) {  // some key of the tile is visible to this wave
-      f32x16_t st[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          st[kb] = mma(lds_row_frag<DH>(kt[cur], kb * 32, ks, lane), qf[ks], st[kb]);
-      }
-      // scale, mask (key > query), online softmax along the keys (rows)
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + crow(e, lane);
-          const float v = (key <= qcol) ? st[kb][e] * c2 : -INFINITY;
-          st[kb][e] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2f(m - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(st[kb][e] - mn);
-          st[kb][e] = p;
-          ls += p;
-        }
-      ls += __shfl_xor(ls, 32, 64);
-      l = l * alpha + ls;
-      m = mn;
-#pragma unroll
-      for (int i = 0; i < NB; ++i) ot[i] *= alpha;
-      // O^T[dh, q] += V^T[dh, key] P^T[key, q]
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 pb = pack_frag(st[kb], i);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            ot[nb] = mma(lds_tr_frag<DH>(vt[cur], kb * 32 + 16 * i, nb * 32, lane), pb, ot[nb]);
-        }
-    }
+    dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+    dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+  };
+  issue(K0, V0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    __syncthreads();  // tile t landed; everyone is done with the other buffer
+    issue(K1, V1, min(t + 1, ntiles - 1));
+    if (t * 64 <= qw + 31) fwd_tile<DH>(K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
     __syncthreads();
+    issue(K0, V0, min(t + 2, ntiles - 1));
+    if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
+      fwd_tile<DH>(K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   if (qcol >= a.e) return;
   const float inv = 1.f / l;
   const float lse = (m + log2f(l)) * kLn2;
@@ -251,10 +276,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O) from a given O (dtype), one wave per (row, head).
+// Delta = rowsum(dO * O) from a given O (dtype), one wave per (row, head);
+// optionally also copies a caller's LSE ([B, T, Hq], rows of the chunk) into
+// the statistics layout.
 // ---------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_t* __restrict__ O) {
+__global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_t* __restrict__ O,
+                                                         const float* __restrict__ lse_src,
+                                                         int64_t lsb, int64_t lst) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over Tc * Hq rows of batch row b
   const int Tc = a.e - a.s;
@@ -266,19 +295,78 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
   float s = 0.f;
   for (int d = lane; d < DH; d += 64) s += bf2f(a.dO[off + d]) * bf2f(O[off + d]);
   s = wave_sum(s);
-  if (lane == 0) a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(t - a.s) * a.dl_st] = s;
+  if (lane == 0) {
+    a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(t - a.s) * a.dl_st] = s;
+    if (lse_src)
+      a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(t - a.s) * a.lse_st] =
+          lse_src[(int64_t)b * lsb + (int64_t)t * lst + h];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Block: 4 waves, 128 keys (32 per wave), one kv head; loops over
-// the G q heads of the group and the 64-query tiles of the chunk.
+// dK, dV.  Block: 4 waves, 128 keys (32 per wave), one kv head; iterates over
+// (q head of the group, 64-query tile of the chunk at or after the keys),
+// the Q / dO tiles and their LSE / Delta rows double-buffered by DMA.
+// Query tiles start at s + 64 j so the statistics rows are 16-byte aligned;
+// statistics rows are padded past the chunk so every 64-row fetch is in
+// bounds, and queries at or past e are masked.
 // ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void dkdv_tile(const char* qt, const char* ot, const float* ls,
+                                          const float* dl, int q0, int kcol, int e, int lane, float c2,
+                                          const uint4 (&kf)[DH / 16], const uint4 (&vf)[DH / 16],
+                                          f32x16_t (&dk)[DH / 32], f32x16_t (&dv)[DH / 32]) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two row blocks
+  f32x16_t sp[2], dp[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    sp[qb] = f32x16_t{};
+    dp[qb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sp[qb] = mma(lds_row_frag<DH>(qt, qb * 32, ks, lane), kf[ks], sp[qb]);
+      dp[qb] = mma(lds_row_frag<DH>(ot, qb * 32, ks, lane), vf[ks], dp[qb]);
+    }
+  }
+  // P = exp(s S - LSE) (0 where key > query or the query is past the chunk),
+  // dS = P (dP - Delta)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int e_ = 0; e_ < 16; ++e_) {
+      const int r = qb * 32 + crow(e_, lane);
+      const int q = q0 + r;
+      // statistics rows past the chunk are padding (any value): select, do
+      // not multiply, so that they cannot leak in
+      const bool on = kcol <= q && q < e;
+      const float p = on ? exp2f(sp[qb][e_] * c2 - ls[r] * kLog2e) : 0.f;
+      sp[qb][e_] = p;
+      dp[qb][e_] = on ? p * (dp[qb][e_] - dl[r]) : 0.f;
+    }
+  // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 pa = pack_frag(sp[qb], i);
+      const uint4 da = pack_frag(dp[qb], i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        dv[nb] = mma(pa, lds_tr_frag<DH>(ot, qb * 32 + 16 * i, nb * 32, lane), dv[nb]);
+        dk[nb] = mma(da, lds_tr_frag<DH>(qt, qb * 32 + 16 * i, nb * 32, lane), dk[nb]);
+      }
+    }
+}
+
 template <int DH>
 __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   constexpr int NB = DH / 32, KS = DH / 16;
-  __shared__ __attribute__((aligned(16))) char qt[64 * DH * 2];
-  __shared__ __attribute__((aligned(16))) char ot[64 * DH * 2];  // dO tile
-  __shared__ float s_lse[64], s_dl[64];
+  __shared__ __attribute__((aligned(16))) char Q0[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char O0[64 * DH * 2];  // dO tile
+  __shared__ __attribute__((aligned(16))) char Q1[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char O1[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) float L0[64], E0[64], L1[64], E1[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kv = blockIdx.y, b = blockIdx.z;
   const int kbase = blockIdx.x * 128;
@@ -301,63 +389,39 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
     dv[i] = f32x16_t{};
   }
   const float c2 = a.scale * kLog2e;
-  // query tiles that see any key of the block: queries >= kbase
-  const int qstart = max(a.s, kbase & ~63);
-  for (int hh = 0; hh < a.G; ++hh) {
+  // query tiles s + 64 j that reach the block's keys (queries >= kbase)
+  const int j0 = kbase > a.s ? (kbase - a.s) / 64 : 0;
+  const int nqt = (a.e - a.s + 63) / 64 - j0;
+  const int n = nqt > 0 ? nqt * a.G : 0;
+  auto issue = [&](char* qd, char* od, float* ld_, float* dd, int it) {
+    const int hh = it / nqt;
+    const int q0 = a.s + (j0 + it % nqt) * 64;
     const int h = kv * a.G + hh;
-    const bf16_t* Qb = a.Q + (int64_t)b * a.q_bs + (int64_t)h * DH;   // row t at (t - qoff)
-    const bf16_t* Ob = a.dO + (int64_t)b * a.q_bs + (int64_t)h * DH;
-    const float* lrow = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh;
-    const float* drow = a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh;
-    for (int q0 = qstart; q0 < a.e; q0 += 64) {
-      __syncthreads();
-      load_tile64<DH>(qt, Qb + (int64_t)(q0 - a.qoff) * ldq, ldq, a.e - q0, tid);
-      load_tile64<DH>(ot, Ob + (int64_t)(q0 - a.qoff) * ldq, ldq, a.e - q0, tid);
-      if (tid < 64) {
-        const int q = q0 + tid;
-        const bool ok = q < a.e;
-        s_lse[tid] = ok ? lrow[(int64_t)(q - a.s) * a.lse_st] * kLog2e : INFINITY;
-        s_dl[tid] = ok ? drow[(int64_t)(q - a.s) * a.dl_st] : 0.f;
-      }
-      __syncthreads();
-      if (q0 + 63 < kw) continue;  // every query of the tile precedes this wave's keys
-      // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two row blocks
-      f32x16_t sp[2], dp[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sp[qb] = f32x16_t{};
-        dp[qb] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sp[qb] = mma(lds_row_frag<DH>(qt, qb * 32, ks, lane), kf[ks], sp[qb]);
-          dp[qb] = mma(lds_row_frag<DH>(ot, qb * 32, ks, lane), vf[ks], dp[qb]);
-        }
-      }
-      // P = exp(s S - LSE) (0 where key > query), dS = P (dP - Delta)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = qb * 32 + crow(e, lane);
-          const float p = (kcol <= q0 + r) ? exp2f(sp[qb][e] * c2 - s_lse[r]) : 0.f;
-          sp[qb][e] = p;
-          dp[qb][e] = p * (dp[qb][e] - s_dl[r]);
-        }
-      // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 pa = pack_frag(sp[qb], i);
-          const uint4 da = pack_frag(dp[qb], i);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            dv[nb] = mma(pa, lds_tr_frag<DH>(ot, qb * 32 + 16 * i, nb * 32, lane), dv[nb]);
-            dk[nb] = mma(da, lds_tr_frag<DH>(qt, qb * 32 + 16 * i, nb * 32, lane), dk[nb]);
-          }
-        }
+    const int64_t qo = (int64_t)b * a.q_bs + (int64_t)(q0 - a.qoff) * ldq + (int64_t)h * DH;
+    dma_tile64<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
+    dma_tile64<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
+    if (wave == 0)
+      dma_f32x64(ld_, a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (q0 - a.s), lane);
+    else if (wave == 1)
+      dma_f32x64(dd, a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (q0 - a.s), lane);
+  };
+  auto qstart = [&](int it) { return a.s + (j0 + it % nqt) * 64; };
+  if (n > 0) issue(Q0, O0, L0, E0, 0);
+  for (int it = 0; it < n; it += 2) {
+    __syncthreads();  // tile it landed; everyone is done with the other buffers
+    issue(Q1, O1, L1, E1, min(it + 1, n - 1));
+    {
+      const int q0 = qstart(it);
+      if (q0 + 63 >= kw) dkdv_tile<DH>(Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
+    }
+    __syncthreads();
+    issue(Q0, O0, L0, E0, min(it + 2, n - 1));
+    if (it + 1 < n) {
+      const int q0 = qstart(it + 1);
+      if (q0 + 63 >= kw) dkdv_tile<DH>(Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 keys x 32 dh]: lane = dh column, rows = keys
   float* dKb = a.dK + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   float* dVb = a.dV + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
@@ -381,13 +445,51 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ.  Block: 4 waves, 128 queries (32 per wave), one q head; key tiles of
-// 64 up to the diagonal.
+// 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void dq_tile(const char* kt, const char* vt, int k0, int qcol, int lane,
+                                        float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
+                                        const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32]) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  f32x16_t st[2], dpt[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    st[kb] = f32x16_t{};
+    dpt[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      st[kb] = mma(lds_row_frag<DH>(kt, kb * 32, ks, lane), qf[ks], st[kb]);
+      dpt[kb] = mma(lds_row_frag<DH>(vt, kb * 32, ks, lane), of[ks], dpt[kb]);
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + kb * 32 + crow(e, lane);
+      const float p = (key <= qcol) ? exp2f(st[kb][e] * c2 - lse2) : 0.f;
+      dpt[kb][e] = p * (dpt[kb][e] - dl);
+    }
+  // dQ[q, dh] += dS[q, key] K[key, dh]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 da = pack_frag(dpt[kb], i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dq[nb] = mma(da, lds_tr_frag<DH>(kt, kb * 32 + 16 * i, nb * 32, lane), dq[nb]);
+    }
+}
+
 template <int DH>
 __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   constexpr int NB = DH / 32, KS = DH / 16;
-  __shared__ __attribute__((aligned(16))) char kt[2][64 * DH * 2];
-  __shared__ __attribute__((aligned(16))) char vt[2][64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char K0[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char V0[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
+  __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
   const int q0 = a.s + blockIdx.x * 128;
@@ -415,49 +517,22 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
 
   const int kend = min(q0 + 128, a.e);
   const int ntiles = (kend + 63) / 64;
-  load_tile64<DH>(kt[0], Kb, ldk, kend, tid);
-  load_tile64<DH>(vt[0], Vb, ldk, kend, tid);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
+  auto issue = [&](char* kd, char* vd, int t) {
     const int k0 = t * 64;
-    if (t + 1 < ntiles) {
-      load_tile64<DH>(kt[cur ^ 1], Kb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
-      load_tile64<DH>(vt[cur ^ 1], Vb + (int64_t)(k0 + 64) * ldk, ldk, kend - k0 - 64, tid);
-    }
-    if (k0 <= qw + 31) {
-      f32x16_t st[2], dpt[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = f32x16_t{};
-        dpt[kb] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          st[kb] = mma(lds_row_frag<DH>(kt[cur], kb * 32, ks, lane), qf[ks], st[kb]);
-          dpt[kb] = mma(lds_row_frag<DH>(vt[cur], kb * 32, ks, lane), of[ks], dpt[kb]);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + crow(e, lane);
-          const float p = (key <= qcol) ? exp2f(st[kb][e] * c2 - lse2) : 0.f;
-          dpt[kb][e] = p * (dpt[kb][e] - dl);
-        }
-      // dQ[q, dh] += dS[q, key] K[key, dh]
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 da = pack_frag(dpt[kb], i);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            dq[nb] = mma(da, lds_tr_frag<DH>(kt[cur], kb * 32 + 16 * i, nb * 32, lane), dq[nb]);
-        }
-    }
+    dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+    dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+  };
+  issue(K0, V0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
     __syncthreads();
+    issue(K1, V1, min(t + 1, ntiles - 1));
+    if (t * 64 <= qw + 31) dq_tile<DH>(K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    __syncthreads();
+    issue(K0, V0, min(t + 2, ntiles - 1));
+    if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
+      dq_tile<DH>(K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries
   bf16_t* dQb = a.dQ + (int64_t)b * a.q_bs / ldq * a.lddq + (int64_t)h * DH;
 #pragma unroll
@@ -490,15 +565,16 @@ sbp_status attn_fwd(const AttnArgs& a, int dh, int B, hipStream_t st) {
   return SBP_OK;
 }
 
-sbp_status attn_delta(const AttnArgs& a, const void* O, int dh, int B, hipStream_t st) {
+sbp_status attn_delta(const AttnArgs& a, const void* O, const float* lse_src, int64_t lsb,
+                      int64_t lst, int dh, int B, hipStream_t st) {
   const int Tc = a.e - a.s;
   const int64_t rows = (int64_t)Tc * a.Hq;
   dim3 grid((unsigned)cdiv(rows, 4), (unsigned)B);
   ProfScope prof("attn_delta", st, 0.0, 4.0 * rows * B * dh);
   if (dh == 128)
-    hipLaunchKernelGGL(attn_delta_kernel<128>, grid, dim3(256), 0, st, a, (const bf16_t*)O);
+    hipLaunchKernelGGL(attn_delta_kernel<128>, grid, dim3(256), 0, st, a, (const bf16_t*)O, lse_src, lsb, lst);
   else
-    hipLaunchKernelGGL(attn_delta_kernel<64>, grid, dim3(256), 0, st, a, (const bf16_t*)O);
+    hipLaunchKernelGGL(attn_delta_kernel<64>, grid, dim3(256), 0, st, a, (const bf16_t*)O, lse_src, lsb, lst);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }
@@ -545,11 +621,11 @@ sbp_status attn_check(int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
 size_t attn_ws(int64_t B, int64_t T, int32_t Hq, int32_t dh, int32_t D, int32_t dtype) {
   (void)dh;
   (void)dtype;
-  // per query chunk: LSE_c and Delta_c, fp32 [B, Hq, T_c]
-  const int64_t Tcm = max_chunk_len(T, D);
+  // per query chunk: LSE_c and Delta_c, fp32 [B, Hq, Lp]
+  const int64_t Lp = attn_stats_pitch(max_chunk_len(T, D));
   WsPlan P;
-  P.take(sizeof(float) * B * Tcm * Hq);
-  P.take(sizeof(float) * B * Tcm * Hq);
+  P.take(sizeof(float) * B * Lp * Hq);
+  P.take(sizeof(float) * B * Lp * Hq);
   return round_up((int64_t)P.off, 256);
 }
 
@@ -590,11 +666,11 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   hipStream_t str = (hipStream_t)stream;
-  const int64_t Tcm = max_chunk_len(T, D);
+  const int64_t Lp = attn_stats_pitch(max_chunk_len(T, D));
   WsPlan P;
   P.base = (char*)ws;
-  float* w_lse = (float*)P.take(sizeof(float) * B * Tcm * Hq);
-  float* w_dl = (float*)P.take(sizeof(float) * B * Tcm * Hq);
+  float* w_lse = (float*)P.take(sizeof(float) * B * Lp * Hq);
+  float* w_dl = (float*)P.take(sizeof(float) * B * Lp * Hq);
   for (int32_t c = D - 1; c >= 0; --c) {
     int64_t s0, e0;
     chunk_bounds(T, D, c, &s0, &e0);
@@ -607,14 +683,12 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
     a.scale = scale;
     // the last chunk (processed first) reaches every key: it overwrites
     a.beta = (accumulate || c != D - 1) ? 1 : 0;
-    a.delta = w_dl; a.dl_sb = (int64_t)Hq * Tcm; a.dl_sh = Tcm; a.dl_st = 1;
+    a.delta = w_dl; a.dl_sb = (int64_t)Hq * Lp; a.dl_sh = Lp; a.dl_st = 1;
+    a.lse = w_lse; a.lse_sb = (int64_t)Hq * Lp; a.lse_sh = Lp; a.lse_st = 1;
     if (lse) {
-      // caller's statistics [B, T, Hq], offset to the chunk start
-      a.lse = const_cast<float*>(lse) + s0 * Hq;
-      a.lse_sb = T * Hq; a.lse_sh = 1; a.lse_st = Hq;
-      st = attn_delta(a, O, dh, (int)B, str);
+      // caller's O and LSE ([B, T, Hq]): Delta, and LSE copied into the chunk layout
+      st = attn_delta(a, O, lse, T * Hq, Hq, dh, (int)B, str);
     } else {
-      a.lse = w_lse; a.lse_sb = (int64_t)Hq * Tcm; a.lse_sh = Tcm; a.lse_st = 1;
       st = attn_fwd(a, dh, (int)B, str);
     }
     if (st != SBP_OK) return st;

@@ -90,8 +90,8 @@ size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
   x.dn = (float*)P.take(f4 * R * s.d);
   x.rinv1 = (float*)P.take(f4 * R);
   x.rinv2 = (float*)P.take(f4 * R);
-  x.lse = (float*)P.take(f4 * R * s.Hq);
-  x.delta = (float*)P.take(f4 * R * s.Hq);
+  x.lse = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
+  x.delta = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   const int64_t maxA = std::max(std::max(s.d, 2 * s.F), s.qkvd);
   const int64_t maxB = std::max(std::max(s.F, s.d), s.qd);
   x.TA = (bf16_t*)P.take(b2 * maxA * s.Tcp);
@@ -214,8 +214,9 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     AttnArgs at;
     at.Q = W.q; at.K = W.Kall; at.V = W.Vall; at.dO = nullptr; at.O = W.o;
     at.dQ = W.dqkv; at.dK = W.dKacc; at.dV = W.dVacc;
-    at.lse = W.lse; at.lse_sb = 0; at.lse_sh = S.Tcm; at.lse_st = 1;
-    at.delta = W.delta; at.dl_sb = 0; at.dl_sh = S.Tcm; at.dl_st = 1;
+    const int64_t Lp = attn_stats_pitch(S.Tcm);
+    at.lse = W.lse; at.lse_sb = 0; at.lse_sh = Lp; at.lse_st = 1;
+    at.delta = W.delta; at.dl_sb = 0; at.dl_sh = Lp; at.dl_st = 1;
     at.ldq = qd; at.lddq = qkvd; at.q_bs = 0; at.qoff = (int)s0;
     at.T = (int)S.T; at.Hq = S.Hq; at.Hkv = S.Hkv; at.G = S.Hq / S.Hkv;
     at.s = (int)s0; at.e = (int)e0; at.scale = scale;
@@ -249,7 +250,7 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
 
     // ---- attention over the causal key prefix ----
     at.dO = W.dov;
-    SBP_TRY(attn_delta(at, W.o, S.dh, 1, str));
+    SBP_TRY(attn_delta(at, W.o, nullptr, 0, 0, S.dh, 1, str));
     SBP_TRY(attn_bwd_chunk(at, S.dh, 1, str));
     SBP_TRY(rows_to_bf16(W.dKacc + s0 * kd, kd, Tc, kd, W.dqkv + qd, qkvd, str));
     SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
