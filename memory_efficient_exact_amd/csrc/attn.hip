@@ -81,39 +81,70 @@ __device__ __forceinline__ void dma_f32x64(float* lds, const float* __restrict__
     __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + lane * 4), (SBP_LDS void*)lds, 16, 0, 0);
 }
 
-// 16-byte row read: row rbase + l%32, k16 step ks (columns 16ks + 8(l/32) ..).
-template <int DH>
-__device__ __forceinline__ uint4 lds_row_frag(const char* lds, int rbase, int ks, int lane) {
-  const int r = rbase + (lane & 31);
-  const int c = ks * 2 + (lane >> 5);
-  return *reinterpret_cast<const uint4*>(lds + r * (DH * 2) + ((c ^ swz(r)) << 4));
+// Double-buffer hand-over.  The DMA writes of a tile are counted by each
+// wave's own vmcnt, so every wave first waits for its share of the tile about
+// to be read, and the barrier then makes all shares visible (it also ends
+// every wave's reads of the buffer about to be refilled).  The wave index is
+// made wave-uniform (readfirstlane) so that the DMA issue branches are scalar
+// and the compiler does not wait on the fresh refill before reading the other
+// buffer.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// Transposed read: 8 bf16 of column cbase + l%32 at rows
-// rbase + 4(l/32) + {0..3} and rbase + 8 + 4(l/32) + {0..3}.
+// Per-lane LDS byte offsets for the two fragment reads of a swizzled tile.
+// The swizzle is an XOR, so the compiler cannot fold the addresses of the
+// different k16 steps / column blocks into immediate offsets and hoists one
+// register per address; factored by hand, every read is one of 6 per-lane
+// offsets plus a compile-time immediate:
+//   row read, row rbase + l%32 (rbase % 32 == 0), k16 step ks:
+//     row[ks & 3] + 128 (ks >> 2) + rbase * 2DH
+//   transposed read of column block nb at rows rbase.. (rbase % 8 == 0):
+//     tr[nb & 1] + 128 (nb >> 1) + rbase * 2DH   (and + 8 rows)
+// (exhaustively checked against the plain swizzle formula).
 template <int DH>
-__device__ __forceinline__ uint4 lds_tr_frag(const char* lds, int rbase, int cbase, int lane) {
-  const int G = (lane >> 4) & 3, j = lane & 15;
-  const int r = rbase + 4 * (G >> 1) + (j >> 2);
-  const int col = cbase + (G & 1) * 16 + 4 * (j & 3);
-  const SBP_LDS char* base = (const SBP_LDS char*)lds;
-  i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(base + tile_off<DH>(r, col)));
-  i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(base + tile_off<DH>(r + 8, col)));
-  uint4 u;
-  u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-  u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-  u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-  u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-  return u;
-}
+struct LdsOff {
+  int row[4], tr[2];
+  __device__ __forceinline__ explicit LdsOff(int lane) {
+    constexpr int ROWB = DH * 2;
+    const int g = lane >> 5, r = lane & 31, sw = swz(r);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) row[kk] = r * ROWB + 32 * (kk ^ (sw >> 1)) + 16 * (g ^ (sw & 1));
+    const int G = (lane >> 4) & 3, j = lane & 15;
+    const int rr = 4 * (G >> 1) + (j >> 2), s = swz(rr), colc = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      tr[q] = rr * ROWB + 64 * (q ^ (s >> 2)) + 16 * (colc ^ (s & 3)) + 8 * (j & 1);
+  }
+  // 16-byte row read: row rbase + l%32, columns 16 ks + 8 (l/32) .. + 8
+  __device__ __forceinline__ uint4 row_frag(const char* t, int rbase, int ks) const {
+    return *reinterpret_cast<const uint4*>(t + row[ks & 3] + 128 * (ks >> 2) + rbase * (DH * 2));
+  }
+  // Transposed read: 8 bf16 of column 32 nb + l%32 at rows rbase + 4(l/32) +
+  // {0..3} and rbase + 8 + 4(l/32) + {0..3}.
+  __device__ __forceinline__ uint4 tr_frag(const char* t, int rbase, int nb) const {
+    const SBP_LDS char* p = (const SBP_LDS char*)t + tr[nb & 1] + 128 * (nb >> 1) + rbase * (DH * 2);
+    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)p);
+    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(p + 8 * DH * 2));
+    uint4 u;
+    u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    u.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    u.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return u;
+  }
+};
 
 // Elements 8i..8i+7 of a result block as a bf16 operand (k16 step i).
 __device__ __forceinline__ uint4 pack_frag(const f32x16_t& a, int i) {
   uint4 u;
-  u.x = (uint32_t)f2bf(a[8 * i + 0]) | ((uint32_t)f2bf(a[8 * i + 1]) << 16);
-  u.y = (uint32_t)f2bf(a[8 * i + 2]) | ((uint32_t)f2bf(a[8 * i + 3]) << 16);
-  u.z = (uint32_t)f2bf(a[8 * i + 4]) | ((uint32_t)f2bf(a[8 * i + 5]) << 16);
-  u.w = (uint32_t)f2bf(a[8 * i + 6]) | ((uint32_t)f2bf(a[8 * i + 7]) << 16);
+  u.x = pk_bf16(a[8 * i + 0], a[8 * i + 1]);
+  u.y = pk_bf16(a[8 * i + 2], a[8 * i + 3]);
+  u.z = pk_bf16(a[8 * i + 4], a[8 * i + 5]);
+  u.w = pk_bf16(a[8 * i + 6], a[8 * i + 7]);
   return u;
 }
 
@@ -141,7 +172,7 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
 // tile t+1 is fetched while tile t is used.
 // ---------------------------------------------------------------------------
 template <int DH>
-__device__ __forceinline__ void fwd_tile(const char* kt, const char* vt, int k0, int qcol, int lane,
+__device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
                                          float c2, const uint4 (&qf)[DH / 16], float& m, float& l,
                                          f32x16_t (&ot)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
@@ -150,7 +181,7 @@ __device__ __forceinline__ void fwd_tile(const char* kt, const char* vt, int k0,
   for (int kb = 0; kb < 2; ++kb) {
     st[kb] = f32x16_t{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) st[kb] = mma(lds_row_frag<DH>(kt, kb * 32, ks, lane), qf[ks], st[kb]);
+    for (int ks = 0; ks < KS; ++ks) st[kb] = mma(lo.row_frag(kt, kb * 32, ks), qf[ks], st[kb]);
   }
   // scale, mask (key > query), online softmax along the keys (rows)
   float mt = -INFINITY;
@@ -165,13 +196,13 @@ __device__ __forceinline__ void fwd_tile(const char* kt, const char* vt, int k0,
     }
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
   const float mn = fmaxf(m, mt);
-  const float alpha = exp2f(m - mn);
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);
   float ls = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = exp2f(st[kb][e] - mn);
+      const float p = __builtin_amdgcn_exp2f(st[kb][e] - mn);
       st[kb][e] = p;
       ls += p;
     }
@@ -188,7 +219,7 @@ __device__ __forceinline__ void fwd_tile(const char* kt, const char* vt, int k0,
       const uint4 pb = pack_frag(st[kb], i);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        ot[nb] = mma(lds_tr_frag<DH>(vt, kb * 32 + 16 * i, nb * 32, lane), pb, ot[nb]);
+        ot[nb] = mma(lo.tr_frag(vt, kb * 32 + 16 * i, nb), pb, ot[nb]);
     }
 }
 
@@ -200,8 +231,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char V0[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const LdsOff<DH> lo(lane);
   const int q0 = a.s + blockIdx.x * 128;            // first query of the block
   const int qw = q0 + wave * 32;                    // first query of the wave
   const int qcol = qw + (lane & 31);                // this lane's query
@@ -231,13 +263,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   };
   issue(K0, V0, 0);
   for (int t = 0; t < ntiles; t += 2) {
-    __syncthreads();  // tile t landed; everyone is done with the other buffer
+    dma_barrier();  // tile t landed; everyone is done with the other buffer
     issue(K1, V1, min(t + 1, ntiles - 1));
-    if (t * 64 <= qw + 31) fwd_tile<DH>(K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
-    __syncthreads();
+    if (t * 64 <= qw + 31) fwd_tile<DH>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
+    dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
     if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      fwd_tile<DH>(K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
+      fwd_tile<DH>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   if (qcol >= a.e) return;
@@ -263,8 +295,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
       }
       if (orow) {
         uint2 w;
-        w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-        w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        w.x = pk_bf16(o[0], o[1]);
+        w.y = pk_bf16(o[2], o[3]);
         *reinterpret_cast<uint2*>(orow + d0) = w;
       }
     }
@@ -312,7 +344,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
 // bounds, and queries at or past e are masked.
 // ---------------------------------------------------------------------------
 template <int DH>
-__device__ __forceinline__ void dkdv_tile(const char* qt, const char* ot, const float* ls,
+__device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, const char* ot, const float* ls,
                                           const float* dl, int q0, int kcol, int e, int lane, float c2,
                                           const uint4 (&kf)[DH / 16], const uint4 (&vf)[DH / 16],
                                           f32x16_t (&dk)[DH / 32], f32x16_t (&dv)[DH / 32]) {
@@ -325,8 +357,8 @@ __device__ __forceinline__ void dkdv_tile(const char* qt, const char* ot, const 
     dp[qb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sp[qb] = mma(lds_row_frag<DH>(qt, qb * 32, ks, lane), kf[ks], sp[qb]);
-      dp[qb] = mma(lds_row_frag<DH>(ot, qb * 32, ks, lane), vf[ks], dp[qb]);
+      sp[qb] = mma(lo.row_frag(qt, qb * 32, ks), kf[ks], sp[qb]);
+      dp[qb] = mma(lo.row_frag(ot, qb * 32, ks), vf[ks], dp[qb]);
     }
   }
   // P = exp(s S - LSE) (0 where key > query or the query is past the chunk),
@@ -334,15 +366,23 @@ __device__ __forceinline__ void dkdv_tile(const char* qt, const char* ot, const 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int e_ = 0; e_ < 16; ++e_) {
-      const int r = qb * 32 + crow(e_, lane);
-      const int q = q0 + r;
-      // statistics rows past the chunk are padding (any value): select, do
-      // not multiply, so that they cannot leak in
-      const bool on = kcol <= q && q < e;
-      const float p = on ? exp2f(sp[qb][e_] * c2 - ls[r] * kLog2e) : 0.f;
-      sp[qb][e_] = p;
-      dp[qb][e_] = on ? p * (dp[qb][e_] - dl[r]) : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      // result elements 4j..4j+3 are rows 8j + 4(l/32) + 0..3 of the block
+      const int r0 = qb * 32 + 8 * j + 4 * (lane >> 5);
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl + r0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e_ = 4 * j + i;
+        const int q = q0 + r0 + i;
+        // statistics rows past the chunk are padding (any value): select, do
+        // not multiply, so that they cannot leak in
+        const bool on = kcol <= q && q < e;
+        const float p = on ? __builtin_amdgcn_exp2f(sp[qb][e_] * c2 - lv[i] * kLog2e) : 0.f;
+        sp[qb][e_] = p;
+        dp[qb][e_] = on ? p * (dp[qb][e_] - dv_[i]) : 0.f;
+      }
     }
   // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
 #pragma unroll
@@ -353,8 +393,8 @@ __device__ __forceinline__ void dkdv_tile(const char* qt, const char* ot, const 
       const uint4 da = pack_frag(dp[qb], i);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        dv[nb] = mma(pa, lds_tr_frag<DH>(ot, qb * 32 + 16 * i, nb * 32, lane), dv[nb]);
-        dk[nb] = mma(da, lds_tr_frag<DH>(qt, qb * 32 + 16 * i, nb * 32, lane), dk[nb]);
+        dv[nb] = mma(pa, lo.tr_frag(ot, qb * 32 + 16 * i, nb), dv[nb]);
+        dk[nb] = mma(da, lo.tr_frag(qt, qb * 32 + 16 * i, nb), dk[nb]);
       }
     }
 }
@@ -367,8 +407,9 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char Q1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char O1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) float L0[64], E0[64], L1[64], E1[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kv = blockIdx.y, b = blockIdx.z;
+  const LdsOff<DH> lo(lane);
   const int kbase = blockIdx.x * 128;
   const int kw = kbase + wave * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
@@ -408,39 +449,45 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   auto qstart = [&](int it) { return a.s + (j0 + it % nqt) * 64; };
   if (n > 0) issue(Q0, O0, L0, E0, 0);
   for (int it = 0; it < n; it += 2) {
-    __syncthreads();  // tile it landed; everyone is done with the other buffers
+    dma_barrier();  // tile it landed; everyone is done with the other buffers
     issue(Q1, O1, L1, E1, min(it + 1, n - 1));
     {
       const int q0 = qstart(it);
-      if (q0 + 63 >= kw) dkdv_tile<DH>(Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
+      if (q0 + 63 >= kw) dkdv_tile<DH>(lo, Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
     }
-    __syncthreads();
+    dma_barrier();
     issue(Q0, O0, L0, E0, min(it + 2, n - 1));
     if (it + 1 < n) {
       const int q0 = qstart(it + 1);
-      if (q0 + 63 >= kw) dkdv_tile<DH>(Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
+      if (q0 + 63 >= kw) dkdv_tile<DH>(lo, Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 keys x 32 dh]: lane = dh column, rows = keys
   float* dKb = a.dK + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   float* dVb = a.dV + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
+  // beta: all 32 old values of a column block are loaded before any store,
+  // so the loads are in flight together
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
+    float ok[16], ov[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kw + crow(e, lane);
+      const int64_t off = (int64_t)key * ldk + nb * 32 + (lane & 31);
+      const bool in = a.beta && key < a.T;
+      ok[e] = in ? dKb[off] : 0.f;
+      ov[e] = in ? dVb[off] : 0.f;
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kw + crow(e, lane);
       if (key >= a.T) continue;
       const int64_t off = (int64_t)key * ldk + nb * 32 + (lane & 31);
-      const float gk = a.scale * dk[nb][e], gv = dv[nb][e];
-      if (a.beta) {
-        dKb[off] += gk;
-        dVb[off] += gv;
-      } else {
-        dKb[off] = gk;
-        dVb[off] = gv;
-      }
+      dKb[off] = ok[e] + a.scale * dk[nb][e];
+      dVb[off] = ov[e] + dv[nb][e];
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +495,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
 // 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
 template <int DH>
-__device__ __forceinline__ void dq_tile(const char* kt, const char* vt, int k0, int qcol, int lane,
+__device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
                                         float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
                                         const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
@@ -459,8 +506,8 @@ __device__ __forceinline__ void dq_tile(const char* kt, const char* vt, int k0, 
     dpt[kb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      st[kb] = mma(lds_row_frag<DH>(kt, kb * 32, ks, lane), qf[ks], st[kb]);
-      dpt[kb] = mma(lds_row_frag<DH>(vt, kb * 32, ks, lane), of[ks], dpt[kb]);
+      st[kb] = mma(lo.row_frag(kt, kb * 32, ks), qf[ks], st[kb]);
+      dpt[kb] = mma(lo.row_frag(vt, kb * 32, ks), of[ks], dpt[kb]);
     }
   }
 #pragma unroll
@@ -468,7 +515,7 @@ __device__ __forceinline__ void dq_tile(const char* kt, const char* vt, int k0, 
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + kb * 32 + crow(e, lane);
-      const float p = (key <= qcol) ? exp2f(st[kb][e] * c2 - lse2) : 0.f;
+      const float p = (key <= qcol) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
       dpt[kb][e] = p * (dpt[kb][e] - dl);
     }
   // dQ[q, dh] += dS[q, key] K[key, dh]
@@ -479,7 +526,7 @@ __device__ __forceinline__ void dq_tile(const char* kt, const char* vt, int k0, 
       const uint4 da = pack_frag(dpt[kb], i);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        dq[nb] = mma(da, lds_tr_frag<DH>(kt, kb * 32 + 16 * i, nb * 32, lane), dq[nb]);
+        dq[nb] = mma(da, lo.tr_frag(kt, kb * 32 + 16 * i, nb), dq[nb]);
     }
 }
 
@@ -490,8 +537,9 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char V0[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const LdsOff<DH> lo(lane);
   const int q0 = a.s + blockIdx.x * 128;
   const int qw = q0 + wave * 32;
   const int qcol = qw + (lane & 31);
@@ -524,13 +572,13 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   };
   issue(K0, V0, 0);
   for (int t = 0; t < ntiles; t += 2) {
-    __syncthreads();
+    dma_barrier();
     issue(K1, V1, min(t + 1, ntiles - 1));
-    if (t * 64 <= qw + 31) dq_tile<DH>(K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
-    __syncthreads();
+    if (t * 64 <= qw + 31) dq_tile<DH>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
     if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      dq_tile<DH>(K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+      dq_tile<DH>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries

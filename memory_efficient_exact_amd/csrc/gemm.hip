@@ -375,8 +375,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_256_kernel(GemmParams p) 
             v[2] += bf2f((bf16_t)(r.y & 0xffff)); v[3] += bf2f((bf16_t)(r.y >> 16));
           }
           uint2 u;
-          u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-          u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          u.x = pk_bf16(v[0], v[1]);
+          u.y = pk_bf16(v[2], v[3]);
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
         }
       } else {
@@ -600,8 +600,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
             v[2] += bf2f((bf16_t)(r.y & 0xffff)); v[3] += bf2f((bf16_t)(r.y >> 16));
           }
           uint2 u;
-          u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-          u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          u.x = pk_bf16(v[0], v[1]);
+          u.y = pk_bf16(v[2], v[3]);
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
         }
       } else {
