@@ -19,7 +19,9 @@ struct AttnArgs {
   float* dK;         // [B, T, Hkv, dh]
   float* dV;
   // per-row statistics of the chunk: element (b, h, t) at
-  // base + b*sb + h*sh + (t - s)*st   (t absolute, s = chunk start)
+  // base + b*sb + h*sh + (t - s)*st   (t absolute, s = chunk start).
+  // lse holds the log-sum-exp of the scaled scores in base-2 units
+  // (natural-log LSE times log2 e), as the kernels evaluate exp2.
   float* lse;
   int64_t lse_sb, lse_sh, lse_st;
   float* delta;

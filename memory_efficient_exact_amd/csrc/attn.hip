@@ -28,9 +28,14 @@
 // element i%4 of the 8-byte chunks fetched by lanes i/4 + 4m (m = 0..3), so
 // 16 lanes that fetch 4 rows x 16 columns receive one column each, 4 rows
 // deep.  LDS tiles are rows of dh bf16 with 16-byte chunk c of row r stored
-// at c ^ f(r), f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps both the
-// 16-byte row reads (8 rows) and the transposed reads (4 rows x 32 bytes)
-// free of bank conflicts.
+// at c ^ f(r).  gfx950's LDS serves 256 bytes (64 four-byte banks) per
+// clock: 16 lanes of a 16-byte row read, 32 lanes of an 8-byte transposed
+// read.  f is chosen so that both are conflict-free: the row read's 16 rows
+// r..r+15 land on 16 distinct chunks of the 256-byte bank line, and the
+// transposed read's 4 rows x 64 bytes on 4 distinct 64-byte quarters.
+//   dh 128 (rows of 256 B):  f(r) = 4 (r & 3) + ((r >> 2) & 3)
+//   dh  64 (rows of 128 B):  f(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)
+// (f depends on r mod 16 only).
 #include "attn.h"
 #include "common.h"
 #include "kernels.h"
@@ -44,13 +49,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-// Byte offset of element (r, col) in a swizzled [rows][DH] bf16 LDS tile.
 template <int DH>
-__device__ __forceinline__ int tile_off(int r, int col) {
-  const int c = col >> 3;
-  return r * (DH * 2) + ((c ^ swz(r)) << 4) + ((col & 7) << 1);
+__device__ __forceinline__ int swz(int r) {
+  return DH == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 #define SBP_AS1 __attribute__((address_space(1)))
@@ -68,7 +69,7 @@ __device__ __forceinline__ void dma_tile64(char* lds, const bf16_t* __restrict__
 #pragma unroll
   for (int i = wave; i < NI; i += 4) {
     const int r = i * RPI + rr;
-    const int c = pc ^ swz(r);
+    const int c = pc ^ swz<DH>(r);
     const int gr = r < nvalid ? r : nvalid - 1;
     __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + (int64_t)gr * ld + c * 8),
                                      (SBP_LDS void*)(lds + i * 1024), 16, 0, 0);
@@ -95,40 +96,41 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Per-lane LDS byte offsets for the two fragment reads of a swizzled tile.
-// The swizzle is an XOR, so the compiler cannot fold the addresses of the
-// different k16 steps / column blocks into immediate offsets and hoists one
-// register per address; factored by hand, every read is one of 6 per-lane
-// offsets plus a compile-time immediate:
-//   row read, row rbase + l%32 (rbase % 32 == 0), k16 step ks:
-//     row[ks & 3] + 128 (ks >> 2) + rbase * 2DH
-//   transposed read of column block nb at rows rbase.. (rbase % 8 == 0):
-//     tr[nb & 1] + 128 (nb >> 1) + rbase * 2DH   (and + 8 rows)
-// (exhaustively checked against the plain swizzle formula).
+// Per-lane LDS byte offsets of the fragment reads of a swizzled tile, so
+// that every read is a per-lane register plus a compile-time immediate:
+//   row read, rows rbase + l%32 (rbase % 32 == 0), k16 step ks (16-byte
+//     chunk 2 ks + l/32):                       row[ks] + rbase * 2DH
+//   transposed read of column block nb, rows rbase + 4(l/32) + 0..3 and
+//     the same + 8 (rbase % 16 == 0):           tr[nb][0 / 1] + rbase * 2DH
+// (checked exhaustively against the DMA placement on the host).
 template <int DH>
 struct LdsOff {
-  int row[4], tr[2];
+  static constexpr int KS = DH / 16, NB = DH / 32, ROWB = DH * 2;
+  int row[KS], tr[NB][2];
   __device__ __forceinline__ explicit LdsOff(int lane) {
-    constexpr int ROWB = DH * 2;
-    const int g = lane >> 5, r = lane & 31, sw = swz(r);
+    const int g = lane >> 5, r = lane & 31, f = swz<DH>(r);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) row[kk] = r * ROWB + 32 * (kk ^ (sw >> 1)) + 16 * (g ^ (sw & 1));
+    for (int ks = 0; ks < KS; ++ks) row[ks] = r * ROWB + 16 * ((2 * ks + g) ^ f);
     const int G = (lane >> 4) & 3, j = lane & 15;
-    const int rr = 4 * (G >> 1) + (j >> 2), s = swz(rr), colc = 2 * (G & 1) + ((j & 3) >> 1);
+    const int rr = 4 * (G >> 1) + (j >> 2), colc = 2 * (G & 1) + ((j & 3) >> 1);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      tr[q] = rr * ROWB + 64 * (q ^ (s >> 2)) + 16 * (colc ^ (s & 3)) + 8 * (j & 1);
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rw = rr + 8 * h;
+        tr[nb][h] = rw * ROWB + 16 * ((4 * nb + colc) ^ swz<DH>(rw)) + 8 * (j & 1);
+      }
   }
   // 16-byte row read: row rbase + l%32, columns 16 ks + 8 (l/32) .. + 8
   __device__ __forceinline__ uint4 row_frag(const char* t, int rbase, int ks) const {
-    return *reinterpret_cast<const uint4*>(t + row[ks & 3] + 128 * (ks >> 2) + rbase * (DH * 2));
+    return *reinterpret_cast<const uint4*>(t + row[ks] + rbase * ROWB);
   }
   // Transposed read: 8 bf16 of column 32 nb + l%32 at rows rbase + 4(l/32) +
   // {0..3} and rbase + 8 + 4(l/32) + {0..3}.
   __device__ __forceinline__ uint4 tr_frag(const char* t, int rbase, int nb) const {
-    const SBP_LDS char* p = (const SBP_LDS char*)t + tr[nb & 1] + 128 * (nb >> 1) + rbase * (DH * 2);
-    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)p);
-    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(p + 8 * DH * 2));
+    const SBP_LDS char* p = (const SBP_LDS char*)t + rbase * ROWB;
+    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(p + tr[nb][0]));
+    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_LDS i16x4_t*)(p + tr[nb][1]));
     uint4 u;
     u.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
     u.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -171,7 +173,7 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
 // (so the compiler can tell the DMA into one from the reads of the other):
 // tile t+1 is fetched while tile t is used.
 // ---------------------------------------------------------------------------
-template <int DH>
+template <int DH, bool MASK>
 __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
                                          float c2, const uint4 (&qf)[DH / 16], float& m, float& l,
                                          f32x16_t (&ot)[DH / 32]) {
@@ -190,7 +192,7 @@ __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, c
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + kb * 32 + crow(e, lane);
-      const float v = (key <= qcol) ? st[kb][e] * c2 : -INFINITY;
+      const float v = (!MASK || key <= qcol) ? st[kb][e] * c2 : -INFINITY;
       st[kb][e] = v;
       mt = fmaxf(mt, v);
     }
@@ -224,7 +226,7 @@ __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, c
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NB = DH / 32;   // 32-wide dh blocks
   constexpr int KS = DH / 16;   // k16 steps over dh
   __shared__ __attribute__((aligned(16))) char K0[64 * DH * 2];
@@ -265,16 +267,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   for (int t = 0; t < ntiles; t += 2) {
     dma_barrier();  // tile t landed; everyone is done with the other buffer
     issue(K1, V1, min(t + 1, ntiles - 1));
-    if (t * 64 <= qw + 31) fwd_tile<DH>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
+    // only tiles that reach past the wave's first query need the causal mask
+    if (t * 64 + 63 <= qw) fwd_tile<DH, false>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
+    else if (t * 64 <= qw + 31) fwd_tile<DH, true>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
     dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
-    if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      fwd_tile<DH>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
+    if (t + 1 < ntiles && (t + 1) * 64 + 63 <= qw)
+      fwd_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
+    else if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
+      fwd_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   if (qcol >= a.e) return;
   const float inv = 1.f / l;
-  const float lse = (m + log2f(l)) * kLn2;
+  const float lse = m + log2f(l);  // base-2 units (scores were scaled by log2 e)
   const int64_t row = (int64_t)b * a.q_bs + (int64_t)qrel * ldq + (int64_t)h * DH;
   // Delta = sum_dh dO * O, O from the fp32 accumulator; O written if asked
   float dsum = 0.f;
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
     a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(t - a.s) * a.dl_st] = s;
     if (lse_src)
       a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(t - a.s) * a.lse_st] =
-          lse_src[(int64_t)b * lsb + (int64_t)t * lst + h];
+          lse_src[(int64_t)b * lsb + (int64_t)t * lst + h] * kLog2e;
   }
 }
 
@@ -343,60 +349,94 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
 // statistics rows are padded past the chunk so every 64-row fetch is in
 // bounds, and queries at or past e are masked.
 // ---------------------------------------------------------------------------
+// P and dS of one 32-query half qb of the tile, in place, for result
+// elements [16 part / KS, 16 (part + 1) / KS).  Branch-free (the exponent is
+// computed for every lane, then selected), so that it can sit between the
+// other half's MFMAs.
+template <int DH>
+__device__ __forceinline__ void dkdv_softmax_part(f32x16_t& sp, f32x16_t& dp, const float* ls,
+                                                  const float* dl, int qb, int part, int q0,
+                                                  int kcol, int e, int lane, float c2, bool mask) {
+  constexpr int PER = 16 / (DH / 16);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e_ = part * PER + k;
+    const int r = qb * 32 + crow(e_, lane);
+    const int q = q0 + r;
+    float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - ls[r]);
+    float g = p * (dp[e_] - dl[r]);
+    if (mask) {  // wave-uniform: a scalar branch
+      asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
+      // statistics rows past the chunk are padding (any value): select, do
+      // not multiply, so that they cannot leak in
+      const bool on = kcol <= q && q < e;
+      p = on ? p : 0.f;
+      g = on ? g : 0.f;
+    }
+    sp[e_] = p;
+    dp[e_] = g;
+  }
+}
+
+// One 64-query tile against the wave's 32 keys, software-pipelined: LDS
+// fragments are read two steps ahead of the MFMAs that use them, and the
+// softmax of one 32-query half is spread over the MFMA steps of the other.
+//   steps 0 .. 2KS-1:  S, dP of half 0, then half 1 (+ softmax of half 0)
+//   steps 0 .. 4NB-1:  dV, dK from half 0 (+ softmax of half 1), then half 1
 template <int DH>
 __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, const char* ot, const float* ls,
                                           const float* dl, int q0, int kcol, int e, int lane, float c2,
-                                          const uint4 (&kf)[DH / 16], const uint4 (&vf)[DH / 16],
+                                          bool mask, const uint4 (&kf)[DH / 16], const uint4 (&vf)[DH / 16],
                                           f32x16_t (&dk)[DH / 32], f32x16_t (&dv)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
-  // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two row blocks
   f32x16_t sp[2], dp[2];
+  sp[0] = sp[1] = dp[0] = dp[1] = f32x16_t{};
+  // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two 32-query halves
+  {
+    uint4 fq[3], fo[3];
+    auto ld = [&](int st) {
+      fq[st % 3] = lo.row_frag(qt, (st / KS) * 32, st % KS);
+      fo[st % 3] = lo.row_frag(ot, (st / KS) * 32, st % KS);
+    };
+    ld(0);
+    ld(1);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    sp[qb] = f32x16_t{};
-    dp[qb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sp[qb] = mma(lo.row_frag(qt, qb * 32, ks), kf[ks], sp[qb]);
-      dp[qb] = mma(lo.row_frag(ot, qb * 32, ks), vf[ks], dp[qb]);
+    for (int st = 0; st < 2 * KS; ++st) {
+      if (st + 2 < 2 * KS) ld(st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int qb = st / KS, ks = st % KS;
+      sp[qb] = mma(fq[st % 3], kf[ks], sp[qb]);
+      dp[qb] = mma(fo[st % 3], vf[ks], dp[qb]);
+      if (qb == 1) dkdv_softmax_part<DH>(sp[0], dp[0], ls, dl, 0, ks, q0, kcol, e, lane, c2, mask);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // P = exp(s S - LSE) (0 where key > query or the query is past the chunk),
-  // dS = P (dP - Delta)
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // result elements 4j..4j+3 are rows 8j + 4(l/32) + 0..3 of the block
-      const int r0 = qb * 32 + 8 * j + 4 * (lane >> 5);
-      const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
-      const float4 d4 = *reinterpret_cast<const float4*>(dl + r0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e_ = 4 * j + i;
-        const int q = q0 + r0 + i;
-        // statistics rows past the chunk are padding (any value): select, do
-        // not multiply, so that they cannot leak in
-        const bool on = kcol <= q && q < e;
-        const float p = on ? __builtin_amdgcn_exp2f(sp[qb][e_] * c2 - lv[i] * kLog2e) : 0.f;
-        sp[qb][e_] = p;
-        dp[qb][e_] = on ? p * (dp[qb][e_] - dv_[i]) : 0.f;
-      }
-    }
   // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
+  {
+    uint4 tq[3], to[3];
+    auto ld = [&](int st) {
+      const int r = (st / (2 * NB)) * 32 + ((st / NB) & 1) * 16, nb = st % NB;
+      to[st % 3] = lo.tr_frag(ot, r, nb);
+      tq[st % 3] = lo.tr_frag(qt, r, nb);
+    };
+    ld(0);
+    ld(1);
+    uint4 pa, da;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 pa = pack_frag(sp[qb], i);
-      const uint4 da = pack_frag(dp[qb], i);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        dv[nb] = mma(pa, lo.tr_frag(ot, qb * 32 + 16 * i, nb), dv[nb]);
-        dk[nb] = mma(da, lo.tr_frag(qt, qb * 32 + 16 * i, nb), dk[nb]);
+    for (int st = 0; st < 4 * NB; ++st) {
+      if (st + 2 < 4 * NB) ld(st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int qb = st / (2 * NB), i = (st / NB) & 1, nb = st % NB;
+      if (nb == 0) {
+        pa = pack_frag(sp[qb], i);
+        da = pack_frag(dp[qb], i);
       }
+      dv[nb] = mma(pa, to[st % 3], dv[nb]);
+      dk[nb] = mma(da, tq[st % 3], dk[nb]);
+      if (qb == 0) dkdv_softmax_part<DH>(sp[1], dp[1], ls, dl, 1, st, q0, kcol, e, lane, c2, mask);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
 }
 
 template <int DH>
@@ -453,13 +493,18 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
     issue(Q1, O1, L1, E1, min(it + 1, n - 1));
     {
       const int q0 = qstart(it);
-      if (q0 + 63 >= kw) dkdv_tile<DH>(lo, Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
+      // tiles wholly after the wave's keys and inside the chunk need no mask
+      if (q0 + 63 >= kw)
+        dkdv_tile<DH>(lo, Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, !(q0 >= kw + 31 && q0 + 64 <= a.e),
+                      kf, vf, dk, dv);
     }
     dma_barrier();
     issue(Q0, O0, L0, E0, min(it + 2, n - 1));
     if (it + 1 < n) {
       const int q0 = qstart(it + 1);
-      if (q0 + 63 >= kw) dkdv_tile<DH>(lo, Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, kf, vf, dk, dv);
+      if (q0 + 63 >= kw)
+        dkdv_tile<DH>(lo, Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, !(q0 >= kw + 31 && q0 + 64 <= a.e),
+                      kf, vf, dk, dv);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
@@ -494,7 +539,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
 // dQ.  Block: 4 waves, 128 queries (32 per wave), one q head; key tiles of
 // 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
-template <int DH>
+template <int DH, bool MASK>
 __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
                                         float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
                                         const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32]) {
@@ -515,7 +560,7 @@ __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, co
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + kb * 32 + crow(e, lane);
-      const float p = (key <= qcol) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
+      const float p = (!MASK || key <= qcol) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
       dpt[kb][e] = p * (dpt[kb][e] - dl);
     }
   // dQ[q, dh] += dS[q, key] K[key, dh]
@@ -531,7 +576,7 @@ __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, co
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   constexpr int NB = DH / 32, KS = DH / 16;
   __shared__ __attribute__((aligned(16))) char K0[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char V0[64 * DH * 2];
@@ -557,7 +602,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   }
   const bool qok = qcol < a.e;
   const float c2 = a.scale * kLog2e;
-  const float lse2 = qok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(qcol - a.s) * a.lse_st] * kLog2e : INFINITY;
+  const float lse2 = qok ? a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)(qcol - a.s) * a.lse_st] : INFINITY;
   const float dl = qok ? a.delta[(int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (int64_t)(qcol - a.s) * a.dl_st] : 0.f;
   f32x16_t dq[NB];
 #pragma unroll
@@ -574,11 +619,14 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(AttnArgs a) {
   for (int t = 0; t < ntiles; t += 2) {
     dma_barrier();
     issue(K1, V1, min(t + 1, ntiles - 1));
-    if (t * 64 <= qw + 31) dq_tile<DH>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    if (t * 64 + 63 <= qw) dq_tile<DH, false>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    else if (t * 64 <= qw + 31) dq_tile<DH, true>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
     dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
-    if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      dq_tile<DH>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    if (t + 1 < ntiles && (t + 1) * 64 + 63 <= qw)
+      dq_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    else if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
+      dq_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries

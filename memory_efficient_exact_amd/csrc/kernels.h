@@ -70,8 +70,10 @@ sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, 
 sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* dn, int64_t ldn,
                        const float* rinv, const void* resid, int64_t ldr, int64_t rows, int64_t d,
                        void* out, int64_t ldo, hipStream_t st);
+// part: gain_grad_splits(rows) * d floats of scratch
+int gain_grad_splits(int64_t rows);
 sbp_status gain_grad(const float* dn, int64_t ldn, const void* x, int64_t ldx, const float* rinv,
-                     int64_t rows, int64_t d, float* dg, int beta, hipStream_t st);
+                     int64_t rows, int64_t d, float* dg, int beta, float* part, hipStream_t st);
 sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStream_t st);
 sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, void* dudg,
                       hipStream_t st);

@@ -58,7 +58,7 @@ struct LayerWs {
   float *dKacc, *dVacc;
   bf16_t *W2T, *W13T, *WoT, *WqkvT;
   bf16_t *h1, *q, *o, *a, *n2, *ug, *mdm, *dudg, *da, *dov, *dqkv;
-  float *dn, *rinv1, *rinv2, *lse, *delta;
+  float *dn, *rinv1, *rinv2, *lse, *delta, *gpart;
   bf16_t *TA, *TB;
 };
 
@@ -92,6 +92,7 @@ size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
   x.rinv2 = (float*)P.take(f4 * R);
   x.lse = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   x.delta = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
+  x.gpart = (float*)P.take(f4 * gain_grad_splits(R) * s.d);
   const int64_t maxA = std::max(std::max(s.d, 2 * s.F), s.qkvd);
   const int64_t maxB = std::max(std::max(s.F, s.d), s.qd);
   x.TA = (bf16_t*)P.take(b2 * maxA * s.Tcp);
@@ -240,7 +241,7 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     SBP_TRY(gemm(W.TA + F * Tp, Tp, W.TB, Tp, g->W3, d, F, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
     SBP_TRY(gemm(W.dudg, 2 * F, W.W13T, 2 * F, W.dn, d, Tc, d, 2 * F, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(W.a, d, w->g2, W.dn, d, W.rinv2, dyc, d, Tc, d, W.da, d, str));
-    SBP_TRY(gain_grad(W.dn, d, W.a, d, W.rinv2, Tc, d, g->g2, wb, str));
+    SBP_TRY(gain_grad(W.dn, d, W.a, d, W.rinv2, Tc, d, g->g2, wb, W.gpart, str));
 
     // ---- output projection ----
     SBP_TRY(tr(W.da, d, Tc, d, W.TA, Tp, Tp));           // da^T [d, Tp]
@@ -263,7 +264,7 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     SBP_TRY(gemm(W.TA + (qd + kd) * Tp, Tp, W.TB, Tp, g->Wv, d, kd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
     SBP_TRY(gemm(W.dqkv, qkvd, W.WqkvT, qkvd, W.dn, d, Tc, d, qkvd, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(xc, d, w->g1, W.dn, d, W.rinv1, W.da, d, Tc, d, DX + s0 * d, d, str));
-    SBP_TRY(gain_grad(W.dn, d, xc, d, W.rinv1, Tc, d, g->g1, wb, str));
+    SBP_TRY(gain_grad(W.dn, d, xc, d, W.rinv1, Tc, d, g->g1, wb, W.gpart, str));
   }
 #undef SBP_TRY
   return SBP_OK;

@@ -83,31 +83,68 @@ sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* d
   return SBP_OK;
 }
 
-// dg[j] (+)= sum_r dn[r][j] * x[r][j] * rinv[r]; 64 columns per block,
-// 4 row groups reduced through LDS (deterministic, no atomics).
-__global__ __launch_bounds__(256) void gain_grad_kernel(const float* __restrict__ dn, int64_t ldn,
+// dg[j] (+)= sum_r dn[r][j] * x[r][j] * rinv[r].
+// Pass 1: block (256 columns, row split s); each thread owns 4 columns
+// (float4 of dn, 4 bf16 of x), the 4 waves stride the split's rows and are
+// summed through LDS into part[s][j].  Pass 2 sums the splits in order, so
+// the result is deterministic.
+__global__ __launch_bounds__(256) void gain_part_kernel(const float* __restrict__ dn, int64_t ldn,
                                                         const bf16_t* __restrict__ x, int64_t ldx,
                                                         const float* __restrict__ rinv, int64_t rows,
-                                                        int d, float* __restrict__ dg, int beta) {
-  __shared__ float sh[4][64];
-  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + c;
-  float acc = 0.f;
+                                                        int d, int64_t rps, float* __restrict__ part) {
+  __shared__ float4 sh[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 256 + lane * 4;
+  const int64_t r0 = (int64_t)blockIdx.y * rps, r1 = min(rows, r0 + rps);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (j < d)
-    for (int64_t r = rg; r < rows; r += 4) acc += dn[r * ldn + j] * bf2f(x[r * ldx + j]) * rinv[r];
-  sh[rg][c] = acc;
+    for (int64_t r = r0 + w; r < r1; r += 4) {
+      const float4 g = *reinterpret_cast<const float4*>(dn + r * ldn + j);
+      const uint2 u = *reinterpret_cast<const uint2*>(x + r * ldx + j);
+      const float ri = rinv[r];
+      acc.x += g.x * bf2f((bf16_t)(u.x & 0xffff)) * ri;
+      acc.y += g.y * bf2f((bf16_t)(u.x >> 16)) * ri;
+      acc.z += g.z * bf2f((bf16_t)(u.y & 0xffff)) * ri;
+      acc.w += g.w * bf2f((bf16_t)(u.y >> 16)) * ri;
+    }
+  sh[w][lane] = acc;
   __syncthreads();
-  if (rg == 0 && j < d) {
-    const float s = sh[0][c] + sh[1][c] + sh[2][c] + sh[3][c];
-    dg[j] = beta ? dg[j] + s : s;
+  if (w == 0 && j < d) {
+    float4 t = sh[0][lane];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      t.x += sh[k][lane].x;
+      t.y += sh[k][lane].y;
+      t.z += sh[k][lane].z;
+      t.w += sh[k][lane].w;
+    }
+    *reinterpret_cast<float4*>(part + (int64_t)blockIdx.y * d + j) = t;
   }
 }
 
+__global__ __launch_bounds__(256) void gain_sum_kernel(const float* __restrict__ part, int nsplit,
+                                                       int d, float* __restrict__ dg, int beta) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  float s = 0.f;
+  for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * d + j];
+  dg[j] = beta ? dg[j] + s : s;
+}
+
+int gain_grad_splits(int64_t rows) { return (int)std::max<int64_t>(1, std::min<int64_t>(64, rows / 32)); }
+
 sbp_status gain_grad(const float* dn, int64_t ldn, const void* x, int64_t ldx, const float* rinv,
-                     int64_t rows, int64_t d, float* dg, int beta, hipStream_t st) {
+                     int64_t rows, int64_t d, float* dg, int beta, float* part, hipStream_t st) {
+  if ((uintptr_t)dn % 16 || (uintptr_t)x % 8 || (uintptr_t)part % 16 || ldn % 4 || ldx % 4 || d % 4)
+    return set_error(SBP_ERR_INVALID_ARG, "gain_grad: rows must be 16-byte (fp32) / 8-byte (bf16) aligned");
   ProfScope prof("gain_grad", st, 0.0, 6.0 * rows * d);
-  hipLaunchKernelGGL(gain_grad_kernel, dim3((unsigned)cdiv(d, 64)), dim3(256), 0, st, dn, ldn,
-                     (const bf16_t*)x, ldx, rinv, rows, (int)d, dg, beta);
+  const int ns = gain_grad_splits(rows);
+  const int64_t rps = cdiv(std::max<int64_t>(rows, 1), ns);
+  hipLaunchKernelGGL(gain_part_kernel, dim3((unsigned)cdiv(d, 256), (unsigned)ns), dim3(256), 0, st, dn,
+                     ldn, (const bf16_t*)x, ldx, rinv, rows, (int)d, rps, part);
+  SBP_LAUNCH_CHECK();
+  hipLaunchKernelGGL(gain_sum_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0, st, part, ns, (int)d,
+                     dg, beta);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }
