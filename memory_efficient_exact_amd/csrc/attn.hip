@@ -96,6 +96,28 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Block -> work mapping for the 8 XCDs.  Workgroups are dispatched
+// round-robin over the XCDs in linear order (x fastest), so the kv head is
+// taken from the low part of the linear id: when Hkv divides 8 every block
+// of one kv head runs on the same XCD and the K / V (or Q / dO) it streams
+// stays in that XCD's L2.  Query blocks are issued heaviest (most keys)
+// first.
+struct QBlock {
+  int h, qblk;
+};
+__device__ __forceinline__ QBlock q_block(int Hkv, int G) {
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int kv = lin % Hkv, r = lin / Hkv;
+  return {kv * G + r % G, (int)gridDim.x - 1 - r / G};
+}
+struct KBlock {
+  int kv, kblk;
+};
+__device__ __forceinline__ KBlock k_block(int Hkv) {
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  return {lin % Hkv, lin / Hkv};
+}
+
 // Per-lane LDS byte offsets of the fragment reads of a swizzled tile, so
 // that every read is a per-lane register plus a compile-time immediate:
 //   row read, rows rbase + l%32 (rbase % 32 == 0), k16 step ks (16-byte
@@ -234,9 +256,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const QBlock qbk = q_block(a.Hkv, a.G);
+  const int h = qbk.h, b = blockIdx.z, kv = h / a.G;
   const LdsOff<DH> lo(lane);
-  const int q0 = a.s + blockIdx.x * 128;            // first query of the block
+  const int q0 = a.s + qbk.qblk * 128;              // first query of the block
   const int qw = q0 + wave * 32;                    // first query of the wave
   const int qcol = qw + (lane & 31);                // this lane's query
   const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
@@ -448,9 +471,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char O1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) float L0[64], E0[64], L1[64], E1[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kv = blockIdx.y, b = blockIdx.z;
+  const KBlock kbk = k_block(a.Hkv);
+  const int kv = kbk.kv, b = blockIdx.z;
   const LdsOff<DH> lo(lane);
-  const int kbase = blockIdx.x * 128;
+  const int kbase = kbk.kblk * 128;
   const int kw = kbase + wave * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
   const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
@@ -583,9 +607,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char K1[64 * DH * 2];
   __shared__ __attribute__((aligned(16))) char V1[64 * DH * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, b = blockIdx.z, kv = h / a.G;
+  const QBlock qbk = q_block(a.Hkv, a.G);
+  const int h = qbk.h, b = blockIdx.z, kv = h / a.G;
   const LdsOff<DH> lo(lane);
-  const int q0 = a.s + blockIdx.x * 128;
+  const int q0 = a.s + qbk.qblk * 128;
   const int qw = q0 + wave * 32;
   const int qcol = qw + (lane & 31);
   const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
