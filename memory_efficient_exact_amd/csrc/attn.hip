@@ -372,22 +372,42 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
 // statistics rows are padded past the chunk so every 64-row fetch is in
 // bounds, and queries at or past e are masked.
 // ---------------------------------------------------------------------------
-// P and dS of one 32-query half qb of the tile, in place, for result
-// elements [16 part / KS, 16 (part + 1) / KS).  Branch-free (the exponent is
+// Softmax jobs of a dK/dV tile: job j = half j / KS, result elements
+// [PER (j % KS), PER (j % KS + 1)), PER = 16 / KS, whose rows are PER
+// consecutive rows (crow of an aligned group of PER elements).
+template <int DH>
+struct DkdvStats {
+  static constexpr int KS = DH / 16, PER = 16 / KS;
+  float l[2][PER], d[2][PER];  // LSE / Delta rows of two jobs in flight
+  // read the rows of job j into slot j & 1 (one vector read per row set)
+  __device__ __forceinline__ void load(const float* ls, const float* dl, int j, int lane) {
+    const int r = (j / KS) * 32 + crow((j % KS) * PER, lane);
+    if constexpr (PER == 2) {
+      const float2 a = *reinterpret_cast<const float2*>(ls + r), b = *reinterpret_cast<const float2*>(dl + r);
+      l[j & 1][0] = a.x; l[j & 1][1] = a.y;
+      d[j & 1][0] = b.x; d[j & 1][1] = b.y;
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(ls + r), b = *reinterpret_cast<const float4*>(dl + r);
+      l[j & 1][0] = a.x; l[j & 1][1] = a.y; l[j & 1][2] = a.z; l[j & 1][3] = a.w;
+      d[j & 1][0] = b.x; d[j & 1][1] = b.y; d[j & 1][2] = b.z; d[j & 1][3] = b.w;
+    }
+  }
+};
+
+// P and dS of softmax job j, in place.  Branch-free (the exponent is
 // computed for every lane, then selected), so that it can sit between the
 // other half's MFMAs.
 template <int DH>
-__device__ __forceinline__ void dkdv_softmax_part(f32x16_t& sp, f32x16_t& dp, const float* ls,
-                                                  const float* dl, int qb, int part, int q0,
-                                                  int kcol, int e, int lane, float c2, bool mask) {
-  constexpr int PER = 16 / (DH / 16);
+__device__ __forceinline__ void dkdv_softmax_job(f32x16_t& sp, f32x16_t& dp, const DkdvStats<DH>& stt,
+                                                 int j, int q0, int kcol, int e, int lane, float c2,
+                                                 bool mask) {
+  constexpr int KS = DH / 16, PER = 16 / KS;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int e_ = part * PER + k;
-    const int r = qb * 32 + crow(e_, lane);
-    const int q = q0 + r;
-    float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - ls[r]);
-    float g = p * (dp[e_] - dl[r]);
+    const int e_ = (j % KS) * PER + k;
+    const int q = q0 + (j / KS) * 32 + crow(e_, lane);
+    float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - stt.l[j & 1][k]);
+    float g = p * (dp[e_] - stt.d[j & 1][k]);
     if (mask) {  // wave-uniform: a scalar branch
       asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
       // statistics rows past the chunk are padding (any value): select, do
@@ -403,7 +423,10 @@ __device__ __forceinline__ void dkdv_softmax_part(f32x16_t& sp, f32x16_t& dp, co
 
 // One 64-query tile against the wave's 32 keys, software-pipelined: LDS
 // fragments are read two steps ahead of the MFMAs that use them, and the
-// softmax of one 32-query half is spread over the MFMA steps of the other.
+// softmax of one 32-query half is spread over the MFMA steps of the other
+// (job j of half 0 at S/dP step KS + j, job j of half 1 at dV/dK step j),
+// its statistics read one step ahead, before that step's fragment reads, so
+// that waiting for them never drains the fragment prefetch.
 //   steps 0 .. 2KS-1:  S, dP of half 0, then half 1 (+ softmax of half 0)
 //   steps 0 .. 4NB-1:  dV, dK from half 0 (+ softmax of half 1), then half 1
 template <int DH>
@@ -414,6 +437,7 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, 
   constexpr int NB = DH / 32, KS = DH / 16;
   f32x16_t sp[2], dp[2];
   sp[0] = sp[1] = dp[0] = dp[1] = f32x16_t{};
+  DkdvStats<DH> stt;
   // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two 32-query halves
   {
     uint4 fq[3], fo[3];
@@ -425,12 +449,14 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, 
     ld(1);
 #pragma unroll
     for (int st = 0; st < 2 * KS; ++st) {
+      if (st >= KS - 1) stt.load(ls, dl, st - KS + 1, lane);  // jobs 0 .. KS
+      __builtin_amdgcn_sched_barrier(0);
       if (st + 2 < 2 * KS) ld(st + 2);
       __builtin_amdgcn_sched_barrier(0);
       const int qb = st / KS, ks = st % KS;
       sp[qb] = mma(fq[st % 3], kf[ks], sp[qb]);
       dp[qb] = mma(fo[st % 3], vf[ks], dp[qb]);
-      if (qb == 1) dkdv_softmax_part<DH>(sp[0], dp[0], ls, dl, 0, ks, q0, kcol, e, lane, c2, mask);
+      if (qb == 1) dkdv_softmax_job<DH>(sp[0], dp[0], stt, ks, q0, kcol, e, lane, c2, mask);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -447,6 +473,8 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, 
     uint4 pa, da;
 #pragma unroll
     for (int st = 0; st < 4 * NB; ++st) {
+      if (st + 1 < KS) stt.load(ls, dl, KS + st + 1, lane);  // jobs KS + 1 .. 2KS - 1
+      __builtin_amdgcn_sched_barrier(0);
       if (st + 2 < 4 * NB) ld(st + 2);
       __builtin_amdgcn_sched_barrier(0);
       const int qb = st / (2 * NB), i = (st / NB) & 1, nb = st % NB;
@@ -456,7 +484,7 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, 
       }
       dv[nb] = mma(pa, to[st % 3], dv[nb]);
       dk[nb] = mma(da, tq[st % 3], dk[nb]);
-      if (qb == 0) dkdv_softmax_part<DH>(sp[1], dp[1], ls, dl, 1, st, q0, kcol, e, lane, c2, mask);
+      if (st < KS) dkdv_softmax_job<DH>(sp[1], dp[1], stt, KS + st, q0, kcol, e, lane, c2, mask);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
