@@ -559,6 +559,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   float beta = (float)p.beta;
   if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
   const bool vec_ok = (p.ldc % 4 == 0) && (EPI != EPI_OUT_RESID || p.ldr % 4 == 0);
+  // All 16 vector passes of a wave's 32-row block are one batch: its old C
+  // (read-modify-write) or residual values are loaded before any of its
+  // stores, so the 16 loads are in flight together.
+  constexpr int BATCH = 16;
+  constexpr bool LOADS = EPI == EPI_F32_ACC || EPI == EPI_OUT_RESID;
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
@@ -569,57 +574,75 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         W[lr * 128 + fn * 32 + (lane & 31)] = acc[fm][fn][e];
       }
     __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int lr = it * 2 + (lane >> 5);
-      const int lc = (lane & 31) * 4;
-      const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + lc]);
-      float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
-      const int row = m0 + wm * WT + fm * 32 + lr;
-      const int col = n0 + wn * WT + lc;
-      if (row >= p.M || col >= p.N) continue;
-      const int64_t off = (int64_t)row * p.ldc + col;
-      if (vec_ok && col + 4 <= p.N) {
-        if constexpr (EPI == EPI_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_PARTIAL) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_F32_ACC) {
-          float4* c = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off);
-          if (beta != 0.f) {
-            const float4 o = *c;
-            *c = make_float4(v[0] + beta * o.x, v[1] + beta * o.y, v[2] + beta * o.z, v[3] + beta * o.w);
+#pragma unroll
+    for (int it0 = 0; it0 < 16; it0 += BATCH) {
+      float4 old[BATCH];
+      if constexpr (LOADS) {
+#pragma unroll
+        for (int bq = 0; bq < BATCH; ++bq) {
+          const int lr = (it0 + bq) * 2 + (lane >> 5);
+          const int row = m0 + wm * WT + fm * 32 + lr;
+          const int col = n0 + wn * WT + (lane & 31) * 4;
+          old[bq] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (row >= p.M || !vec_ok || col + 4 > p.N) continue;
+          if constexpr (EPI == EPI_F32_ACC) {
+            if (beta != 0.f)
+              old[bq] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) +
+                                                         (int64_t)row * p.ldc + col);
           } else {
-            *c = make_float4(v[0], v[1], v[2], v[3]);
+            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.R) +
+                                                            (int64_t)row * p.ldr + col);
+            old[bq] = make_float4(bf2f((bf16_t)(r.x & 0xffff)), bf2f((bf16_t)(r.x >> 16)),
+                                  bf2f((bf16_t)(r.y & 0xffff)), bf2f((bf16_t)(r.y >> 16)));
+          }
+        }
+      }
+#pragma unroll
+      for (int bq = 0; bq < BATCH; ++bq) {
+        const int lr = (it0 + bq) * 2 + (lane >> 5);
+        const int lc = (lane & 31) * 4;
+        const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + lc]);
+        float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
+        const int row = m0 + wm * WT + fm * 32 + lr;
+        const int col = n0 + wn * WT + lc;
+        if (row >= p.M || col >= p.N) continue;
+        const int64_t off = (int64_t)row * p.ldc + col;
+        if (vec_ok && col + 4 <= p.N) {
+          if constexpr (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_PARTIAL) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_F32_ACC) {
+            const float4 o = old[bq];
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) =
+                make_float4(v[0] + beta * o.x, v[1] + beta * o.y, v[2] + beta * o.z, v[3] + beta * o.w);
+          } else {
+            if constexpr (EPI == EPI_OUT_RESID) {
+              v[0] += old[bq].x; v[1] += old[bq].y; v[2] += old[bq].z; v[3] += old[bq].w;
+            }
+            uint2 u;
+            u.x = pk_bf16(v[0], v[1]);
+            u.y = pk_bf16(v[2], v[3]);
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
           }
         } else {
-          if constexpr (EPI == EPI_OUT_RESID) {
-            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.R) + (int64_t)row * p.ldr + col);
-            v[0] += bf2f((bf16_t)(r.x & 0xffff)); v[1] += bf2f((bf16_t)(r.x >> 16));
-            v[2] += bf2f((bf16_t)(r.y & 0xffff)); v[3] += bf2f((bf16_t)(r.y >> 16));
-          }
-          uint2 u;
-          u.x = pk_bf16(v[0], v[1]);
-          u.y = pk_bf16(v[2], v[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
-        }
-      } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (col + j >= p.N) break;
-          if constexpr (EPI == EPI_F32) {
-            reinterpret_cast<float*>(p.C)[off + j] = v[j];
-          } else if constexpr (EPI == EPI_PARTIAL) {
-            reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
-          } else if constexpr (EPI == EPI_F32_ACC) {
-            float* c = reinterpret_cast<float*>(p.C) + off + j;
-            *c = (beta != 0.f) ? (v[j] + beta * *c) : v[j];
-          } else if constexpr (EPI == EPI_OUT) {
-            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j]);
-          } else {
-            const float r = Elem<bf16_t>::load(reinterpret_cast<const bf16_t*>(p.R), (int64_t)row * p.ldr + col + j);
-            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j] + r);
+          for (int j = 0; j < 4; ++j) {
+            if (col + j >= p.N) break;
+            if constexpr (EPI == EPI_F32) {
+              reinterpret_cast<float*>(p.C)[off + j] = v[j];
+            } else if constexpr (EPI == EPI_PARTIAL) {
+              reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
+            } else if constexpr (EPI == EPI_F32_ACC) {
+              float* c = reinterpret_cast<float*>(p.C) + off + j;
+              *c = (beta != 0.f) ? (v[j] + beta * *c) : v[j];
+            } else if constexpr (EPI == EPI_OUT) {
+              Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j]);
+            } else {
+              const float r = Elem<bf16_t>::load(reinterpret_cast<const bf16_t*>(p.R), (int64_t)row * p.ldr + col + j);
+              Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j] + r);
+            }
           }
         }
       }
