@@ -7,8 +7,9 @@
 // a per-token weight multiplies (GRPO / DPO, "Practical Guidance", "Loss
 // Objectives").
 //
-//   lm_prep     one block: N, 1/N, which chunks hold a valid token, and
-//               which chunk's dW GEMM overwrites instead of adding.
+//   lm_prep     one block: N, 1/N, which chunks (and which groups of G
+//               chunks sharing one dW GEMM) hold a valid token, and which
+//               group's dW GEMM overwrites instead of adding.
 //   ce_stats    one block per row: online max / sum-exp over the fp32 logits
 //               row (wave64 shuffles, then LDS across waves) -> lse, l_t.
 //   ce_grad     64 x 128 tiles: dZ = (c_t/N)(exp(z - lse) - onehot), written
@@ -22,8 +23,8 @@
 namespace sbp {
 
 __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict__ y, int64_t T,
-                                                       int32_t D, int reduction, int accumulate,
-                                                       LmPrep pr) {
+                                                       int32_t D, int32_t G, int reduction,
+                                                       int accumulate, LmPrep pr) {
   __shared__ int s_cnt[16];
   __shared__ int s_first[16];
   const int tid = threadIdx.x;
@@ -63,13 +64,19 @@ __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict
   }
   __syncthreads();
   const int f = s_first[0];
-  for (int c = tid; c < D; c += blockDim.x) pr.beta_zero[c] = (!accumulate && c == f) ? 1 : 0;
+  const int ng = (D + G - 1) / G;
+  for (int g = tid; g < ng; g += blockDim.x) {
+    int any = 0;
+    for (int c = g * G; c < min(D, (g + 1) * G); ++c) any |= pr.chunk_active[c];
+    pr.group_active[g] = any;
+    pr.beta_zero[g] = (!accumulate && f < D && g == f / G) ? 1 : 0;
+  }
 }
 
-sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int reduction, int accumulate,
-                   const LmPrep& pr, hipStream_t st) {
+sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int reduction,
+                   int accumulate, const LmPrep& pr, hipStream_t st) {
   ProfScope prof("lm_prep", st, 0.0, 4.0 * T);
-  hipLaunchKernelGGL(lm_prep_kernel, dim3(1), dim3(1024), 0, st, targets, T, D, reduction,
+  hipLaunchKernelGGL(lm_prep_kernel, dim3(1), dim3(1024), 0, st, targets, T, D, G, reduction,
                      accumulate, pr);
   SBP_LAUNCH_CHECK();
   return SBP_OK;

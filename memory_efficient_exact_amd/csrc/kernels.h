@@ -35,11 +35,12 @@ struct LmPrep {   // device-side scalars written by lm_prep
   int* n_valid;       // [1]
   float* inv_norm;    // [1]  1/N (mean_valid, N>0), 1 (sum), 0 (N == 0)
   int* chunk_active;  // [D]
-  int* beta_zero;     // [D]  1 for the chunk whose dW GEMM must overwrite
+  int* group_active;  // [ceil(D/G)]  1 if a chunk of dW group g (chunks gG .. gG+G-1) is active
+  int* beta_zero;     // [ceil(D/G)]  1 for the group whose dW GEMM must overwrite
   int* none_active;   // [1]  1 if no chunk has a valid token
 };
-sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int reduction, int accumulate,
-                   const LmPrep& pr, hipStream_t st);
+sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int reduction,
+                   int accumulate, const LmPrep& pr, hipStream_t st);
 // Per-row log-sum-exp and per-token loss for rows [s, s+Tc) of one chunk.
 sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
                     int64_t s, int64_t Tc, int64_t V, float* lse, float* loss_part,

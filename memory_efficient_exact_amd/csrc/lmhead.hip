@@ -8,8 +8,12 @@
 //   dZ_c, dZ_c^T                   dtype, zero-padded      (ce_grad)
 //   H_c^T                          dtype [d, T_c]          (transpose_pad)
 //   dH_c  = dZ_c W = dZ_c (W^T)^T  split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
-//   dW   += dZ_c^T H_c             fp32 read-modify-write  (gemm EPI_F32_ACC)
-// W^T is formed once per call.  Peak workspace is O(T_c V + V d), not O(T V).
+//   dW   += dZ_g^T H_g             fp32 read-modify-write  (gemm EPI_F32_ACC)
+// W^T is formed once per call.  The weight gradient is taken once per group
+// g of G consecutive chunks (dZ_c^T and H_c^T of the group side by side in
+// the K dimension, so that the sum over the group's tokens is one GEMM):
+// the fp32 read-modify-write of dW is paid once per G chunks and K is G T_c
+// long.  Peak workspace is O(G T_c V + V d), not O(T V).
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +38,8 @@ struct LmShape {
   int dtype;
   int64_t Tcm, Tcp, Vp;
   int S;  // split count of the dH GEMM
+  int G;  // chunks per dW GEMM
+  int64_t Kg;  // K extent of the dW group buffers: G * Tcp
   size_t esz;
 };
 
@@ -51,6 +57,11 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   S = std::max<int64_t>(1, std::min<int64_t>(S, 16));
   S = std::min<int64_t>(S, std::max<int64_t>(1, s.Vp / 512));
   s.S = (int)S;
+  // dW group: about 4096 tokens of K per weight-gradient GEMM (its fp32
+  // read-modify-write of the V x d gradient then costs a quarter byte per
+  // flop or less); a function of the shape only.
+  s.G = (int)std::max<int64_t>(1, std::min<int64_t>(D, 4096 / s.Tcp));
+  s.Kg = s.G * s.Tcp;
   return s;
 }
 
@@ -60,9 +71,9 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   LmWs x;
   x.Z = (float*)P.take(sizeof(float) * s.Tcm * s.Vp);
   x.dZ = P.take(s.esz * s.Tcm * s.Vp);
-  x.dZt = P.take(s.esz * s.Vp * s.Tcp);
+  x.dZt = P.take(s.esz * s.Vp * s.Kg);
   x.Wt = P.take(s.esz * s.d * s.Vp);
-  x.Ht = P.take(s.esz * s.d * s.Tcp);
+  x.Ht = P.take(s.esz * s.d * s.Kg);
   x.part = (float*)P.take(sizeof(float) * (size_t)s.S * s.Tcm * s.d);
   x.lse = (float*)P.take(sizeof(float) * s.Tcm);
   x.loss_part = (float*)P.take(sizeof(float) * s.T);
@@ -70,7 +81,8 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   x.prep.inv_norm = (float*)P.take(sizeof(float));
   x.prep.none_active = (int*)P.take(sizeof(int));
   x.prep.chunk_active = (int*)P.take(sizeof(int) * s.D);
-  x.prep.beta_zero = (int*)P.take(sizeof(int) * s.D);
+  x.prep.group_active = (int*)P.take(sizeof(int) * cdiv(s.D, s.G));
+  x.prep.beta_zero = (int*)P.take(sizeof(int) * cdiv(s.D, s.G));
   if (w) *w = x;
   return round_up((int64_t)P.off, 256);
 }
@@ -133,15 +145,20 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     if (_s != SBP_OK) return _s;     \
   } while (0)
 
-  SBP_TRY(lm_prep(targets, T, D, reduction, accumulate, w.prep, str));
+  SBP_TRY(lm_prep(targets, T, D, s.G, reduction, accumulate, w.prep, str));
   // W^T [d, Vp], zero columns V..Vp (they meet the zero pad of dZ in the dH GEMM)
   SBP_TRY(transpose_pad(dtype, W, d, V, d, w.Wt, s.Vp, s.Vp, nullptr, str));
   for (int32_t c = 0; c < D; ++c) {
     int64_t s0, e0;
     chunk_bounds(T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
-    const int64_t Tcp = round_up(Tc, 128);
     const int* act = w.prep.chunk_active + c;
+    // slot j of dW group g: columns [j Tcp, (j + 1) Tcp) of dZ^T and H^T,
+    // zero past the chunk's T_c.  In a group of several chunks an inactive
+    // chunk still writes its slot (zeros for dZ^T: every row has c_t = 0).
+    const int g = c / s.G, j = c % s.G;
+    const bool last_in_group = j == s.G - 1 || c == D - 1;
+    const int* slot_act = s.G == 1 ? act : nullptr;
 
     GemmParams g1;
     g1.A = Hb + s0 * d * s.esz; g1.lda = d;
@@ -154,8 +171,9 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
 
     SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
     SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
-                    w.dZ, s.Vp, w.dZt, Tcp, Tcp, act, str));
-    SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, w.Ht, Tcp, Tcp, act, str));
+                    w.dZ, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp, slot_act, str));
+    SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, (char*)w.Ht + j * s.Tcp * s.esz, s.Kg,
+                          s.Tcp, slot_act, str));
 
     GemmParams g2;
     g2.A = w.dZ; g2.lda = s.Vp;
@@ -170,14 +188,15 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     SBP_TRY(splitk_reduce(dtype, w.part, s.Tcm * d, s.S, Tc, d, d, (char*)dH + s0 * d * s.esz, d,
                           act, str));
 
+    if (!last_in_group) continue;
     GemmParams g3;
-    g3.A = w.dZt; g3.lda = Tcp;
-    g3.B = w.Ht; g3.ldb = Tcp;
+    g3.A = w.dZt; g3.lda = s.Kg;
+    g3.B = w.Ht; g3.ldb = s.Kg;
     g3.C = dW; g3.ldc = d;
-    g3.M = (int)V; g3.N = (int)d; g3.K = (int)Tcp;
+    g3.M = (int)V; g3.N = (int)d; g3.K = (int)((j + 1) * s.Tcp);
     g3.beta = 1;
-    g3.beta_zero = w.prep.beta_zero + c;
-    g3.active = act;
+    g3.beta_zero = w.prep.beta_zero + g;
+    g3.active = w.prep.group_active + g;
     g3.m_fastest = 0;
     SBP_TRY(gemm_nt(dtype, EPI_F32_ACC, g3, GEMM_TILE_RING, str, "gemm_dW"));
   }
