@@ -409,7 +409,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_256_kernel(GemmParams p) 
 // arrays.  Every DMA instruction fetches 8 rows x 128 bytes -- whole cache
 // lines; fetching half lines (16 rows x 64 bytes) was measured on the box to
 // move ~40% less data per second.  Rows are 8 x 16-byte chunks, chunk c of
-// row r at c ^ (r & 7).  Per stage t (4 k16 steps):
+// row r at c ^ ((r >> 1) & 7): gfx950's LDS serves 256 bytes (64 banks) per
+// clock, 16 lanes of a 16-byte fragment read, and rows r .. r+15 then fill
+// the 16 chunk positions of the two 128-byte halves of a bank line.  Per
+// stage t (4 k16 steps):
 //   read step 1 | MFMAs step 0 | read step 2 | MFMAs step 1 | read step 3 |
 //   MFMAs step 2 | wait for stage t+1, bare barrier | fetch stage t+2 into
 //   stage t's buffer | read step 0 of stage t+1 | MFMAs step 3
@@ -428,12 +431,12 @@ __device__ __forceinline__ void ring_load(const uint4* __restrict__ L, int ks, i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wm * WT + i * 32 + (lane & 31);
-    f.a[i] = L[r * 8 + (ch ^ (r & 7))];
+    f.a[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = BM + wn * WT + i * 32 + (lane & 31);
-    f.b[i] = L[r * 8 + (ch ^ (r & 7))];
+    f.b[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
   }
 }
 
@@ -464,7 +467,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   // DMA role: waves 0-1 fetch the A panel, 2-3 the B panel, 128 rows each
   const int opnd = wave >> 1;
   const int rbase = (wave & 1) * 128;
-  const int chunk = (lane & 7) ^ (lane >> 3);
+  // instruction j fills LDS rows lds_row0 + 8j + lane / 8 (lds_row0 % 16 == 0),
+  // slot lane % 8, with logical chunk slot ^ ((row >> 1) & 7)
+  const int chunk_even = (lane & 7) ^ (lane >> 4), chunk_odd = (lane & 7) ^ (4 + (lane >> 4));
   const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
   const int64_t ld = opnd ? p.ldb : p.lda;
   const int lim = opnd ? p.N : p.M;
@@ -474,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   auto issue_one = [&](uint4* L, int k0, int j) {
     int gr = r0 + j * 8;
     gr = gr < lim ? gr : lim - 1;
-    const bf16_t* g = X + (int64_t)gr * ld + k0 + chunk * 8;
+    const bf16_t* g = X + (int64_t)gr * ld + k0 + ((j & 1) ? chunk_odd : chunk_even) * 8;
     __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
                                      (SBP_AS3 void*)&L[(lds_row0 + j * 8) * 8], 16, 0, 0);
   };
