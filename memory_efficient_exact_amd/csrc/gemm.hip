@@ -214,13 +214,16 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
   const int lin = xcd * base + (xcd < rem ? xcd : rem) + idx;
   split = lin / ntile;
   const int t = lin - split * ntile;
-  if (p.m_fastest) {
-    tm = t % p.tiles_m;
-    tn = t / p.tiles_m;
-  } else {
-    tn = t % p.tiles_n;
-    tm = t / p.tiles_n;
-  }
+  // Grouped order: 8 tile rows at a time, m fastest inside the group, so an
+  // XCD's ~32 concurrent blocks cover about 8 x 4 tiles and share their A
+  // and B panels through its L2 (operand panels of long-K products are
+  // megabytes, so reuse has to be concurrent rather than over time).
+  constexpr int GM = 8;
+  const int g = t / (GM * p.tiles_n);
+  const int rows = min(GM, p.tiles_m - g * GM);
+  const int tl = t - g * GM * p.tiles_n;
+  tm = g * GM + tl % rows;
+  tn = tl / rows;
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

@@ -23,7 +23,7 @@ struct GemmParams {
   int k_split = 1;                 // EPI_PARTIAL: number of K ranges
   int k_per_split = 0;             // multiple of the K step (0 = even split)
   int64_t split_stride = 0;        // EPI_PARTIAL: elements between partial outputs
-  int m_fastest = 1;               // tile order inside an XCD's range
+  int m_fastest = 1;               // tile order inside an XCD's range (register-staged kernel only)
   int tiles_m = 0, tiles_n = 0;    // filled by the launcher
 };
 
