@@ -324,12 +324,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         if cfg["kind"] == "lmhead":
-            sample = args.cpu_sample or (256 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
+            sample = args.cpu_sample or (4096 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
             out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
         elif cfg["kind"] == "attn":
             out["cpu_baseline"] = cpu_baseline_attn(inp, cfg)
         else:
-            out["cpu_baseline"] = cpu_baseline_layer(inp, cfg, args.cpu_sample or 256)
+            out["cpu_baseline"] = cpu_baseline_layer(inp, cfg, args.cpu_sample or 1024)
     print(json.dumps(out), flush=True)
 
 

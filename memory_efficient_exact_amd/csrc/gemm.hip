@@ -458,6 +458,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   constexpr int BM = 256, BN = 256, BK = 64, WT = 128;
   __shared__ uint4 L0[(BM + BN) * 8];
   __shared__ uint4 L1[(BM + BN) * 8];
+  __shared__ uint32_t PF[4][64];  // sink of the L2 prefetches (never read)
   if (p.active && *p.active == 0) return;
   int tm, tn, split;
   tile_coords(p, tm, tn, split);
@@ -490,6 +491,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < 16; ++j) issue_one(L, k0, j);
   };
+  // L2 prefetch of the stage after the one being fetched: one 4-byte DMA per
+  // row touches the row's cache line of that K slice (2 instructions per
+  // wave), so that its real fetch a stage later finds the line in L2 (or
+  // already on its way).  The ring thus hides two stages of memory latency
+  // with two LDS buffers.
+  auto prefetch = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int gr = (opnd ? n0 : m0) + rbase + h * 64 + lane;
+      gr = gr < lim ? gr : lim - 1;
+      __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(X + (int64_t)gr * ld + k0),
+                                       (SBP_AS3 void*)&PF[wave][0], 4, 0, 0);
+    }
+  };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -510,6 +525,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue(L1, kb + BK);
+    prefetch(kb + min(2, nk - 1) * BK);
     ring_load(L0, 0, wm, wn, lane, f0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
@@ -531,7 +547,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     __builtin_amdgcn_sched_barrier(0);
     ring_mma(f0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stage t+1 landed, step 3 read
+    // stage t+1 landed (only the 2 prefetches issued after it may still be
+    // in flight), step 3 read
+    __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -553,6 +571,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
             0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    prefetch(kb + min(t + 3, nk - 1) * BK);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   };
   for (int it = 0; it < nk; it += 2) {
