@@ -76,10 +76,13 @@ __device__ __forceinline__ void dma_tile64(char* lds, const bf16_t* __restrict__
   }
 }
 
-// DMA 64 consecutive fp32 (16-byte aligned, in bounds) with lanes 0..15.
-__device__ __forceinline__ void dma_f32x64(float* lds, const float* __restrict__ src, int lane) {
-  if (lane < 16)
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + lane * 4), (SBP_LDS void*)lds, 16, 0, 0);
+// DMA of quarter q (16 floats) of a row of 64 consecutive fp32 (16-byte
+// aligned, in bounds) with lanes 0..3: four waves fetch one row together, so
+// that every wave issues the same number of DMAs.
+__device__ __forceinline__ void dma_f32x16(float* lds, const float* __restrict__ src, int q, int lane) {
+  if (lane < 4)
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + q * 16 + lane * 4),
+                                     (SBP_LDS void*)(lds + q * 16), 16, 0, 0);
 }
 
 // Double-buffer hand-over.  The DMA writes of a tile are counted by each
@@ -365,156 +368,140 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a, const bf16_
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Block: 4 waves, 128 keys (32 per wave), one kv head; iterates over
-// (q head of the group, 64-query tile of the chunk at or after the keys),
-// the Q / dO tiles and their LSE / Delta rows double-buffered by DMA.
-// Query tiles start at s + 64 j so the statistics rows are 16-byte aligned;
-// statistics rows are padded past the chunk so every 64-row fetch is in
-// bounds, and queries at or past e are masked.
+// dK, dV.  Block: 8 waves (two per SIMD), 128 keys, one kv head.  Wave w owns
+// the 32 keys kbase + 32 (w & 3) and the query half w >> 2 of every 64-query
+// tile; the two waves of a key group add their dK / dV partials through LDS
+// at the end.  K and V of the block stay in LDS for the whole loop (B
+// operands of S = Q K^T and dP = dO V^T, read per step), which keeps a wave
+// within 256 registers so that two waves share each SIMD and cover each
+// other's latencies.  The block iterates over (q head of the group, 64-query
+// tile of the chunk at or after the keys); the Q / dO tiles and their LSE /
+// Delta rows are double-buffered by DMA.  Query tiles start at s + 64 j so
+// the statistics rows are 16-byte aligned; statistics rows are padded past
+// the chunk so every 64-row fetch is in bounds, and queries at or past e are
+// masked.
 // ---------------------------------------------------------------------------
-// Softmax jobs of a dK/dV tile: job j = half j / KS, result elements
-// [PER (j % KS), PER (j % KS + 1)), PER = 16 / KS, whose rows are PER
-// consecutive rows (crow of an aligned group of PER elements).
-template <int DH>
-struct DkdvStats {
-  static constexpr int KS = DH / 16, PER = 16 / KS;
-  float l[2][PER], d[2][PER];  // LSE / Delta rows of two jobs in flight
-  // read the rows of job j into slot j & 1 (one vector read per row set)
-  __device__ __forceinline__ void load(const float* ls, const float* dl, int j, int lane) {
-    const int r = (j / KS) * 32 + crow((j % KS) * PER, lane);
-    if constexpr (PER == 2) {
-      const float2 a = *reinterpret_cast<const float2*>(ls + r), b = *reinterpret_cast<const float2*>(dl + r);
-      l[j & 1][0] = a.x; l[j & 1][1] = a.y;
-      d[j & 1][0] = b.x; d[j & 1][1] = b.y;
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(ls + r), b = *reinterpret_cast<const float4*>(dl + r);
-      l[j & 1][0] = a.x; l[j & 1][1] = a.y; l[j & 1][2] = a.z; l[j & 1][3] = a.w;
-      d[j & 1][0] = b.x; d[j & 1][1] = b.y; d[j & 1][2] = b.z; d[j & 1][3] = b.w;
-    }
-  }
-};
 
-// P and dS of softmax job j, in place.  Branch-free (the exponent is
-// computed for every lane, then selected), so that it can sit between the
-// other half's MFMAs.
+// DMA of rows [0, 64) of a [rows][DH] tile by the 8 waves of a block (same
+// placement as dma_tile64).
 template <int DH>
-__device__ __forceinline__ void dkdv_softmax_job(f32x16_t& sp, f32x16_t& dp, const DkdvStats<DH>& stt,
-                                                 int j, int q0, int kcol, int e, int lane, float c2,
-                                                 bool mask) {
-  constexpr int KS = DH / 16, PER = 16 / KS;
+__device__ __forceinline__ void dma_tile64_w8(char* lds, const bf16_t* __restrict__ src, int64_t ld,
+                                              int nvalid, int wave, int lane) {
+  constexpr int ROWB = DH * 2, RPI = 1024 / ROWB, NI = 64 / RPI, CPR = DH / 8;
+  const int rr = lane / CPR, pc = lane % CPR;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e_ = (j % KS) * PER + k;
-    const int q = q0 + (j / KS) * 32 + crow(e_, lane);
-    float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - stt.l[j & 1][k]);
-    float g = p * (dp[e_] - stt.d[j & 1][k]);
-    if (mask) {  // wave-uniform: a scalar branch
-      asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
-      // statistics rows past the chunk are padding (any value): select, do
-      // not multiply, so that they cannot leak in
-      const bool on = kcol <= q && q < e;
-      p = on ? p : 0.f;
-      g = on ? g : 0.f;
-    }
-    sp[e_] = p;
-    dp[e_] = g;
+  for (int i = wave; i < NI; i += 8) {
+    const int r = i * RPI + rr;
+    const int c = pc ^ swz<DH>(r);
+    const int gr = r < nvalid ? r : nvalid - 1;
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + (int64_t)gr * ld + c * 8),
+                                     (SBP_LDS void*)(lds + i * 1024), 16, 0, 0);
   }
 }
 
-// One 64-query tile against the wave's 32 keys, software-pipelined: LDS
-// fragments are read two steps ahead of the MFMAs that use them, and the
-// softmax of one 32-query half is spread over the MFMA steps of the other
-// (job j of half 0 at S/dP step KS + j, job j of half 1 at dV/dK step j),
-// its statistics read one step ahead, before that step's fragment reads, so
-// that waiting for them never drains the fragment prefetch.
-//   steps 0 .. 2KS-1:  S, dP of half 0, then half 1 (+ softmax of half 0)
-//   steps 0 .. 4NB-1:  dV, dK from half 0 (+ softmax of half 1), then half 1
+// One wave's share of a 64-query tile: its 32 queries (tile rows qrow ..
+// qrow + 31) against its 32 keys (K / V tile rows krow .. krow + 31).
 template <int DH>
-__device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* qt, const char* ot, const float* ls,
-                                          const float* dl, int q0, int kcol, int e, int lane, float c2,
-                                          bool mask, const uint4 (&kf)[DH / 16], const uint4 (&vf)[DH / 16],
-                                          f32x16_t (&dk)[DH / 32], f32x16_t (&dv)[DH / 32]) {
+__device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int krow,
+                                          const char* qt, const char* ot, const float* ls,
+                                          const float* dl, int qrow, int q0, int kcol, int e, int lane,
+                                          float c2, bool mask, f32x16_t (&dk)[DH / 32],
+                                          f32x16_t (&dv)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
-  f32x16_t sp[2], dp[2];
-  sp[0] = sp[1] = dp[0] = dp[1] = f32x16_t{};
-  DkdvStats<DH> stt;
-  // S = Q K^T and dP = dO V^T: [64 queries x 32 keys] as two 32-query halves
+  // S = Q K^T and dP = dO V^T: [32 queries x 32 keys], fragments one step ahead
+  f32x16_t sp = f32x16_t{}, dp = f32x16_t{};
   {
-    uint4 fq[3], fo[3];
-    auto ld = [&](int st) {
-      fq[st % 3] = lo.row_frag(qt, (st / KS) * 32, st % KS);
-      fo[st % 3] = lo.row_frag(ot, (st / KS) * 32, st % KS);
+    uint4 fq[2], fk[2], fo[2], fv[2];
+    auto ld = [&](int ks) {
+      fq[ks & 1] = lo.row_frag(qt, qrow, ks);
+      fk[ks & 1] = lo.row_frag(kt, krow, ks);
+      fo[ks & 1] = lo.row_frag(ot, qrow, ks);
+      fv[ks & 1] = lo.row_frag(vt, krow, ks);
     };
     ld(0);
-    ld(1);
 #pragma unroll
-    for (int st = 0; st < 2 * KS; ++st) {
-      if (st >= KS - 1) stt.load(ls, dl, st - KS + 1, lane);  // jobs 0 .. KS
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) ld(ks + 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < 2 * KS) ld(st + 2);
+      sp = mma(fq[ks & 1], fk[ks & 1], sp);
+      dp = mma(fo[ks & 1], fv[ks & 1], dp);
       __builtin_amdgcn_sched_barrier(0);
-      const int qb = st / KS, ks = st % KS;
-      sp[qb] = mma(fq[st % 3], kf[ks], sp[qb]);
-      dp[qb] = mma(fo[st % 3], vf[ks], dp[qb]);
-      if (qb == 1) dkdv_softmax_job<DH>(sp[0], dp[0], stt, ks, q0, kcol, e, lane, c2, mask);
-      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // P = exp(s S - LSE), dS = P (dP - Delta); elements 4j..4j+3 are rows
+  // 8j + 4(l/32) + 0..3 of the wave's 32 queries
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r0 = qrow + 8 * j + 4 * (lane >> 5);
+    const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
+    const float4 d4 = *reinterpret_cast<const float4*>(dl + r0);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e_ = 4 * j + i;
+      float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - lv[i]);
+      float g = p * (dp[e_] - dv_[i]);
+      if (mask) {  // wave-uniform: a scalar branch
+        asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
+        // statistics rows past the chunk are padding (any value): select, do
+        // not multiply, so that they cannot leak in
+        const int q = q0 + r0 + i;
+        const bool on = kcol <= q && q < e;
+        p = on ? p : 0.f;
+        g = on ? g : 0.f;
+      }
+      sp[e_] = p;
+      dp[e_] = g;
     }
   }
   // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
   {
-    uint4 tq[3], to[3];
+    uint4 tq[2], to[2];
     auto ld = [&](int st) {
-      const int r = (st / (2 * NB)) * 32 + ((st / NB) & 1) * 16, nb = st % NB;
-      to[st % 3] = lo.tr_frag(ot, r, nb);
-      tq[st % 3] = lo.tr_frag(qt, r, nb);
+      const int r = qrow + (st / NB) * 16, nb = st % NB;
+      to[st & 1] = lo.tr_frag(ot, r, nb);
+      tq[st & 1] = lo.tr_frag(qt, r, nb);
     };
     ld(0);
-    ld(1);
     uint4 pa, da;
 #pragma unroll
-    for (int st = 0; st < 4 * NB; ++st) {
-      if (st + 1 < KS) stt.load(ls, dl, KS + st + 1, lane);  // jobs KS + 1 .. 2KS - 1
+    for (int st = 0; st < 2 * NB; ++st) {
+      if (st + 1 < 2 * NB) ld(st + 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < 4 * NB) ld(st + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      const int qb = st / (2 * NB), i = (st / NB) & 1, nb = st % NB;
+      const int i = st / NB, nb = st % NB;
       if (nb == 0) {
-        pa = pack_frag(sp[qb], i);
-        da = pack_frag(dp[qb], i);
+        pa = pack_frag(sp, i);
+        da = pack_frag(dp, i);
       }
-      dv[nb] = mma(pa, to[st % 3], dv[nb]);
-      dk[nb] = mma(da, tq[st % 3], dk[nb]);
-      if (st < KS) dkdv_softmax_job<DH>(sp[1], dp[1], stt, KS + st, q0, kcol, e, lane, c2, mask);
+      dv[nb] = mma(pa, to[st & 1], dv[nb]);
+      dk[nb] = mma(da, tq[st & 1], dk[nb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
-  constexpr int NB = DH / 32, KS = DH / 16;
-  __shared__ __attribute__((aligned(16))) char Q0[64 * DH * 2];
-  __shared__ __attribute__((aligned(16))) char O0[64 * DH * 2];  // dO tile
-  __shared__ __attribute__((aligned(16))) char Q1[64 * DH * 2];
-  __shared__ __attribute__((aligned(16))) char O1[64 * DH * 2];
+__global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
+  constexpr int NB = DH / 32, TB = 64 * DH * 2;
+  __shared__ __attribute__((aligned(16))) char Kt[2 * TB];  // 128 keys
+  __shared__ __attribute__((aligned(16))) char Vt[2 * TB];
+  __shared__ __attribute__((aligned(16))) char Q0[TB];
+  __shared__ __attribute__((aligned(16))) char O0[TB];  // dO tile
+  __shared__ __attribute__((aligned(16))) char Q1[TB];
+  __shared__ __attribute__((aligned(16))) char O1[TB];
   __shared__ __attribute__((aligned(16))) float L0[64], E0[64], L1[64], E1[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, qh = wave >> 2;
   const KBlock kbk = k_block(a.Hkv);
   const int kv = kbk.kv, b = blockIdx.z;
   const LdsOff<DH> lo(lane);
   const int kbase = kbk.kblk * 128;
-  const int kw = kbase + wave * 32;
+  const int kw = kbase + kg * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
+  const int qrow = qh * 32;           // the wave's rows of each query tile
   const int64_t ldq = a.ldq, ldk = (int64_t)a.Hkv * DH;
-  const bf16_t* Kb = a.K + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
-  const bf16_t* Vb = a.V + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
-  // K, V of this wave's keys as B operands (column = key, k = dh)
-  uint4 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = glb_frag<DH>(Kb, ldk, kcol, a.T, ks, lane >> 5);
-    vf[ks] = glb_frag<DH>(Vb, ldk, kcol, a.T, ks, lane >> 5);
-  }
+  const bf16_t* Kb = a.K + ((int64_t)b * a.T + kbase) * ldk + (int64_t)kv * DH;
+  const bf16_t* Vb = a.V + ((int64_t)b * a.T + kbase) * ldk + (int64_t)kv * DH;
   f32x16_t dk[NB], dv[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -526,40 +513,67 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   const int j0 = kbase > a.s ? (kbase - a.s) / 64 : 0;
   const int nqt = (a.e - a.s + 63) / 64 - j0;
   const int n = nqt > 0 ? nqt * a.G : 0;
+  // K, V of the block's keys (rows past T fetch row T - 1; those keys are
+  // masked and never written)
+  const int kvalid = a.T - kbase;
+  dma_tile64_w8<DH>(Kt, Kb, ldk, kvalid, wave, lane);
+  dma_tile64_w8<DH>(Kt + TB, Kb + 64 * ldk, ldk, kvalid - 64, wave, lane);
+  dma_tile64_w8<DH>(Vt, Vb, ldk, kvalid, wave, lane);
+  dma_tile64_w8<DH>(Vt + TB, Vb + 64 * ldk, ldk, kvalid - 64, wave, lane);
+  // each wave: 2 x (64 rows of Q and dO) / 8 waves, plus one quarter row of
+  // LSE (waves 0-3) or Delta (waves 4-7)
   auto issue = [&](char* qd, char* od, float* ld_, float* dd, int it) {
     const int hh = it / nqt;
     const int q0 = a.s + (j0 + it % nqt) * 64;
     const int h = kv * a.G + hh;
     const int64_t qo = (int64_t)b * a.q_bs + (int64_t)(q0 - a.qoff) * ldq + (int64_t)h * DH;
-    dma_tile64<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
-    dma_tile64<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
-    if (wave == 0)
-      dma_f32x64(ld_, a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (q0 - a.s), lane);
-    else if (wave == 1)
-      dma_f32x64(dd, a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (q0 - a.s), lane);
+    dma_tile64_w8<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
+    dma_tile64_w8<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
+    if (wave < 4)
+      dma_f32x16(ld_, a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (q0 - a.s), wave, lane);
+    else
+      dma_f32x16(dd, a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (q0 - a.s), wave - 4, lane);
   };
   auto qstart = [&](int it) { return a.s + (j0 + it % nqt) * 64; };
+  auto tile = [&](const char* qt, const char* ot, const float* ls, const float* dl, int it) {
+    const int q0 = qstart(it), qw = q0 + qrow;
+    // only the wave's queries at or after its keys; those wholly after them
+    // and inside the chunk need no mask
+    if (qw + 31 >= kw)
+      dkdv_tile<DH>(lo, Kt, Vt, kg * 32, qt, ot, ls, dl, qrow, q0, kcol, a.e, lane, c2,
+                    !(qw >= kw + 31 && qw + 32 <= a.e), dk, dv);
+  };
   if (n > 0) issue(Q0, O0, L0, E0, 0);
   for (int it = 0; it < n; it += 2) {
-    dma_barrier();  // tile it landed; everyone is done with the other buffers
+    dma_barrier();  // tile it (and K, V) landed; everyone is done with the other buffers
     issue(Q1, O1, L1, E1, min(it + 1, n - 1));
-    {
-      const int q0 = qstart(it);
-      // tiles wholly after the wave's keys and inside the chunk need no mask
-      if (q0 + 63 >= kw)
-        dkdv_tile<DH>(lo, Q0, O0, L0, E0, q0, kcol, a.e, lane, c2, !(q0 >= kw + 31 && q0 + 64 <= a.e),
-                      kf, vf, dk, dv);
-    }
+    tile(Q0, O0, L0, E0, it);
     dma_barrier();
     issue(Q0, O0, L0, E0, min(it + 2, n - 1));
-    if (it + 1 < n) {
-      const int q0 = qstart(it + 1);
-      if (q0 + 63 >= kw)
-        dkdv_tile<DH>(lo, Q1, O1, L1, E1, q0, kcol, a.e, lane, c2, !(q0 >= kw + 31 && q0 + 64 <= a.e),
-                      kf, vf, dk, dv);
-    }
+    if (it + 1 < n) tile(Q1, O1, L1, E1, it + 1);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS
+  __syncthreads();                // every wave is done with K, V
+  // query half 1 hands its partials to query half 0 through the K / V
+  // arrays (one NB x 16 x 64 fp32 block per key group, in register order)
+  float* red = reinterpret_cast<float*>((kg < 2 ? Kt : Vt) + (kg & 1) * TB);
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    f32x16_t (&acc)[NB] = round == 0 ? dk : dv;
+    if (qh == 1)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e_ = 0; e_ < 16; ++e_) red[(nb * 16 + e_) * 64 + lane] = acc[nb][e_];
+    __syncthreads();
+    if (qh == 0)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e_ = 0; e_ < 16; ++e_) acc[nb][e_] += red[(nb * 16 + e_) * 64 + lane];
+    __syncthreads();
+  }
+  if (qh != 0) return;
   // result blocks [32 keys x 32 dh]: lane = dh column, rows = keys
   float* dKb = a.dK + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
   float* dVb = a.dV + ((int64_t)b * a.T) * ldk + (int64_t)kv * DH;
@@ -569,20 +583,20 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(AttnArgs a) {
   for (int nb = 0; nb < NB; ++nb) {
     float ok[16], ov[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kw + crow(e, lane);
+    for (int e_ = 0; e_ < 16; ++e_) {
+      const int key = kw + crow(e_, lane);
       const int64_t off = (int64_t)key * ldk + nb * 32 + (lane & 31);
       const bool in = a.beta && key < a.T;
-      ok[e] = in ? dKb[off] : 0.f;
-      ov[e] = in ? dVb[off] : 0.f;
+      ok[e_] = in ? dKb[off] : 0.f;
+      ov[e_] = in ? dVb[off] : 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kw + crow(e, lane);
+    for (int e_ = 0; e_ < 16; ++e_) {
+      const int key = kw + crow(e_, lane);
       if (key >= a.T) continue;
       const int64_t off = (int64_t)key * ldk + nb * 32 + (lane & 31);
-      dKb[off] = ok[e] + a.scale * dk[nb][e];
-      dVb[off] = ov[e] + dv[nb][e];
+      dKb[off] = ok[e_] + a.scale * dk[nb][e_];
+      dVb[off] = ov[e_] + dv[nb][e_];
     }
   }
 }
@@ -734,9 +748,9 @@ sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st) {
     dim3 grid((unsigned)cdiv(a.e, 128), (unsigned)a.Hkv, (unsigned)B);
     ProfScope prof("attn_dkdv", st, 8.0 * dh * pairs, 0.0);
     if (dh == 128)
-      hipLaunchKernelGGL(attn_dkdv_kernel<128>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attn_dkdv_kernel<128>, grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL(attn_dkdv_kernel<64>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attn_dkdv_kernel<64>, grid, dim3(512), 0, st, a);
     SBP_LAUNCH_CHECK();
   }
   {

@@ -86,6 +86,24 @@ def test_weighted_masked_packed_skips_chunks():
     _check(inp, 32, "bf16")
 
 
+def test_weight_gradient_groups_first_group_inactive():
+    # T_c = 1024 makes the weight gradient one GEMM per 4 chunks (4 groups);
+    # every token of the first group is ignored, so the second group's GEMM
+    # must overwrite the stale dW passed in, and the groups after it add;
+    # one chunk inside the third group is ignored as well (zero slot).
+    inp = synthetic.lmhead_inputs(16384, 64, 512, "bf16", seed=11, w_std=0.02)
+    inp.targets[:4096] = -1
+    inp.targets[9216:10240] = -1
+    L, rH, rW, _, _ = oracle.lmhead_ce(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                       inp.targets.numpy())
+    dW0 = torch.full((512, 64), 7.0, device="cuda:0")
+    loss, dH, dW, _ = _run(inp, 16, dW=dW0)
+    assert abs(loss.item() - L) / abs(L) <= TOL["bf16"]
+    assert normwise(dH.float().cpu().numpy(), rH) <= TOL["bf16"]
+    assert normwise(dW.cpu().numpy(), rW) <= TOL["bf16"]
+    assert (dH[:4096] == 0).all()
+
+
 def test_sum_reduction():
     inp = synthetic.lmhead_inputs(400, 64, 900, "f32", seed=9, weighted=True, ignore_frac=0.2)
     _check(inp, 5, "f32", reduction="sum")
