@@ -12,6 +12,8 @@
 //               group's dW GEMM overwrites instead of adding.
 //   ce_stats    one block per row: online max / sum-exp over the fp32 logits
 //               row (wave64 shuffles, then LDS across waves) -> lse, l_t.
+//   ce_merge    the same from the (max, sum-exp) partials that the bf16
+//               logits GEMM writes per 64 columns (no pass over the row).
 //   ce_grad     64 x 128 tiles: dZ = (c_t/N)(exp(z - lse) - onehot), written
 //               twice in the GEMM operand layouts -- dZ [T_c, V] (K = V
 //               contiguous for dH = dZ W) and dZ^T [V, T_c] (K = T_c
@@ -163,6 +165,66 @@ sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const f
   ProfScope prof("ce_stats", st, 0.0, 4.0 * (double)Tc * V);
   hipLaunchKernelGGL(ce_stats_kernel, dim3((unsigned)Tc), dim3(256), 0, st, Z, ldz, targets,
                      weights, s, V, lse, loss_part, token_loss);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+// Same outputs as ce_stats, from the logits GEMM's per-64-column (max,
+// sum-exp) partials instead of a pass over the fp32 logits row.
+__global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict__ parts, int64_t ldp,
+                                                       int nparts, const float* __restrict__ Z,
+                                                       int64_t ldz, const int32_t* __restrict__ targets,
+                                                       const float* __restrict__ weights, int64_t s0,
+                                                       float* __restrict__ lse_out,
+                                                       float* __restrict__ loss_part,
+                                                       float* __restrict__ token_loss) {
+  __shared__ float sm[4], ss[4];
+  const int r = blockIdx.x;
+  const int64_t t = s0 + r;
+  const int tid = threadIdx.x;
+  const int y = targets[t];
+  if (y < 0) {
+    if (tid == 0) {
+      loss_part[t] = 0.f;
+      if (token_loss) token_loss[t] = 0.f;
+      lse_out[r] = 0.f;
+    }
+    return;
+  }
+  float m = -INFINITY, sx = 0.f;
+  for (int i = tid; i < nparts; i += 256) {
+    const float2 q = parts[(int64_t)r * ldp + i];
+    lse_merge(m, sx, q.x, q.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(sx, o, 64);
+    lse_merge(m, sx, m2, s2);
+  }
+  if ((tid & 63) == 0) {
+    sm[tid >> 6] = m;
+    ss[tid >> 6] = sx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = sm[0], S = ss[0];
+    for (int w = 1; w < 4; ++w) lse_merge(M, S, sm[w], ss[w]);
+    const float lse = M + __logf(S);
+    const float ell = lse - Z[(int64_t)r * ldz + y];
+    const float w = weights ? weights[t] : 1.f;
+    lse_out[r] = lse;
+    loss_part[t] = w * ell;
+    if (token_loss) token_loss[t] = ell;
+  }
+}
+
+sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z, int64_t ldz,
+                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
+                    float* loss_part, float* token_loss, hipStream_t st) {
+  ProfScope prof("ce_merge", st, 0.0, 8.0 * (double)Tc * nparts);
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts, Z, ldz,
+                     targets, weights, s, lse, loss_part, token_loss);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

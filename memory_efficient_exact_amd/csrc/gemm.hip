@@ -635,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         if (row >= p.M || col >= p.N) continue;
         const int64_t off = (int64_t)row * p.ldc + col;
         if (vec_ok && col + 4 <= p.N) {
-          if constexpr (EPI == EPI_F32) {
+          if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
           } else if constexpr (EPI == EPI_PARTIAL) {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (col + j >= p.N) break;
-            if constexpr (EPI == EPI_F32) {
+            if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
               reinterpret_cast<float*>(p.C)[off + j] = v[j];
             } else if constexpr (EPI == EPI_PARTIAL) {
               reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
@@ -674,6 +674,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         }
       }
     }
+    if constexpr (EPI == EPI_F32_LSE) {
+      // (max, sum-exp) of each row's 64-column quarters of the wave's block,
+      // one lane per (row l % 32, quarter l / 32), read from the staged block
+      // in a lane-rotated order (conflict-free); no cross-lane traffic.
+      const int lr = lane & 31, hq = lane >> 5;
+      const int row = m0 + wm * WT + fm * 32 + lr;
+      const int cbase = n0 + wn * WT + hq * 64;
+      const float* Wr = &W[lr * 128 + hq * 64];
+      // one pass, online: the running sum is rescaled when a float4 raises
+      // the running max
+      float m = -INFINITY, sx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c4 = (j + lane) & 15;
+        const float4 q = *reinterpret_cast<const float4*>(Wr + c4 * 4);
+        const int c = cbase + c4 * 4;
+        const float x0 = c + 0 < p.N ? q.x : -INFINITY, x1 = c + 1 < p.N ? q.y : -INFINITY;
+        const float x2 = c + 2 < p.N ? q.z : -INFINITY, x3 = c + 3 < p.N ? q.w : -INFINITY;
+        const float m4 = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+        if (m4 > m) {
+          sx = (m == -INFINITY) ? 0.f : sx * __expf(m - m4);
+          m = m4;
+        }
+        if (m != -INFINITY) sx += __expf(x0 - m) + __expf(x1 - m) + __expf(x2 - m) + __expf(x3 - m);
+      }
+      if (row < p.M) p.row_stats[(int64_t)row * p.ld_stats + 4 * tn + 2 * wn + hq] = make_float2(m, sx);
+    }
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -684,6 +711,7 @@ static void launch_bf16_ring(int epi, GemmParams p, hipStream_t st) {
   const int grid = p.tiles_m * p.tiles_n * p.k_split;
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32>, dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_F32_LSE: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32_LSE>, dim3(grid), dim3(256), 0, st, p); break;
     case EPI_F32_ACC: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32_ACC>, dim3(grid), dim3(256), 0, st, p); break;
     case EPI_OUT: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT>, dim3(grid), dim3(256), 0, st, p); break;
     case EPI_OUT_RESID: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT_RESID>, dim3(grid), dim3(256), 0, st, p); break;
@@ -729,10 +757,14 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
   const double bytes = ((double)p.M * p.K + (double)p.N * p.K) * esz +
                        (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : 4.0 * p.k_split);
+  // (the row statistics of EPI_F32_LSE add 8 bytes per 128 output columns)
   ProfScope prof(name, st, flops, bytes);
+  const bool ring_ok = dtype == SBP_BF16 && p.K % 128 == 0 && p.k_per_split % 128 == 0 &&
+                       p.lda % 8 == 0 && p.ldb % 8 == 0;
+  if (epi == EPI_F32_LSE && !(tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 && p.row_stats))
+    return set_error(SBP_ERR_UNSUPPORTED, "row-statistics epilogue needs the bf16 ring GEMM without split-K");
   if (dtype == SBP_BF16) {
-    if (tile == GEMM_TILE_RING && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
-        p.ldb % 8 == 0)
+    if (tile == GEMM_TILE_RING && ring_ok)
       launch_bf16_ring(epi, p, st);
     else if (tile == GEMM_TILE_256 && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
         p.ldb % 8 == 0)

@@ -6,7 +6,9 @@
 namespace sbp {
 
 // ---------------------------------------------------------------- GEMM ----
-enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4 };
+// EPI_F32_LSE: as EPI_F32, plus the (max, sum-exp) of every 64-column quarter
+// of a tile row (columns < N) into row_stats (ring kernel only, k_split 1).
+enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_F32_LSE = 5 };
 enum { GEMM_TILE_128 = 0, GEMM_TILE_256 = 1, GEMM_TILE_256_REG = 2, GEMM_TILE_RING = 3 };
 
 struct GemmParams {
@@ -24,6 +26,8 @@ struct GemmParams {
   int k_per_split = 0;             // multiple of the K step (0 = even split)
   int64_t split_stride = 0;        // EPI_PARTIAL: elements between partial outputs
   int m_fastest = 1;               // tile order inside an XCD's range (register-staged kernel only)
+  float2* row_stats = nullptr;     // EPI_F32_LSE: [M, ld_stats], entry 4 tn + quarter
+  int64_t ld_stats = 0;
   int tiles_m = 0, tiles_n = 0;    // filled by the launcher
 };
 
@@ -42,6 +46,11 @@ struct LmPrep {   // device-side scalars written by lm_prep
 sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int reduction,
                    int accumulate, const LmPrep& pr, hipStream_t st);
 // Per-row log-sum-exp and per-token loss for rows [s, s+Tc) of one chunk.
+// Row statistics from the logits GEMM's per-64-column partials (nparts per
+// row, pitch ldp): lse, l_t = lse - z_t[y_t] (z read from Z), c_t l_t.
+sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z, int64_t ldz,
+                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
+                    float* loss_part, float* token_loss, hipStream_t st);
 sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
                     int64_t s, int64_t Tc, int64_t V, float* lse, float* loss_part,
                     float* token_loss, hipStream_t st);

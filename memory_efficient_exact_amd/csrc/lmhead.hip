@@ -3,8 +3,10 @@
 // Per chunk c = [s, e) (skill page "Implementation": the sequence
 // decomposition, the logits-gradient routine and the linear-layer chunk
 // gradient), with every GEMM in the NT form of gemm.hip:
-//   Z_c   = H_c W^T                fp32 [T_c, V]          (gemm, EPI_F32)
-//   lse, l_t, c_t l_t              per row                 (ce_stats)
+//   Z_c   = H_c W^T                fp32 [T_c, V]          (gemm, EPI_F32_LSE: with
+//                                  per-64-column row (max, sum-exp) partials)
+//   lse, l_t, c_t l_t              per row                 (ce_merge of the partials;
+//                                  ce_stats over Z where the GEMM cannot: fp32, d % 128)
 //   dZ_c, dZ_c^T                   dtype, zero-padded      (ce_grad)
 //   H_c^T                          dtype [d, T_c]          (transpose_pad)
 //   dH_c  = dZ_c W = dZ_c (W^T)^T  split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
@@ -29,6 +31,7 @@ struct LmWs {
   float* part;
   float* lse;
   float* loss_part;
+  float2* parts;  // [T_c, nparts] row (max, sum-exp) partials of the logits GEMM
   LmPrep prep;
 };
 
@@ -38,6 +41,8 @@ struct LmShape {
   int dtype;
   int64_t Tcm, Tcp, Vp;
   int S;  // split count of the dH GEMM
+  bool fused_stats;  // the logits GEMM writes the row statistics partials
+  int nparts;
   int G;  // chunks per dW GEMM
   int64_t Kg;  // K extent of the dW group buffers: G * Tcp
   size_t esz;
@@ -62,6 +67,8 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   // flop or less); a function of the shape only.
   s.G = (int)std::max<int64_t>(1, std::min<int64_t>(D, 4096 / s.Tcp));
   s.Kg = s.G * s.Tcp;
+  s.fused_stats = dtype == SBP_BF16 && d % 128 == 0;
+  s.nparts = (int)(4 * cdiv(V, 256));
   return s;
 }
 
@@ -77,6 +84,7 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   x.part = (float*)P.take(sizeof(float) * (size_t)s.S * s.Tcm * s.d);
   x.lse = (float*)P.take(sizeof(float) * s.Tcm);
   x.loss_part = (float*)P.take(sizeof(float) * s.T);
+  x.parts = s.fused_stats ? (float2*)P.take(sizeof(float2) * s.Tcm * s.nparts) : nullptr;
   x.prep.n_valid = (int*)P.take(sizeof(int));
   x.prep.inv_norm = (float*)P.take(sizeof(float));
   x.prep.none_active = (int*)P.take(sizeof(int));
@@ -167,9 +175,16 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
     g1.M = (int)Tc; g1.N = (int)V; g1.K = (int)d;
     g1.active = act;
     g1.m_fastest = 1;
-    SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
-
-    SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
+    if (s.fused_stats) {
+      g1.row_stats = w.parts;
+      g1.ld_stats = s.nparts;
+      SBP_TRY(gemm_nt(dtype, EPI_F32_LSE, g1, GEMM_TILE_RING, str, "gemm_logits"));
+      SBP_TRY(ce_merge(w.parts, s.nparts, s.nparts, w.Z, s.Vp, targets, weights, s0, Tc, w.lse,
+                       w.loss_part, token_loss, str));
+    } else {
+      SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
+      SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
+    }
     SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
                     w.dZ, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp, slot_act, str));
     SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, (char*)w.Ht + j * s.Tcp * s.esz, s.Kg,
