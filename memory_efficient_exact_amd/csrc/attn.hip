@@ -222,22 +222,30 @@ __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, c
       mt = fmaxf(mt, v);
     }
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float mn = fmaxf(m, mt);
-  const float alpha = __builtin_amdgcn_exp2f(m - mn);
+  // Lazy rescale: the running max m only moves (and O, l are rescaled) when
+  // some lane's tile max exceeds it by more than 8 (base 2); otherwise P is
+  // taken against the stale m and stays <= 2^8 (exact in the fp32 sums, the
+  // same relative precision in bf16).  LSE = m + log2 l either way.
+  const bool raise = __ballot(mt > m + 8.f) != 0;
   float ls = 0.f;
+  if (raise) {  // wave-uniform
+    const float mn = fmaxf(m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) ot[i] *= alpha;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(st[kb][e] - mn);
+      const float p = __builtin_amdgcn_exp2f(st[kb][e] - m);
       st[kb][e] = p;
       ls += p;
     }
   ls += __shfl_xor(ls, 32, 64);
-  l = l * alpha + ls;
-  m = mn;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) ot[i] *= alpha;
+  l += ls;
   // O^T[dh, q] += V^T[dh, key] P^T[key, q]
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
