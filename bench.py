@@ -278,6 +278,14 @@ def main():
     tokens = T * cfg.get("B", 1)
     value = tokens / (ms / 1e3)
 
+    # The library's timer counts each launch's flops as issued; the LM head's
+    # GEMMs of fully masked chunks (groups) are launched but return at once,
+    # so there each GEMM kind is credited a third of the step's algorithmic
+    # flops (the three chunk GEMMs have the same 2 N V d each).
+    if cfg["kind"] == "lmhead":
+        for kname in ("gemm_logits", "gemm_dH", "gemm_dW"):
+            if kname in prof:
+                prof[kname] = dict(prof[kname], flops=flops * args.steps / 3.0)
     # dominant kernel and its roofline (live hipEvent timing inside the call)
     dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
     name, k = dom
