@@ -4,22 +4,23 @@
 // operands K-contiguous), so one kernel serves them all:
 //   logits      Z_c   = H_c  . W^T      A = H_c  [T_c, d],  B = W   [V, d]
 //   input grad  dH_c  = dZ_c . W        A = dZ_c [T_c, V],  B = W^T [d, V]
-//   weight grad dW   += dZ_c^T . H_c    A = dZ_c^T [V, T_c], B = H_c^T [d, T_c]
+//   weight grad dW   += dZ_g^T . H_g    A = dZ_g^T [V, K_g], B = H_g^T [d, K_g]
 // (the transposed operands are written by the producing kernels or by a
-// transpose kernel; see transpose.hip / ce.hip).
+// transpose kernel; see misc.hip / ce.hip).
 //
-// Tiling: a 256-thread block (4 waves of 64) owns a BM x BN output tile and
-// walks K in steps of 128 bytes per row (64 bf16 or 32 fp32).  Global loads
-// are 16-byte vectors staged through registers into a double-buffered LDS
-// tile; LDS rows are 8 x 16-byte chunks with chunk c of row r stored at
-// c ^ (r & 7) so the fragment reads of 8 consecutive rows hit distinct banks.
-// Each wave computes a (BM/WGM) x (BN/WGN) sub-tile from 16x16 MFMA blocks:
-// bf16 uses v_mfma_f32_16x16x32_bf16 (one 16-byte fragment per lane per
-// instruction), fp32 uses v_mfma_f32_16x16x4_f32 four times per fragment.
-// The lane that holds k-chunk g of an A row also holds k-chunk g of the B
-// column, so the k order inside an instruction never matters.
-// Output layout of a 16x16 block: lane l, element i -> row 4*(l/16)+i,
-// column l%16.
+// Two kernels:
+//  * gemm_nt_bf16_ring_kernel (bf16, K a multiple of 128, the default): a
+//    256 x 256 tile, 4 waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16
+//    blocks, operands fed global -> LDS by DMA through two 64 KB stages (its
+//    section below has the details);
+//  * gemm_nt_kernel (fp32, and bf16 with other K): a 128 x 128 tile, 4 waves
+//    of 64 x 64 as 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, or
+//    v_mfma_f32_16x16x4_f32 four times per fragment), 16-byte global loads
+//    staged through registers into a double-buffered LDS tile whose rows are
+//    8 x 16-byte chunks, chunk c of row r at c ^ (r & 7).  The lane that
+//    holds k-chunk g of an A row also holds k-chunk g of the B column, so the
+//    k order inside an instruction never matters.  Output layout of a 16x16
+//    block: lane l, element i -> row 4*(l/16)+i, column l%16.
 //
 // Block -> tile mapping is XCD-aware: consecutive block ids go round-robin
 // to the 8 XCDs, so block b is given the (b/8)-th tile of a contiguous range
@@ -192,16 +193,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// 256 x 256 bf16 variant for K % 64 == 0: operands go global -> LDS directly
-// (global_load_lds_dwordx4, no register staging), so the 64 KB of the next K
-// step is in flight while the 4 waves (each a 128 x 128 sub-tile, 256 fp32
-// accumulators per lane) run 128 MFMAs on the current one.  Waves 0-1 fetch
-// the A panel, waves 2-3 the B panel; one instruction fills 8 LDS rows (1 KB),
-// lane i writing slot i, so the XOR swizzle is applied to the global address
-// (lane i fetches logical chunk (i%8) ^ (i/8) of its row).  Rows past M or N
-// are clamped to the last valid row; they only feed outputs that are masked.
-// ---------------------------------------------------------------------------
 #define SBP_AS1 __attribute__((address_space(1)))
 #define SBP_AS3 __attribute__((address_space(3)))
 
@@ -227,184 +218,6 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// One 64-wide K step of a wave's 128 x 128 sub-tile from LDS tile L, as
-// 4 k16 steps of 4 x 4 v_mfma_f32_32x32x16_bf16 (A fragment: lane l holds row
-// l%32, 16-byte chunk l/32 of the k16 step; B likewise by column).  Fragments
-// are double-buffered in registers: step ks+1 is read while step ks runs.
-__device__ __forceinline__ void mma_tile_256(const uint4* __restrict__ L, int wm, int wn, int lane,
-                                             f32x16_t (&acc)[4][4]) {
-  constexpr int BM = 256, WT = 128;
-  uint4 af[2][4], bfr[2][4];
-  auto load = [&](int ks, int buf) {
-    const int ch = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int r = wm * WT + f * 32 + (lane & 31);
-      af[buf][f] = L[r * 8 + (ch ^ (r & 7))];
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int r = BM + wn * WT + f * 32 + (lane & 31);
-      bfr[buf][f] = L[r * 8 + (ch ^ (r & 7))];
-    }
-  };
-  load(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) load(ks + 1, (ks + 1) & 1);
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, af[ks & 1][fm]), __builtin_bit_cast(bf16x8_t, bfr[ks & 1][fn]),
-            acc[fm][fn], 0, 0, 0);
-  }
-}
-
-// Two distinct LDS arrays (not one array indexed by stage) so that the
-// compiler can tell the DMA into one from the fragment reads of the other and
-// does not wait for the prefetch before computing.
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_nt_bf16_256_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, BK = 64, WT = 128;
-  __shared__ uint4 lds0[(BM + BN) * 8];
-  __shared__ uint4 lds1[(BM + BN) * 8];
-  if (p.active && *p.active == 0) return;
-  int tm, tn, split;
-  tile_coords(p, tm, tn, split);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int kb = split * p.k_per_split;
-  const int ke = min(p.K, kb + p.k_per_split);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // DMA role of this wave: waves 0-1 fetch A rows, waves 2-3 B rows
-  const int opnd = wave >> 1;
-  const int rbase = (wave & 1) * 128;
-  const int sub_r = lane >> 3;
-  const int chunk = (lane & 7) ^ sub_r;
-  const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
-  const int64_t ld = opnd ? p.ldb : p.lda;
-  const int lim = opnd ? p.N : p.M;
-  const int r0 = (opnd ? n0 : m0) + rbase + sub_r;
-  const int lds_row0 = opnd * BM + rbase;
-
-  auto issue = [&](uint4* L, int k0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      int gr = r0 + j * 8;
-      gr = gr < lim ? gr : lim - 1;
-      const bf16_t* g = X + (int64_t)gr * ld + k0 + chunk * 8;
-      __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
-                                       (SBP_AS3 void*)&L[(lds_row0 + j * 8) * 8], 16, 0, 0);
-    }
-  };
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
-
-  const int nk = ke > kb ? (ke - kb) / BK : 0;
-  if (nk > 0) issue(lds0, kb);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // every K range is a multiple of 2 * BK (checked by the launcher)
-  const int npair = nk >> 1;
-  for (int pr = 0; pr < npair; ++pr) {
-    const int it = 2 * pr;
-    issue(lds1, kb + (it + 1) * BK);
-    mma_tile_256(lds0, wm, wn, lane, acc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (it + 2 < nk) issue(lds0, kb + (it + 2) * BK);
-    mma_tile_256(lds1, wm, wn, lane, acc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  // Epilogue through LDS: each wave parks 64 rows x 128 columns of fp32
-  // accumulators (32 KB; waves 0-1 in lds0, 2-3 in lds1), then writes them
-  // back as row-contiguous 4-wide vectors.  32x32 MFMA output: lane l,
-  // element e -> row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  __syncthreads();
-  float* W = reinterpret_cast<float*>(wave < 2 ? lds0 : lds1) + (wave & 1) * (64 * 128);
-  float beta = (float)p.beta;
-  if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
-  const bool vec_ok = (p.ldc % 4 == 0) && (EPI != EPI_OUT_RESID || p.ldr % 4 == 0);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int fmi = 0; fmi < 2; ++fmi)
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int lr = fmi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          W[lr * 128 + fn * 32 + (lane & 31)] = acc[2 * half + fmi][fn][e];
-        }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int lr = it * 2 + (lane >> 5);
-      const int lc = (lane & 31) * 4;
-      const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + lc]);
-      float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
-      const int row = m0 + wm * WT + half * 64 + lr;
-      const int col = n0 + wn * WT + lc;
-      if (row >= p.M || col >= p.N) continue;
-      const int64_t off = (int64_t)row * p.ldc + col;
-      if (vec_ok && col + 4 <= p.N) {
-        if constexpr (EPI == EPI_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_PARTIAL) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_F32_ACC) {
-          float4* c = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off);
-          if (beta != 0.f) {
-            const float4 o = *c;
-            *c = make_float4(v[0] + beta * o.x, v[1] + beta * o.y, v[2] + beta * o.z, v[3] + beta * o.w);
-          } else {
-            *c = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        } else {
-          if constexpr (EPI == EPI_OUT_RESID) {
-            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.R) + (int64_t)row * p.ldr + col);
-            v[0] += bf2f((bf16_t)(r.x & 0xffff)); v[1] += bf2f((bf16_t)(r.x >> 16));
-            v[2] += bf2f((bf16_t)(r.y & 0xffff)); v[3] += bf2f((bf16_t)(r.y >> 16));
-          }
-          uint2 u;
-          u.x = pk_bf16(v[0], v[1]);
-          u.y = pk_bf16(v[2], v[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (col + j >= p.N) break;
-          if constexpr (EPI == EPI_F32) {
-            reinterpret_cast<float*>(p.C)[off + j] = v[j];
-          } else if constexpr (EPI == EPI_PARTIAL) {
-            reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
-          } else if constexpr (EPI == EPI_F32_ACC) {
-            float* c = reinterpret_cast<float*>(p.C) + off + j;
-            *c = (beta != 0.f) ? (v[j] + beta * *c) : v[j];
-          } else if constexpr (EPI == EPI_OUT) {
-            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j]);
-          } else {
-            const float r = Elem<bf16_t>::load(reinterpret_cast<const bf16_t*>(p.R), (int64_t)row * p.ldr + col + j);
-            Elem<bf16_t>::store(reinterpret_cast<bf16_t*>(p.C), off + j, v[j] + r);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Pipelined variant (the default for bf16): the same 256 x 256 tile and
@@ -719,19 +532,6 @@ static void launch_bf16_ring(int epi, GemmParams p, hipStream_t st) {
   }
 }
 
-static void launch_bf16_256(int epi, GemmParams p, hipStream_t st) {
-  p.tiles_m = (int)cdiv(p.M, 256);
-  p.tiles_n = (int)cdiv(p.N, 256);
-  const int grid = p.tiles_m * p.tiles_n * p.k_split;
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(gemm_nt_bf16_256_kernel<EPI_F32>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_F32_ACC: hipLaunchKernelGGL(gemm_nt_bf16_256_kernel<EPI_F32_ACC>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_OUT: hipLaunchKernelGGL(gemm_nt_bf16_256_kernel<EPI_OUT>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_OUT_RESID: hipLaunchKernelGGL(gemm_nt_bf16_256_kernel<EPI_OUT_RESID>, dim3(grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL(gemm_nt_bf16_256_kernel<EPI_PARTIAL>, dim3(grid), dim3(256), 0, st, p); break;
-  }
-}
-
 template <typename T, int BM, int BN, int WGM, int WGN>
 static void launch_cfg(int epi, GemmParams p, hipStream_t st) {
   p.tiles_m = (int)cdiv(p.M, BM);
@@ -766,11 +566,6 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
   if (dtype == SBP_BF16) {
     if (tile == GEMM_TILE_RING && ring_ok)
       launch_bf16_ring(epi, p, st);
-    else if (tile == GEMM_TILE_256 && p.K % 128 == 0 && p.k_per_split % 128 == 0 && p.lda % 8 == 0 &&
-        p.ldb % 8 == 0)
-      launch_bf16_256(epi, p, st);
-    else if (tile == GEMM_TILE_256_REG)
-      launch_cfg<bf16_t, 256, 256, 2, 2>(epi, p, st);
     else
       launch_cfg<bf16_t, 128, 128, 2, 2>(epi, p, st);
   } else {

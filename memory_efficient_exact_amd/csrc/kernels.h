@@ -9,7 +9,7 @@ namespace sbp {
 // EPI_F32_LSE: as EPI_F32, plus the (max, sum-exp) of every 64-column quarter
 // of a tile row (columns < N) into row_stats (ring kernel only, k_split 1).
 enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_F32_LSE = 5 };
-enum { GEMM_TILE_128 = 0, GEMM_TILE_256 = 1, GEMM_TILE_256_REG = 2, GEMM_TILE_RING = 3 };
+enum { GEMM_TILE_128 = 0, GEMM_TILE_RING = 3 };
 
 struct GemmParams {
   const void* A = nullptr;  // [M, K] row-major, K contiguous, pitch lda elements
