@@ -27,12 +27,57 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict_
   }
 }
 
+// bf16 with 16-byte rows on both sides (C, pitches and bases multiples of 8
+// elements, Rp a multiple of 8): each thread moves 8 elements per access.
+// The 64 x 64 tile sits in LDS with a row pitch of 66 elements, so the 8
+// strided reads of a column segment fall in distinct banks.
+__global__ __launch_bounds__(256) void transpose_pad_bf16x8_kernel(
+    const bf16_t* __restrict__ src, int64_t lds_, int64_t R, int64_t C, bf16_t* __restrict__ dst,
+    int64_t ldd, int64_t Rp, const int* __restrict__ active) {
+  if (active && *active == 0) return;
+  __shared__ uint16_t tile[64][66];
+  const int t = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  // load: 8 threads per row (8 columns each), 32 rows per pass
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + (t >> 3), cc = (t & 7) * 8;
+    const int64_t r = r0 + i, c = c0 + cc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + r * lds_ + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tile[i][cc + 2 * k] = (uint16_t)(w[k] & 0xffff);
+      tile[i][cc + 2 * k + 1] = (uint16_t)(w[k] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: 8 threads per output row (8 source rows each), 32 rows per pass
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int j = pass * 32 + (t >> 3), rr = (t & 7) * 8;
+    const int64_t c = c0 + j, r = r0 + rr;
+    if (c >= C || r >= Rp) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)tile[rr + 2 * k][j] | ((uint32_t)tile[rr + 2 * k + 1][j] << 16);
+    *reinterpret_cast<uint4*>(dst + c * ldd + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 sbp_status transpose_pad(int dtype, const void* src, int64_t lds_, int64_t R, int64_t C,
                          void* dst, int64_t ldd, int64_t Rp, const int* active, hipStream_t st) {
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
   ProfScope prof("transpose", st, 0.0, (double)esz * ((double)R * C + (double)Rp * C));
   dim3 grid((unsigned)cdiv(C, 64), (unsigned)cdiv(Rp, 64));
-  if (dtype == SBP_BF16)
+  const bool vec8 = dtype == SBP_BF16 && C % 8 == 0 && lds_ % 8 == 0 && ldd % 8 == 0 && Rp % 8 == 0 &&
+                    (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0;
+  if (vec8)
+    hipLaunchKernelGGL(transpose_pad_bf16x8_kernel, grid, dim3(256), 0, st, (const bf16_t*)src, lds_, R, C,
+                       (bf16_t*)dst, ldd, Rp, active);
+  else if (dtype == SBP_BF16)
     hipLaunchKernelGGL(transpose_pad_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src,
                        lds_, R, C, (bf16_t*)dst, ldd, Rp, active);
   else
