@@ -21,7 +21,25 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
   return sh[0] + sh[1] + sh[2] + sh[3];
 }
 
-// one block per row
+// 8 bf16 <-> 8 fp32 (16-byte vectors; every row pitch and base here is a
+// multiple of 8 elements and 16-byte aligned).
+__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = bf2f((bf16_t)(w[k] & 0xffff));
+    f[2 * k + 1] = bf2f((bf16_t)(w[k] >> 16));
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]), pk_bf16(f[6], f[7]));
+}
+__device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// one block per row, 8 elements per thread and step
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const bf16_t* __restrict__ x, int64_t ldx,
                                                           const bf16_t* __restrict__ g, int d,
                                                           float eps, bf16_t* __restrict__ out,
@@ -30,19 +48,29 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const bf16_t* __restri
   const int64_t r = blockIdx.x;
   const bf16_t* xr = x + r * ldx;
   float ss = 0.f;
-  for (int j = threadIdx.x; j < d; j += 256) {
-    const float v = bf2f(xr[j]);
-    ss += v * v;
+  for (int j = threadIdx.x * 8; j < d; j += 2048) {
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(xr + j), v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
   }
   ss = block_sum256(ss, sh);
   const float ri = rsqrtf(ss / (float)d + eps);
   if (threadIdx.x == 0) rinv[r] = ri;
-  for (int j = threadIdx.x; j < d; j += 256) out[r * ldo + j] = f2bf(bf2f(g[j]) * bf2f(xr[j]) * ri);
+  for (int j = threadIdx.x * 8; j < d; j += 2048) {
+    float v[8], gg[8];
+    unpack8(*reinterpret_cast<const uint4*>(xr + j), v);
+    unpack8(*reinterpret_cast<const uint4*>(g + j), gg);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = gg[k] * v[k] * ri;
+    *reinterpret_cast<uint4*>(out + r * ldo + j) = pack8(v);
+  }
 }
 
 sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, int64_t d,
                        float eps, void* out, int64_t ldo, float* rinv, hipStream_t st) {
   if (rows <= 0) return SBP_OK;
+  if (d % 8 || ldx % 8 || ldo % 8) return set_error(SBP_ERR_INVALID_ARG, "rmsnorm_fwd: d and pitches must be multiples of 8");
   ProfScope prof("rmsnorm_fwd", st, 0.0, 4.0 * rows * d);
   hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)rows), dim3(256), 0, st, (const bf16_t*)x, ldx,
                      (const bf16_t*)g, (int)d, eps, (bf16_t*)out, ldo, rinv);
@@ -59,15 +87,24 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   const int64_t r = blockIdx.x;
   const float ri = rinv[r];
   float acc = 0.f;
-  for (int j = threadIdx.x; j < d; j += 256) {
-    const float xh = bf2f(x[r * ldx + j]) * ri;
-    acc += xh * bf2f(g[j]) * dn[r * ldn + j];
+  for (int j = threadIdx.x * 8; j < d; j += 2048) {
+    float xv[8], gv[8], dv[8];
+    unpack8(*reinterpret_cast<const uint4*>(x + r * ldx + j), xv);
+    unpack8(*reinterpret_cast<const uint4*>(g + j), gv);
+    load8f(dn + r * ldn + j, dv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += xv[k] * ri * gv[k] * dv[k];
   }
   const float mean = block_sum256(acc, sh) / (float)d;
-  for (int j = threadIdx.x; j < d; j += 256) {
-    const float xh = bf2f(x[r * ldx + j]) * ri;
-    const float v = (bf2f(g[j]) * dn[r * ldn + j] - xh * mean) * ri;
-    out[r * ldo + j] = f2bf(bf2f(resid[r * ldr + j]) + v);
+  for (int j = threadIdx.x * 8; j < d; j += 2048) {
+    float xv[8], gv[8], dv[8], rv[8];
+    unpack8(*reinterpret_cast<const uint4*>(x + r * ldx + j), xv);
+    unpack8(*reinterpret_cast<const uint4*>(g + j), gv);
+    load8f(dn + r * ldn + j, dv);
+    unpack8(*reinterpret_cast<const uint4*>(resid + r * ldr + j), rv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rv[k] += (gv[k] * dv[k] - xv[k] * ri * mean) * ri;
+    *reinterpret_cast<uint4*>(out + r * ldo + j) = pack8(rv);
   }
 }
 
@@ -75,6 +112,8 @@ sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* d
                        const float* rinv, const void* resid, int64_t ldr, int64_t rows, int64_t d,
                        void* out, int64_t ldo, hipStream_t st) {
   if (rows <= 0) return SBP_OK;
+  if (d % 8 || ldx % 8 || ldn % 8 || ldr % 8 || ldo % 8)
+    return set_error(SBP_ERR_INVALID_ARG, "rmsnorm_bwd: d and pitches must be multiples of 8");
   ProfScope prof("rmsnorm_bwd", st, 0.0, 10.0 * rows * d);
   hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)rows), dim3(256), 0, st, (const bf16_t*)x, ldx,
                      (const bf16_t*)g, dn, ldn, rinv, (const bf16_t*)resid, ldr, (int)d,
@@ -151,20 +190,25 @@ sbp_status gain_grad(const float* dn, int64_t ldn, const void* x, int64_t ldx, c
 
 __device__ __forceinline__ float sigmoidf_(float u) { return 1.f / (1.f + __expf(-u)); }
 
-// ug = [u | g] rows of 2F; m = silu(u) * g
+// ug = [u | g] rows of 2F; m = silu(u) * g, 8 elements per thread and step
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const bf16_t* __restrict__ ug, int64_t rows,
                                                          int64_t F, bf16_t* __restrict__ m) {
-  const int64_t n = rows * F;
+  const int64_t F8 = F / 8, n = rows * F8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / F, j = i - r * F;
-    const float u = bf2f(ug[r * 2 * F + j]), gg = bf2f(ug[r * 2 * F + F + j]);
-    m[i] = f2bf(u * sigmoidf_(u) * gg);
+    const int64_t r = i / F8, j = (i - r * F8) * 8;
+    float u[8], gg[8], o[8];
+    unpack8(*reinterpret_cast<const uint4*>(ug + r * 2 * F + j), u);
+    unpack8(*reinterpret_cast<const uint4*>(ug + r * 2 * F + F + j), gg);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = u[k] * sigmoidf_(u[k]) * gg[k];
+    *reinterpret_cast<uint4*>(m + r * F + j) = pack8(o);
   }
 }
 
 sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStream_t st) {
+  if (F % 8) return set_error(SBP_ERR_INVALID_ARG, "swiglu_fwd: F must be a multiple of 8");
   ProfScope prof("swiglu_fwd", st, 0.0, 6.0 * rows * F);
-  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * F, 256), 16384);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * F / 8, 256), 16384);
   hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)ug, rows, F,
                      (bf16_t*)m);
   SBP_LAUNCH_CHECK();
@@ -175,21 +219,29 @@ sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStrea
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16_t* __restrict__ dm,
                                                          const bf16_t* __restrict__ ug, int64_t rows,
                                                          int64_t F, bf16_t* __restrict__ dudg) {
-  const int64_t n = rows * F;
+  const int64_t F8 = F / 8, n = rows * F8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / F, j = i - r * F;
-    const float u = bf2f(ug[r * 2 * F + j]), gg = bf2f(ug[r * 2 * F + F + j]);
-    const float d = bf2f(dm[i]);
-    const float s = sigmoidf_(u);
-    dudg[r * 2 * F + j] = f2bf(d * gg * s * (1.f + u * (1.f - s)));
-    dudg[r * 2 * F + F + j] = f2bf(d * u * s);
+    const int64_t r = i / F8, j = (i - r * F8) * 8;
+    float u[8], gg[8], d[8], du[8], dg[8];
+    unpack8(*reinterpret_cast<const uint4*>(ug + r * 2 * F + j), u);
+    unpack8(*reinterpret_cast<const uint4*>(ug + r * 2 * F + F + j), gg);
+    unpack8(*reinterpret_cast<const uint4*>(dm + r * F + j), d);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float sg = sigmoidf_(u[k]);
+      du[k] = d[k] * gg[k] * sg * (1.f + u[k] * (1.f - sg));
+      dg[k] = d[k] * u[k] * sg;
+    }
+    *reinterpret_cast<uint4*>(dudg + r * 2 * F + j) = pack8(du);
+    *reinterpret_cast<uint4*>(dudg + r * 2 * F + F + j) = pack8(dg);
   }
 }
 
 sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, void* dudg,
                       hipStream_t st) {
+  if (F % 8) return set_error(SBP_ERR_INVALID_ARG, "swiglu_bwd: F must be a multiple of 8");
   ProfScope prof("swiglu_bwd", st, 0.0, 10.0 * rows * F);
-  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * F, 256), 16384);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * F / 8, 256), 16384);
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)dm,
                      (const bf16_t*)ug, rows, F, (bf16_t*)dudg);
   SBP_LAUNCH_CHECK();
@@ -199,18 +251,21 @@ sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, v
 __global__ __launch_bounds__(256) void rows_to_bf16_kernel(const float* __restrict__ src, int64_t lds_,
                                                            int64_t rows, int64_t cols,
                                                            bf16_t* __restrict__ dst, int64_t ldd) {
-  const int64_t n = rows * cols;
+  const int64_t C8 = cols / 8, n = rows * C8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cols, j = i - r * cols;
-    dst[r * ldd + j] = f2bf(src[r * lds_ + j]);
+    const int64_t r = i / C8, j = (i - r * C8) * 8;
+    float v[8];
+    load8f(src + r * lds_ + j, v);
+    *reinterpret_cast<uint4*>(dst + r * ldd + j) = pack8(v);
   }
 }
 
 sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t cols, void* dst,
                         int64_t ldd, hipStream_t st) {
   if (rows <= 0) return SBP_OK;
+  if (cols % 8 || lds_ % 8 || ldd % 8) return set_error(SBP_ERR_INVALID_ARG, "rows_to_bf16: sizes must be multiples of 8");
   ProfScope prof("rows_to_bf16", st, 0.0, 6.0 * rows * cols);
-  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * cols, 256), 16384);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * cols / 8, 256), 16384);
   hipLaunchKernelGGL(rows_to_bf16_kernel, dim3(grid), dim3(256), 0, st, src, lds_, rows, cols,
                      (bf16_t*)dst, ldd);
   SBP_LAUNCH_CHECK();
