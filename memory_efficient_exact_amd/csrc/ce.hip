@@ -246,8 +246,9 @@ __device__ __forceinline__ void store8<float>(float* p, const float* v) {
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Tile: 64 rows (tokens of the chunk) x 128 columns (vocab).
-template <typename OutT>
+// Tile: 64 rows (tokens of the chunk) x 128 columns (vocab).  With TR the
+// tile is also written transposed (dZt, vocab-major).
+template <typename OutT, bool TR>
 __global__ __launch_bounds__(256) void ce_grad_kernel(
     const float* __restrict__ Z, int64_t ldz, const int32_t* __restrict__ targets,
     const float* __restrict__ weights, const float* __restrict__ inv_norm,
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(
     OutT* __restrict__ dZ, int64_t ldg, OutT* __restrict__ dZt, int64_t ldgt, int64_t Tcp,
     const int* __restrict__ active) {
   if (active && *active == 0) return;
-  __shared__ float tile[64][129];
+  __shared__ float tile[TR ? 64 : 1][129];
   __shared__ float s_lse[64], s_sc[64];
   __shared__ int s_y[64];
   const int tid = threadIdx.x;
@@ -308,10 +309,13 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(
         for (int j = 0; j < 8; ++j) g[j] = 0.f;
       }
       if (r < Tc && v < Vp) store8<OutT>(dZ + r * ldg + v, g);
+      if constexpr (TR) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tile[lrow][cg * 8 + j] = g[j];
+        for (int j = 0; j < 8; ++j) tile[lrow][cg * 8 + j] = g[j];
+      }
     }
   }
+  if constexpr (!TR) return;
   __syncthreads();
   // pass 2: rows of dZ^T (vocab-major), 8 consecutive tokens per thread
   {
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(
       if (v < Vp && r < Tcp) {
         float g[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) g[j] = tile[rg * 8 + j][lcol];
+        for (int j = 0; j < 8; ++j) g[j] = tile[TR ? rg * 8 + j : 0][lcol];
         store8<OutT>(dZt + v * ldgt + r, g);
       }
     }
@@ -337,16 +341,21 @@ sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* target
                    int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,
                    int64_t ldgt, int64_t Tcp, const int* active, hipStream_t st) {
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
-  ProfScope prof("ce_grad", st, 0.0, (double)Tc * V * (4.0 + 2.0 * esz));
+  ProfScope prof("ce_grad", st, 0.0, (double)Tc * V * (4.0 + (dZt ? 2.0 : 1.0) * esz));
+  if (!dZt) Tcp = Tc;
   dim3 grid((unsigned)cdiv(Vp, 128), (unsigned)cdiv(Tcp, 64));
-  if (dtype == SBP_BF16)
-    hipLaunchKernelGGL(ce_grad_kernel<bf16_t>, grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)dZt, ldgt, Tcp,
-                       active);
+  if (dtype == SBP_BF16 && dZt)
+    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, true>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
+                       inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)dZt, ldgt, Tcp, active);
+  else if (dtype == SBP_BF16)
+    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, false>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
+                       inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)nullptr, ldgt, Tcp, active);
+  else if (dZt)
+    hipLaunchKernelGGL((ce_grad_kernel<float, true>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
+                       inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)dZt, ldgt, Tcp, active);
   else
-    hipLaunchKernelGGL(ce_grad_kernel<float>, grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)dZt, ldgt, Tcp,
-                       active);
+    hipLaunchKernelGGL((ce_grad_kernel<float, false>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
+                       inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)nullptr, ldgt, Tcp, active);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

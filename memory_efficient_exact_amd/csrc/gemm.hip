@@ -1,19 +1,19 @@
-// NT GEMM on CDNA4 matrix cores:  C[M,N] (op)= alpha * A[M,K] . B[N,K]^T
-//
-// Every chunk GEMM of the StreamBP path is put in this one form (both
-// operands K-contiguous), so one kernel serves them all:
+// GEMM on CDNA4 matrix cores:  C[M,N] (op)= alpha * A[M,K] . B[N,K]^T, where
+// the bf16 kernel also takes both operands stored K-major (A as [K, M], B as
+// [K, N]), so that weight gradients, which contract over tokens, read the
+// activations in place:
 //   logits      Z_c   = H_c  . W^T      A = H_c  [T_c, d],  B = W   [V, d]
 //   input grad  dH_c  = dZ_c . W        A = dZ_c [T_c, V],  B = W^T [d, V]
-//   weight grad dW   += dZ_g^T . H_g    A = dZ_g^T [V, K_g], B = H_g^T [d, K_g]
-// (the transposed operands are written by the producing kernels or by a
-// transpose kernel; see misc.hip / ce.hip).
+//   weight grad dW   += dZ_g^T . H_g    A = dZ_g [K_g, V],  B = H_g [K_g, d], both K-major
+// (W^T is formed once per call; the fp32 path also forms dZ^T and H^T; see
+// misc.hip / ce.hip).
 //
 // Two kernels:
-//  * gemm_nt_bf16_ring_kernel (bf16, K a multiple of 128, the default): a
-//    256 x 256 tile, 4 waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16
-//    blocks, operands fed global -> LDS by DMA through two 64 KB stages (its
-//    section below has the details);
-//  * gemm_nt_kernel (fp32, and bf16 with other K): a 128 x 128 tile, 4 waves
+//  * gemm_nt_bf16_ring_kernel (bf16, the default): a 256 x 256 tile, 4
+//    waves of 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16 blocks, operands
+//    fed global -> LDS by DMA through two 64 KB stages (its section below
+//    has the details);
+//  * gemm_nt_kernel (fp32, and bf16 the ring cannot take): a 128 x 128 tile, 4 waves
 //    of 64 x 64 as 16x16 MFMA blocks (v_mfma_f32_16x16x32_bf16, or
 //    v_mfma_f32_16x16x4_f32 four times per fragment), 16-byte global loads
 //    staged through registers into a double-buffered LDS tile whose rows are
@@ -218,6 +218,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Pipelined variant (the default for bf16): the same 256 x 256 tile and
@@ -239,21 +240,101 @@ struct RingFrag {
   uint4 a[4], b[4];
 };
 
-// Fragments of k16 step ks (0..3) of a 64-wide stage in LDS tile L.
+// LDS DMA as inline assembly (global_load_lds: lane l's bytes land at M0 +
+// size * l).  Issued this way the compiler neither tracks the LDS writes nor
+// adds waits for them -- its alias tracking cannot tell the transposed LDS
+// reads apart from in-flight fills and would drain every DMA before them --
+// so the kernel orders them itself with explicit waits and barriers.  The
+// s_nop is the one wait state gfx9 needs between an M0 write and an LDS DMA.
+// 16 zero bytes: the source of every DMA lane outside the operands
+__device__ uint4 g_ring_zero;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;  // low half of a generic LDS address
+}
+__device__ __forceinline__ void dma_x4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma_x1(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// A K-major operand ([K, P] in memory, P contiguous) is staged as four
+// 8 KB segments, segment s holding p in [64 s, 64 s + 64) of the stage's 64
+// k-rows: 128 bytes per k-row, 16-byte chunk c of k-row r at c ^ 4 ((r >> 1)
+// & 1).  One DMA instruction then fetches 8 k-rows x 128 bytes, the shape of
+// a row-major fetch (contiguous 512-byte runs per instruction were measured
+// slower).  Fragments (lane l: p = l % 32 of the fragment, k = 8 (l/32) ..
+// + 8 of the k16 step) are read transposed with two ds_read_b64_tr_b16:
+// within each 16-lane group, lane j fetches 4 p of k-row 8 (l/32) + (j >> 2)
+// (+ 4 for the second read) and receives one p of 4 consecutive k-rows, so
+// the k order matches a row-major fragment's.  A 32-lane half reads 4 k-rows
+// x 64 bytes, which the XOR spreads over the 4 64-byte quarters of a 256-byte
+// bank line (conflict-free).
+// Per-lane part of a transposed fragment read: k-row 8 (l/32) + q with q =
+// (l >> 2) & 3, chunk x = 2 ((l >> 4) & 1) + ((l & 3) >> 1), 8-byte half l & 1.
+__device__ __forceinline__ int kmaj_lane_off(int lane) {
+  const int q = (lane >> 2) & 3, x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  return (8 * (lane >> 5) + q) * 128 + x * 16 + 8 * (lane & 1);
+}
+// Fragment i of the sub-tile starting at p_base (a multiple of 128) of the
+// K-major region at byte offset rbyte of L, k16 step ks.
+__device__ __forceinline__ uint4 kmaj_frag(const uint4* L, int rbyte, int lo, int p_base, int i, int ks,
+                                          int lane) {
+  const int q = (lane >> 2) & 3;
+  const SBP_AS3 char* b = (const SBP_AS3 char*)L + rbyte + lo + ks * 16 * 128 +
+                          (p_base / 64 + (i >> 1)) * 8192 + 64 * ((i & 1) ^ (q >> 1));
+  i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_AS3 i16x4_t*)b);
+  i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBP_AS3 i16x4_t*)(b + 4 * 128));
+  uint4 u;
+  u.x = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+  u.y = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+  u.z = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+  u.w = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+  return u;
+}
+
+// Fragments of k16 step ks (0..3) of a 64-wide stage in LDS tile L (A in
+// bytes [0, 32K), B in [32K, 64K)).
+template <bool AKM, bool BKM>
 __device__ __forceinline__ void ring_load(const uint4* __restrict__ L, int ks, int wm, int wn, int lane,
-                                          RingFrag& f) {
+                                          int klo, RingFrag& f) {
   constexpr int BM = 256, WT = 128;
   const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = wm * WT + i * 32 + (lane & 31);
-    f.a[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
+    if constexpr (AKM) {
+      f.a[i] = kmaj_frag(L, 0, klo, wm * WT, i, ks, lane);
+    } else {
+      const int r = wm * WT + i * 32 + (lane & 31);
+      f.a[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = BM + wn * WT + i * 32 + (lane & 31);
-    f.b[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
+    if constexpr (BKM) {
+      f.b[i] = kmaj_frag(L, BM * 128, klo, wn * WT, i, ks, lane);
+    } else {
+      const int r = BM + wn * WT + i * 32 + (lane & 31);
+      f.b[i] = L[r * 8 + (ch ^ ((r >> 1) & 7))];
+    }
   }
+}
+
+// Reads of the next fragments spread over the first MFMAs of a group (two
+// reads per MFMA), for the K-major tiles' 16 transposed reads per k16 step.
+template <int NR>
+__device__ __forceinline__ void interleave_reads() {
+#pragma unroll
+  for (int i = 0; i < NR / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR / 2, 0);
 }
 
 __device__ __forceinline__ void ring_mma(const RingFrag& f, f32x16_t (&acc)[4][4]) {
@@ -266,7 +347,7 @@ __device__ __forceinline__ void ring_mma(const RingFrag& f, f32x16_t (&acc)[4][4
           0, 0, 0);
 }
 
-template <int EPI>
+template <int EPI, bool AKM, bool BKM>
 __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256, BK = 64, WT = 128;
   __shared__ uint4 L0[(BM + BN) * 8];
@@ -276,46 +357,108 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   int tm, tn, split;
   tile_coords(p, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
+  // K runs to a multiple of 128: chunks at k >= K read zeros (so K itself
+  // need only be a multiple of 8)
+  const int Kpad = (p.K + 127) & ~127;
   const int kb = split * p.k_per_split;
-  const int ke = min(p.K, kb + p.k_per_split);
+  const int ke = min(Kpad, kb + p.k_per_split);
+  const bf16_t* zero = reinterpret_cast<const bf16_t*>(&g_ring_zero);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // DMA role: waves 0-1 fetch the A panel, 2-3 the B panel, 128 rows each
+  // DMA role: waves 0-1 fetch the A panel, 2-3 the B panel: 128 rows each of
+  // a row-major operand, or 32 k-rows each of a K-major one
   const int opnd = wave >> 1;
+  static_assert(AKM == BKM, "both operands K-major or neither");
+  constexpr bool kmaj = AKM;
+  const int klo = kmaj_lane_off(lane);
   const int rbase = (wave & 1) * 128;
-  // instruction j fills LDS rows lds_row0 + 8j + lane / 8 (lds_row0 % 16 == 0),
+  // row-major: instruction j fills LDS rows 256 opnd + rbase + 8j + lane / 8,
   // slot lane % 8, with logical chunk slot ^ ((row >> 1) & 7)
   const int chunk_even = (lane & 7) ^ (lane >> 4), chunk_odd = (lane & 7) ^ (4 + (lane >> 4));
   const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
   const int64_t ld = opnd ? p.ldb : p.lda;
   const int lim = opnd ? p.N : p.M;
   const int r0 = (opnd ? n0 : m0) + rbase + (lane >> 3);
-  const int lds_row0 = opnd * BM + rbase;
 
-  auto issue_one = [&](uint4* L, int k0, int j) {
-    int gr = r0 + j * 8;
-    gr = gr < lim ? gr : lim - 1;
-    const bf16_t* g = X + (int64_t)gr * ld + k0 + ((j & 1) ? chunk_odd : chunk_even) * 8;
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)g,
-                                     (SBP_AS3 void*)&L[(lds_row0 + j * 8) * 8], 16, 0, 0);
+  // Per-lane parts of the fetch addresses.  Instruction j of a stage reads
+  // row rb + ro(j), column c(j) + co(j) -- k0 goes to the row of a K-major
+  // operand and to the column of a row-major one -- and zeros outside
+  // [0, rlim) x [0, clim):
+  //   row-major: rows r0 + 8j, column k0 + 8 (chunk slot ^ ((row >> 1) & 7)),
+  //              filling the 1 KB at 32768 opnd + 16384 (wave & 1) + 1024 j;
+  //   K-major:   k-rows k0 + 32 (wave & 1) + 8 (j & 3) + lane / 8 of segment
+  //              s = j >> 2, p = 64 s + 8 (slot ^ 4 ((lane >> 4) & 1)),
+  //              filling the 1 KB at 32768 opnd + 8192 s + 4096 (wave & 1)
+  //              + 1024 (j & 3).
+  const int p0 = opnd ? n0 : m0;
+  const int kl = (wave & 1) * 32 + (lane >> 3);
+  const int rlim = kmaj ? p.K : lim, clim = kmaj ? lim : p.K;
+  const int c_km = p0 + 8 * ((lane & 7) ^ (4 * ((lane >> 4) & 1)));
+  const int c_even = kmaj ? c_km : chunk_even * 8;
+  const int c_odd = kmaj ? c_km : chunk_odd * 8;
+  const uint32_t dst0 = (uint32_t)(opnd * 32768 + (wave & 1) * (kmaj ? 4096 : 16384));
+  // the stage's two base addresses (even / odd j) are computed once and
+  // kept opaque, so that each instruction adds a uniform offset to one
+  struct StageSrc {
+    const bf16_t *e, *o;
+    int rb, ce, co;
   };
-  auto issue = [&](uint4* L, int k0) {
+  auto stage_src = [&](int k0) __attribute__((always_inline)) {
+    StageSrc q;
+    q.rb = kmaj ? k0 + kl : r0;
+    q.ce = c_even + (kmaj ? 0 : k0);
+    q.co = c_odd + (kmaj ? 0 : k0);
+    const bf16_t* row = X + (int64_t)q.rb * ld;
+    q.e = row + q.ce;
+    q.o = row + q.co;
+    asm volatile("" : "+v"(q.e), "+v"(q.o));
+    return q;
+  };
+  auto src_addr = [&](const StageSrc& q, int j) __attribute__((always_inline)) {
+    const int ro = kmaj ? 8 * (j & 3) : 8 * j, co = kmaj ? 64 * (j >> 2) : 0;
+    const bool ok = q.rb + ro < rlim && ((j & 1) ? q.co : q.ce) + co < clim;
+    const bf16_t* g = ((j & 1) ? q.o : q.e) + (int64_t)ro * ld + co;
+    return ok ? g : zero;
+  };
+  auto dst_of = [&](int j) __attribute__((always_inline)) {
+    return dst0 + (kmaj ? 8192u * (j >> 2) + 1024u * (j & 3) : 1024u * j);
+  };
+  // four DMAs whose addresses are all formed first (in distinct registers, so
+  // that no address register is rewritten right after its load issues)
+  auto issue_four = [&](uint4* L, const StageSrc& q, int j0) __attribute__((always_inline)) {
+    const bf16_t* g0 = src_addr(q, j0);
+    const bf16_t* g1 = src_addr(q, j0 + 1);
+    const bf16_t* g2 = src_addr(q, j0 + 2);
+    const bf16_t* g3 = src_addr(q, j0 + 3);
+    asm volatile("" ::"v"(g0), "v"(g1), "v"(g2), "v"(g3));
+    const uint32_t l = lds_addr(L);
+    dma_x4(g0, l + dst_of(j0));
+    dma_x4(g1, l + dst_of(j0 + 1));
+    dma_x4(g2, l + dst_of(j0 + 2));
+    dma_x4(g3, l + dst_of(j0 + 3));
+  };
+  auto issue = [&](uint4* L, int k0) __attribute__((always_inline)) {
+    const StageSrc q = stage_src(k0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) issue_one(L, k0, j);
+    for (int j = 0; j < 16; j += 4) issue_four(L, q, j);
   };
   // L2 prefetch of the stage after the one being fetched: one 4-byte DMA per
   // row touches the row's cache line of that K slice (2 instructions per
   // wave), so that its real fetch a stage later finds the line in L2 (or
   // already on its way).  The ring thus hides two stages of memory latency
   // with two LDS buffers.
-  auto prefetch = [&](int k0) {
+  auto prefetch = [&](int k0) __attribute__((always_inline)) {
+    // row-major: rows p0 + rbase + 64h + lane at column k0; K-major: k-rows
+    // k0 + 32 (wave & 1) + 16h + lane / 4, 128-byte line lane % 4 of the
+    // tile's 512 bytes
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      int gr = (opnd ? n0 : m0) + rbase + h * 64 + lane;
-      gr = gr < lim ? gr : lim - 1;
-      __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(X + (int64_t)gr * ld + k0),
-                                       (SBP_AS3 void*)&PF[wave][0], 4, 0, 0);
+      const int row = kmaj ? min(k0 + (wave & 1) * 32 + 16 * h + (lane >> 2), p.K - 1)
+                           : min(p0 + rbase + 64 * h + lane, lim - 1);
+      const int col = max(0, kmaj ? min(p0 + 64 * (lane & 3), lim - 8) : min(k0, p.K - 8));
+      dma_x1(X + (int64_t)row * ld + col, lds_addr(&PF[wave][0]));
     }
   };
 
@@ -326,9 +469,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   // nk is 0 or even.  The refill past the end re-fetches the last stage into
-  // a buffer nobody reads, so every step has the same shape.  Waits use the
-  // builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
-  // 11:8) so the compiler's own wait insertion knows what has landed.
+  // a buffer nobody reads, so every step has the same shape.  The compiler
+  // does not see the DMAs (inline assembly), so every wait for them is
+  // explicit (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+  // lgkmcnt 11:8); vmcnt retires loads in issue order.
   const int nk = ke > kb ? (ke - kb) / BK : 0;
   RingFrag f0, f1;
   if (nk > 0) {
@@ -339,26 +483,29 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     asm volatile("" ::: "memory");
     issue(L1, kb + BK);
     prefetch(kb + min(2, nk - 1) * BK);
-    ring_load(L0, 0, wm, wn, lane, f0);
+    ring_load<AKM, BKM>(L0, 0, wm, wn, lane, klo, f0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
-  auto step = [&](const uint4* Lc, const uint4* Ln, uint4* Lrefill, int t) {
+  auto step = [&](const uint4* Lc, const uint4* Ln, uint4* Lrefill, int t) __attribute__((always_inline)) {
     // lgkmcnt(0) after each MFMA group: the reads issued before it have long
     // landed, and saying so keeps at most 8 reads outstanding (the counter
     // cannot express waits with more than 15 in flight).
-    ring_load(Lc, 1, wm, wn, lane, f1);
-    __builtin_amdgcn_sched_barrier(0);
+    ring_load<AKM, BKM>(Lc, 1, wm, wn, lane, klo, f1);
+    if constexpr (!kmaj) __builtin_amdgcn_sched_barrier(0);
     ring_mma(f0, acc);
+    if constexpr (kmaj) interleave_reads<16>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    ring_load(Lc, 2, wm, wn, lane, f0);
-    __builtin_amdgcn_sched_barrier(0);
+    ring_load<AKM, BKM>(Lc, 2, wm, wn, lane, klo, f0);
+    if constexpr (!kmaj) __builtin_amdgcn_sched_barrier(0);
     ring_mma(f1, acc);
+    if constexpr (kmaj) interleave_reads<16>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    ring_load(Lc, 3, wm, wn, lane, f1);
-    __builtin_amdgcn_sched_barrier(0);
+    ring_load<AKM, BKM>(Lc, 3, wm, wn, lane, klo, f1);
+    if constexpr (!kmaj) __builtin_amdgcn_sched_barrier(0);
     ring_mma(f0, acc);
+    if constexpr (kmaj) interleave_reads<16>();
     __builtin_amdgcn_sched_barrier(0);
     // stage t+1 landed (only the 2 prefetches issued after it may still be
     // in flight), step 3 read
@@ -369,13 +516,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     // the next stage's first fragments, then the refill DMA spread over the
     // 16 MFMAs of step 3 (4 DMA instructions per 4 MFMAs) so that the wave
     // never stalls issuing a burst of DMAs while the matrix unit idles
-    ring_load(Ln, 0, wm, wn, lane, f0);
+    ring_load<AKM, BKM>(Ln, 0, wm, wn, lane, klo, f0);
     __builtin_amdgcn_sched_barrier(0);
-    const int kr = kb + min(t + 2, nk - 1) * BK;
+    const StageSrc src = stage_src(kb + min(t + 2, nk - 1) * BK);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int j = 4 * q; j < 4 * q + 4; ++j) issue_one(Lrefill, kr, j);
+      issue_four(Lrefill, src, 4 * q);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
@@ -393,7 +539,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   }
 
   // Epilogue through LDS: each wave parks 32 rows x 128 columns of fp32 (16 KB)
-  // in its own quarter of L0|L1, then writes row-contiguous 4-wide vectors.
+  // in its own quarter of L0|L1, then writes row-contiguous 4-wide vectors
+  // (after the trailing refill and prefetch DMAs have landed).
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   __syncthreads();
   float* W = reinterpret_cast<float*>((wave < 2 ? L0 : L1)) + (wave & 1) * (32 * 128);
   float beta = (float)p.beta;
@@ -518,18 +666,26 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   }
 }
 
+template <bool AKM, bool BKM>
+static void launch_bf16_ring_layout(int epi, const GemmParams& p, int grid, hipStream_t st) {
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_F32_LSE: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32_LSE, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_F32_ACC: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32_ACC, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_OUT: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_OUT, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_OUT_RESID: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_OUT_RESID, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_PARTIAL, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+  }
+}
+
 static void launch_bf16_ring(int epi, GemmParams p, hipStream_t st) {
   p.tiles_m = (int)cdiv(p.M, 256);
   p.tiles_n = (int)cdiv(p.N, 256);
   const int grid = p.tiles_m * p.tiles_n * p.k_split;
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_F32_LSE: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32_LSE>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_F32_ACC: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_F32_ACC>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_OUT: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT>, dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_OUT_RESID: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_OUT_RESID>, dim3(grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL(gemm_nt_bf16_ring_kernel<EPI_PARTIAL>, dim3(grid), dim3(256), 0, st, p); break;
-  }
+  if (p.a_kmajor)
+    launch_bf16_ring_layout<true, true>(epi, p, grid, st);
+  else
+    launch_bf16_ring_layout<false, false>(epi, p, grid, st);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN>
@@ -559,10 +715,14 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
                        (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : 4.0 * p.k_split);
   // (the row statistics of EPI_F32_LSE add 8 bytes per 128 output columns)
   ProfScope prof(name, st, flops, bytes);
-  const bool ring_ok = dtype == SBP_BF16 && p.K % 128 == 0 && p.k_per_split % 128 == 0 &&
-                       p.lda % 8 == 0 && p.ldb % 8 == 0;
+  const bool ring_ok = dtype == SBP_BF16 && (p.K % 8 == 0 || p.a_kmajor) &&
+                       p.k_per_split % 128 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
+                       (!p.a_kmajor || p.lda >= round_up(p.M, 8)) &&
+                       (!p.b_kmajor || p.ldb >= round_up(p.N, 8));
   if (epi == EPI_F32_LSE && !(tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 && p.row_stats))
     return set_error(SBP_ERR_UNSUPPORTED, "row-statistics epilogue needs the bf16 ring GEMM without split-K");
+  if ((p.a_kmajor || p.b_kmajor) && !(tile == GEMM_TILE_RING && ring_ok && p.a_kmajor == p.b_kmajor))
+    return set_error(SBP_ERR_UNSUPPORTED, "K-major GEMM operands need the bf16 ring GEMM, both K-major");
   if (dtype == SBP_BF16) {
     if (tile == GEMM_TILE_RING && ring_ok)
       launch_bf16_ring(epi, p, st);

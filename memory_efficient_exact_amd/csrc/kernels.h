@@ -12,12 +12,14 @@ enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL
 enum { GEMM_TILE_128 = 0, GEMM_TILE_RING = 3 };
 
 struct GemmParams {
-  const void* A = nullptr;  // [M, K] row-major, K contiguous, pitch lda elements
-  const void* B = nullptr;  // [N, K] row-major, pitch ldb
+  const void* A = nullptr;  // [M, K] row-major, K contiguous, pitch lda elements ([K, M] if a_kmajor)
+  const void* B = nullptr;  // [N, K] row-major, pitch ldb ([K, N] if b_kmajor)
   void* C = nullptr;        // [M, N] pitch ldc (fp32 for F32/F32_ACC/PARTIAL, else dtype)
   const void* R = nullptr;  // residual [M, N] pitch ldr (EPI_OUT_RESID)
   int64_t lda = 0, ldb = 0, ldc = 0, ldr = 0;
-  int M = 0, N = 0, K = 0;  // K % 8 == 0 (bf16) / K % 4 == 0 (fp32); lda/ldb likewise
+  // K % 8 == 0 (bf16) / K % 4 == 0 (fp32); lda/ldb likewise.  The bf16 ring
+  // GEMM with K-major operands takes any K.
+  int M = 0, N = 0, K = 0;
   float alpha = 1.f;
   int beta = 0;                    // EPI_F32_ACC: C = acc + beta * C
   const int* beta_zero = nullptr;  // EPI_F32_ACC: device flag, non-zero forces beta = 0
@@ -26,6 +28,11 @@ struct GemmParams {
   int k_per_split = 0;             // multiple of the K step (0 = even split)
   int64_t split_stride = 0;        // EPI_PARTIAL: elements between partial outputs
   int m_fastest = 1;               // tile order inside an XCD's range (register-staged kernel only)
+  // bf16 ring GEMM only: both operands stored K-major, A as [K, M] and B as
+  // [K, N], with pitches lda >= round_up(M, 8) and ldb >= round_up(N, 8)
+  // between k-rows (rows are read in 8-element chunks up to that bound);
+  // the two flags must be equal
+  int a_kmajor = 0, b_kmajor = 0;
   float2* row_stats = nullptr;     // EPI_F32_LSE: [M, ld_stats], entry 4 tn + quarter
   int64_t ld_stats = 0;
   int tiles_m = 0, tiles_n = 0;    // filled by the launcher
@@ -54,7 +61,8 @@ sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z
 sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
                     int64_t s, int64_t Tc, int64_t V, float* lse, float* loss_part,
                     float* token_loss, hipStream_t st);
-// dZ (dtype) [Tc, ldg] and dZ^T (dtype) [Vp, ldgt] for one chunk; zero pads.
+// dZ (dtype) [Tc, ldg] and, if dZt is not NULL, dZ^T (dtype) [Vp, ldgt] for
+// one chunk; zero pads (columns V .. Vp of dZ, columns Tc .. Tcp of dZ^T).
 sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* targets,
                    const float* weights, const float* inv_norm, const float* lse, int64_t s,
                    int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,

@@ -19,9 +19,12 @@
 //   final because later chunks already added theirs and earlier chunks never
 //   reach them);  dWq, dWk, dWv += [dq | dK_c | dV_c]^T h1;
 //   dh1 = [dq | dK_c | dV_c] [Wq; Wk; Wv];  dx = da + RMSNorm1'(dh1), dg1 +=.
-// Every product is an NT GEMM (gemm.hip): the weight transposes are formed
-// once per call, the chunk-time transposes (operands contracted over the
-// chunk's tokens) per chunk, zero-padded to the GEMM's K granule.
+// Every product is one bf16 ring GEMM (gemm.hip).  Weight gradients contract
+// over the chunk's tokens and read both activations K-major, in place (e.g.
+// dW2 = dy^T m from dy [T_c, d] and m [T_c, F]).  Products that contract
+// over a weight's rows (dm = dy W2, dn2 = [du | dg] [W1; W3], do = da Wo,
+// dh1 = [dq | dK | dV] [Wq; Wk; Wv]) read weight transposes formed once per
+// call.
 #include "attn.h"
 #include "common.h"
 #include "kernels.h"
@@ -35,7 +38,7 @@ struct LayerShape {
   int64_t T, d, F, qd, kd, qkvd;
   int Hq, Hkv, dh;
   int32_t D;
-  int64_t Tcm, Tcp;
+  int64_t Tcm;
   float eps;
 };
 
@@ -48,7 +51,6 @@ LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
   s.qkvd = s.qd + 2 * s.kd;
   s.D = D;
   s.Tcm = max_chunk_len(L->T, D);
-  s.Tcp = round_up(s.Tcm, 128);
   s.eps = L->eps;
   return s;
 }
@@ -59,7 +61,6 @@ struct LayerWs {
   bf16_t *W2T, *W13T, *WoT, *WqkvT;
   bf16_t *h1, *q, *o, *a, *n2, *ug, *mdm, *dudg, *da, *dov, *dqkv;
   float *dn, *rinv1, *rinv2, *lse, *delta, *gpart;
-  bf16_t *TA, *TB;
 };
 
 size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
@@ -93,10 +94,6 @@ size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
   x.lse = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   x.delta = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   x.gpart = (float*)P.take(f4 * gain_grad_splits(R) * s.d);
-  const int64_t maxA = std::max(std::max(s.d, 2 * s.F), s.qkvd);
-  const int64_t maxB = std::max(std::max(s.F, s.d), s.qd);
-  x.TA = (bf16_t*)P.take(b2 * maxA * s.Tcp);
-  x.TB = (bf16_t*)P.take(b2 * maxB * s.Tcp);
   if (w) *w = x;
   return round_up((int64_t)P.off, 256);
 }
@@ -165,15 +162,21 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     if (_s != SBP_OK) return _s;     \
   } while (0)
 
-  // C[M, N] (op)= A[M, K] B[N, K]^T
+  // C[M, N] (op)= A B^T with A [M, K] and B [N, K] (kmaj: A [K, M], B [K, N])
   auto gemm = [&](const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                   int64_t M, int64_t N, int64_t K, int epi, int beta, const void* R, int64_t ldr,
-                  const char* name) -> sbp_status {
+                  const char* name, int kmaj = 0) -> sbp_status {
     GemmParams p;
     p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc; p.R = R; p.ldr = ldr;
     p.M = (int)M; p.N = (int)N; p.K = (int)K; p.beta = beta;
-    p.m_fastest = M <= N ? 1 : 0;
+    p.a_kmajor = p.b_kmajor = kmaj;
     return gemm_nt(SBP_BF16, epi, p, GEMM_TILE_RING, str, name);
+  };
+  // weight gradient G[M, N] (+)= A^T B over the chunk's Tc tokens, A [Tc, M]
+  // and B [Tc, N] read K-major
+  auto gemm_wg = [&](const void* A, int64_t lda, const void* B, int64_t ldb, float* G, int64_t M,
+                     int64_t N, int64_t Tc, int beta) -> sbp_status {
+    return gemm(A, lda, B, ldb, G, N, M, N, Tc, EPI_F32_ACC, beta, nullptr, 0, "gemm_layer_dW", 1);
   };
   auto tr = [&](const void* src, int64_t ld_src, int64_t rows, int64_t cols, void* dst,
                 int64_t ld_dst, int64_t rows_pad) -> sbp_status {
@@ -204,7 +207,6 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     int64_t s0, e0;
     chunk_bounds(S.T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
-    const int64_t Tp = round_up(Tc, 128);
     const int wb = (c == D - 1) ? (accumulate ? 1 : 0) : 1;  // weight-gradient beta
     const bf16_t* xc = X + s0 * d;
     const bf16_t* dyc = DY + s0 * d;
@@ -230,24 +232,18 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     SBP_TRY(swiglu_fwd(W.ug, Tc, F, W.mdm, str));
 
     // ---- MLP backward ----
-    SBP_TRY(tr(dyc, d, Tc, d, W.TA, Tp, Tp));            // dy^T [d, Tp]
-    SBP_TRY(tr(W.mdm, F, Tc, F, W.TB, Tp, Tp));          // m^T  [F, Tp]
-    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->W2, F, d, F, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm_wg(dyc, d, W.mdm, F, g->W2, d, F, Tc, wb));                    // dW2 += dy^T m
     SBP_TRY(gemm(dyc, d, W.W2T, d, W.mdm, F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));  // dm
     SBP_TRY(swiglu_bwd(W.mdm, W.ug, Tc, F, W.dudg, str));
-    SBP_TRY(tr(W.dudg, 2 * F, Tc, 2 * F, W.TA, Tp, Tp)); // [du | dg]^T [2F, Tp]
-    SBP_TRY(tr(W.n2, d, Tc, d, W.TB, Tp, Tp));           // n2^T [d, Tp]
-    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->W1, d, F, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
-    SBP_TRY(gemm(W.TA + F * Tp, Tp, W.TB, Tp, g->W3, d, F, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm_wg(W.dudg, 2 * F, W.n2, d, g->W1, F, d, Tc, wb));             // dW1 += du^T n2
+    SBP_TRY(gemm_wg(W.dudg + F, 2 * F, W.n2, d, g->W3, F, d, Tc, wb));         // dW3 += dg^T n2
     SBP_TRY(gemm(W.dudg, 2 * F, W.W13T, 2 * F, W.dn, d, Tc, d, 2 * F, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(W.a, d, w->g2, W.dn, d, W.rinv2, dyc, d, Tc, d, W.da, d, str));
     SBP_TRY(gain_grad(W.dn, d, W.a, d, W.rinv2, Tc, d, g->g2, wb, W.gpart, str));
 
     // ---- output projection ----
-    SBP_TRY(tr(W.da, d, Tc, d, W.TA, Tp, Tp));           // da^T [d, Tp]
-    SBP_TRY(tr(W.o, qd, Tc, qd, W.TB, Tp, Tp));          // o^T  [qd, Tp]
-    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->Wo, qd, d, qd, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
-    SBP_TRY(gemm(W.da, d, W.WoT, d, W.dov, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));
+    SBP_TRY(gemm_wg(W.da, d, W.o, qd, g->Wo, d, qd, Tc, wb));                  // dWo += da^T o
+    SBP_TRY(gemm(W.da, d, W.WoT, d, W.dov, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));  // do
 
     // ---- attention over the causal key prefix ----
     at.dO = W.dov;
@@ -257,11 +253,9 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
 
     // ---- q, k, v projections and the first norm ----
-    SBP_TRY(tr(W.dqkv, qkvd, Tc, qkvd, W.TA, Tp, Tp));   // [dq | dK | dV]^T
-    SBP_TRY(tr(W.h1, d, Tc, d, W.TB, Tp, Tp));           // h1^T
-    SBP_TRY(gemm(W.TA, Tp, W.TB, Tp, g->Wq, d, qd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
-    SBP_TRY(gemm(W.TA + qd * Tp, Tp, W.TB, Tp, g->Wk, d, kd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
-    SBP_TRY(gemm(W.TA + (qd + kd) * Tp, Tp, W.TB, Tp, g->Wv, d, kd, d, Tp, EPI_F32_ACC, wb, nullptr, 0, "gemm_layer_dW"));
+    SBP_TRY(gemm_wg(W.dqkv, qkvd, W.h1, d, g->Wq, qd, d, Tc, wb));             // dWq += dq^T h1
+    SBP_TRY(gemm_wg(W.dqkv + qd, qkvd, W.h1, d, g->Wk, kd, d, Tc, wb));        // dWk += dK^T h1
+    SBP_TRY(gemm_wg(W.dqkv + qd + kd, qkvd, W.h1, d, g->Wv, kd, d, Tc, wb));   // dWv += dV^T h1
     SBP_TRY(gemm(W.dqkv, qkvd, W.WqkvT, qkvd, W.dn, d, Tc, d, qkvd, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(xc, d, w->g1, W.dn, d, W.rinv1, W.da, d, Tc, d, DX + s0 * d, d, str));
     SBP_TRY(gain_grad(W.dn, d, xc, d, W.rinv1, Tc, d, g->g1, wb, W.gpart, str));

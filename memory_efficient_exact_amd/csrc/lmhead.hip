@@ -2,20 +2,23 @@
 //
 // Per chunk c = [s, e) (skill page "Implementation": the sequence
 // decomposition, the logits-gradient routine and the linear-layer chunk
-// gradient), with every GEMM in the NT form of gemm.hip:
+// gradient):
 //   Z_c   = H_c W^T                fp32 [T_c, V]          (gemm, EPI_F32_LSE: with
 //                                  per-64-column row (max, sum-exp) partials)
 //   lse, l_t, c_t l_t              per row                 (ce_merge of the partials;
 //                                  ce_stats over Z where the GEMM cannot: fp32, d % 128)
-//   dZ_c, dZ_c^T                   dtype, zero-padded      (ce_grad)
-//   H_c^T                          dtype [d, T_c]          (transpose_pad)
-//   dH_c  = dZ_c W = dZ_c (W^T)^T  split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
+//   dZ_c                           dtype, zero-padded      (ce_grad)
+//   dH_c  = dZ_c W                 split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
 //   dW   += dZ_g^T H_g             fp32 read-modify-write  (gemm EPI_F32_ACC)
-// W^T is formed once per call.  The weight gradient is taken once per group
-// g of G consecutive chunks (dZ_c^T and H_c^T of the group side by side in
-// the K dimension, so that the sum over the group's tokens is one GEMM):
-// the fp32 read-modify-write of dW is paid once per G chunks and K is G T_c
-// long.  Peak workspace is O(G T_c V + V d), not O(T V).
+// The weight gradient is taken once per group g of G consecutive chunks, so
+// that the fp32 read-modify-write of dW is paid once per G chunks and the
+// GEMM's K (the group's tokens) is about 4096 long.
+// W^T is formed once per call (dH contracts over W's rows).  bf16: the dW
+// GEMM reads dZ_g and H_g ([tokens, .], contracted over tokens) K-major, in
+// place: dZ_c is written into a group buffer whose rows are the group's
+// tokens in order, and H_g is a row range of H.  fp32 (NT GEMMs only):
+// dZ_c^T and H_c^T side by side in K per group (slots of T_c rounded up to
+// the K granule).  Workspace O(G T_c V + V d).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,10 +27,10 @@ namespace {
 
 struct LmWs {
   float* Z;
-  void* dZ;
-  void* dZt;
+  void* dZ;   // bf16: the group buffer [G T_c, Vp]; fp32: [T_c, Vp]
+  void* dZt;  // fp32 only
   void* Wt;
-  void* Ht;
+  void* Ht;   // fp32 only
   float* part;
   float* lse;
   float* loss_part;
@@ -44,7 +47,8 @@ struct LmShape {
   bool fused_stats;  // the logits GEMM writes the row statistics partials
   int nparts;
   int G;  // chunks per dW GEMM
-  int64_t Kg;  // K extent of the dW group buffers: G * Tcp
+  int64_t Kg;  // fp32: K extent of the dW group buffers, G * Tcp
+  bool kmajor;  // bf16: GEMM operands read K-major in place
   size_t esz;
 };
 
@@ -53,7 +57,7 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   s.T = T; s.d = d; s.V = V; s.D = D; s.dtype = dtype;
   s.esz = dtype == SBP_BF16 ? 2 : 4;
   s.Tcm = max_chunk_len(T, D);
-  s.Tcp = round_up(s.Tcm, 128);  // K granule of the bf16 GEMM
+  s.Tcp = round_up(s.Tcm, 128);  // fp32 dW slot width; also sets the group size
   s.Vp = round_up(V, 128);
   // dH GEMM: few output tiles, long K = V.  Split K so that the launch has
   // ~1024 blocks (4 per CU); a function of the shape only.
@@ -67,6 +71,7 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   // flop or less); a function of the shape only.
   s.G = (int)std::max<int64_t>(1, std::min<int64_t>(D, 4096 / s.Tcp));
   s.Kg = s.G * s.Tcp;
+  s.kmajor = dtype == SBP_BF16;
   s.fused_stats = dtype == SBP_BF16 && d % 128 == 0;
   s.nparts = (int)(4 * cdiv(V, 256));
   return s;
@@ -77,10 +82,15 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   P.base = base;
   LmWs x;
   x.Z = (float*)P.take(sizeof(float) * s.Tcm * s.Vp);
-  x.dZ = P.take(s.esz * s.Tcm * s.Vp);
-  x.dZt = P.take(s.esz * s.Vp * s.Kg);
   x.Wt = P.take(s.esz * s.d * s.Vp);
-  x.Ht = P.take(s.esz * s.d * s.Kg);
+  if (s.kmajor) {
+    x.dZ = P.take(s.esz * s.G * s.Tcm * s.Vp);
+    x.dZt = x.Ht = nullptr;
+  } else {
+    x.dZ = P.take(s.esz * s.Tcm * s.Vp);
+    x.dZt = P.take(s.esz * s.Vp * s.Kg);
+    x.Ht = P.take(s.esz * s.d * s.Kg);
+  }
   x.part = (float*)P.take(sizeof(float) * (size_t)s.S * s.Tcm * s.d);
   x.lse = (float*)P.take(sizeof(float) * s.Tcm);
   x.loss_part = (float*)P.take(sizeof(float) * s.T);
@@ -154,19 +164,25 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
   } while (0)
 
   SBP_TRY(lm_prep(targets, T, D, s.G, reduction, accumulate, w.prep, str));
-  // W^T [d, Vp], zero columns V..Vp (they meet the zero pad of dZ in the dH GEMM)
+  // W^T [d, Vp], zero columns V..Vp (they meet the zero pad of dZ in the dH
+  // GEMM)
   SBP_TRY(transpose_pad(dtype, W, d, V, d, w.Wt, s.Vp, s.Vp, nullptr, str));
+  int64_t s_group = 0;  // first token of the current dW group
   for (int32_t c = 0; c < D; ++c) {
     int64_t s0, e0;
     chunk_bounds(T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
     const int* act = w.prep.chunk_active + c;
-    // slot j of dW group g: columns [j Tcp, (j + 1) Tcp) of dZ^T and H^T,
-    // zero past the chunk's T_c.  In a group of several chunks an inactive
-    // chunk still writes its slot (zeros for dZ^T: every row has c_t = 0).
+    // chunk c is slot j of dW group g.  bf16: its dZ rows are rows
+    // [s0 - s_group, e0 - s_group) of the group buffer; fp32: columns
+    // [j Tcp, (j + 1) Tcp) of dZ^T and H^T, zero past the chunk's T_c.  In a
+    // group of several chunks an inactive chunk still writes its slot (zeros:
+    // every row has c_t = 0).
     const int g = c / s.G, j = c % s.G;
+    if (j == 0) s_group = s0;
     const bool last_in_group = j == s.G - 1 || c == D - 1;
     const int* slot_act = s.G == 1 ? act : nullptr;
+    char* dZc = (char*)w.dZ + (s.kmajor ? (s0 - s_group) * s.Vp * s.esz : 0);
 
     GemmParams g1;
     g1.A = Hb + s0 * d * s.esz; g1.lda = d;
@@ -185,13 +201,20 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
       SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
       SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
     }
-    SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
-                    w.dZ, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp, slot_act, str));
-    SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, (char*)w.Ht + j * s.Tcp * s.esz, s.Kg,
-                          s.Tcp, slot_act, str));
+    if (s.kmajor) {
+      SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
+                      dZc, s.Vp, nullptr, 0, 0, slot_act, str));
+    } else {
+      SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
+                      dZc, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp, slot_act, str));
+      SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, (char*)w.Ht + j * s.Tcp * s.esz, s.Kg,
+                            s.Tcp, slot_act, str));
+    }
 
+    // dH_c = dZ_c (W^T)^T over K = Vp: the zero pad of dZ_c (columns V ..
+    // Vp) meets the zero columns of W^T
     GemmParams g2;
-    g2.A = w.dZ; g2.lda = s.Vp;
+    g2.A = dZc; g2.lda = s.Vp;
     g2.B = w.Wt; g2.ldb = s.Vp;
     g2.C = w.part; g2.ldc = d;
     g2.M = (int)Tc; g2.N = (int)d; g2.K = (int)s.Vp;
@@ -204,11 +227,19 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
                           act, str));
 
     if (!last_in_group) continue;
+    // dW += dZ_g^T H_g over the group's tokens [s_group, e0)
     GemmParams g3;
-    g3.A = w.dZt; g3.lda = s.Kg;
-    g3.B = w.Ht; g3.ldb = s.Kg;
+    if (s.kmajor) {
+      g3.A = w.dZ; g3.lda = s.Vp; g3.a_kmajor = 1;
+      g3.B = Hb + s_group * d * s.esz; g3.ldb = d; g3.b_kmajor = 1;
+      g3.K = (int)(e0 - s_group);
+    } else {
+      g3.A = w.dZt; g3.lda = s.Kg;
+      g3.B = w.Ht; g3.ldb = s.Kg;
+      g3.K = (int)((j + 1) * s.Tcp);
+    }
     g3.C = dW; g3.ldc = d;
-    g3.M = (int)V; g3.N = (int)d; g3.K = (int)((j + 1) * s.Tcp);
+    g3.M = (int)V; g3.N = (int)d;
     g3.beta = 1;
     g3.beta_zero = w.prep.beta_zero + g;
     g3.active = w.prep.group_active + g;
