@@ -27,6 +27,7 @@
 // owned by XCD b%8.  Blocks that share an L2 then share operand panels, and
 // with split-K the splits fall on whole XCDs.
 #include "common.h"
+#include <type_traits>
 #include "kernels.h"
 
 namespace sbp {
@@ -257,6 +258,14 @@ __device__ __forceinline__ void dma_x4(const void* g, uint32_t lds) {
                "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+// The same fill with a uniform 64-bit base and a per-lane 32-bit byte offset
+// (scalar-base addressing): the per-instruction address step is then a
+// scalar add, with no vector instructions between the DMAs and the MFMAs.
+__device__ __forceinline__ void dma_x4_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 __device__ __forceinline__ void dma_x1(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g),
                "{m0}"(__builtin_amdgcn_readfirstlane(lds))
@@ -399,14 +408,30 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   const int c_even = kmaj ? c_km : chunk_even * 8;
   const int c_odd = kmaj ? c_km : chunk_odd * 8;
   const uint32_t dst0 = (uint32_t)(opnd * 32768 + (wave & 1) * (kmaj ? 4096 : 16384));
+  // Interior tiles (every row of the tile below lim, every stage below K)
+  // take the scalar-base path: a uniform stage base
+  // X + p0 ld + k0 (row-major) or X + k0 ld + p0 (K-major) plus per-lane byte
+  // offsets that are the same for every stage; other stages the general path
+  // with the zero redirect.  The 32-bit offsets need ld < 2^22.
+  // (decided per wave, for the whole loop: the operand's rows of this tile
+  // all below lim, and K a multiple of 128 so that no stage -- the padded
+  // ones included -- reaches past K)
+  const bool fast_tile = ld < (1 << 22) && p0 + 256 <= lim && p.K % 128 == 0;
+  const uint32_t off_e = kmaj ? (uint32_t)((int64_t)kl * ld + (c_km - p0)) * 2u
+                              : (uint32_t)((int64_t)(rbase + (lane >> 3)) * ld + c_even) * 2u;
+  const uint32_t off_o = kmaj ? off_e : (uint32_t)((int64_t)(rbase + (lane >> 3)) * ld + c_odd) * 2u;
   // the stage's two base addresses (even / odd j) are computed once and
   // kept opaque, so that each instruction adds a uniform offset to one
   struct StageSrc {
     const bf16_t *e, *o;
     int rb, ce, co;
+    const char* sb;  // uniform stage base (scalar-base path)
+    bool fast;
   };
   auto stage_src = [&](int k0) __attribute__((always_inline)) {
     StageSrc q;
+    q.fast = fast_tile;
+    q.sb = reinterpret_cast<const char*>(kmaj ? X + (int64_t)k0 * ld + p0 : X + (int64_t)p0 * ld + k0);
     q.rb = kmaj ? k0 + kl : r0;
     q.ce = c_even + (kmaj ? 0 : k0);
     q.co = c_odd + (kmaj ? 0 : k0);
@@ -415,6 +440,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     q.o = row + q.co;
     asm volatile("" : "+v"(q.e), "+v"(q.o));
     return q;
+  };
+  // uniform byte step of instruction j from the stage base (instruction j
+  // reads what the general path's src_addr(q, j) reads when all lanes are in
+  // range)
+  auto step_of = [&](int j) __attribute__((always_inline)) {
+    return kmaj ? ((int64_t)8 * (j & 3) * ld + 64 * (j >> 2)) * 2 : (int64_t)8 * j * ld * 2;
   };
   auto src_addr = [&](const StageSrc& q, int j) __attribute__((always_inline)) {
     const int ro = kmaj ? 8 * (j & 3) : 8 * j, co = kmaj ? 64 * (j >> 2) : 0;
@@ -427,6 +458,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   };
   // four DMAs whose addresses are all formed first (in distinct registers, so
   // that no address register is rewritten right after its load issues)
+  auto issue_one = [&](uint4* L, const StageSrc& q, int j) __attribute__((always_inline)) {
+    dma_x4(src_addr(q, j), lds_addr(L) + dst_of(j));
+  };
+  auto issue_one_s = [&](uint4* L, const StageSrc& q, int j) __attribute__((always_inline)) {
+    dma_x4_s(q.sb + step_of(j), (j & 1) ? off_o : off_e, lds_addr(L) + dst_of(j));
+  };
   auto issue_four = [&](uint4* L, const StageSrc& q, int j0) __attribute__((always_inline)) {
     const bf16_t* g0 = src_addr(q, j0);
     const bf16_t* g1 = src_addr(q, j0 + 1);
@@ -473,6 +510,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   // does not see the DMAs (inline assembly), so every wait for them is
   // explicit (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
   // lgkmcnt 11:8); vmcnt retires loads in issue order.
+  //
+  // A stage's 16 DMA instructions per wave are issued in two halves, each
+  // spread over 16 MFMAs: instructions 0-7 of stage t+2 right after the
+  // barrier that frees its buffer (under the last k16 step of stage t), and
+  // 8-15 under the first k16 step of stage t+1, followed by the L2 prefetch
+  // of stage t+3.  The vector-memory pipe moves about 64 bytes per clock per
+  // CU, so a whole stage (64 KB) under one 16-MFMA window would stall the
+  // MFMA issue; two windows keep it under half busy.  The second half has
+  // two k16 steps to land before the barrier that waits for it.
   const int nk = ke > kb ? (ke - kb) / BK : 0;
   RingFrag f0, f1;
   if (nk > 0) {
@@ -481,20 +527,44 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(L1, kb + BK);
-    prefetch(kb + min(2, nk - 1) * BK);
+    {
+      const StageSrc q1 = stage_src(kb + min(1, nk - 1) * BK);
+      issue_four(L1, q1, 0);
+      issue_four(L1, q1, 4);
+    }
     ring_load<AKM, BKM>(L0, 0, wm, wn, lane, klo, f0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
-  auto step = [&](const uint4* Lc, const uint4* Ln, uint4* Lrefill, int t) __attribute__((always_inline)) {
+  // 16 MFMAs on fragments f, two DMA instructions (j0 + 2q, j0 + 2q + 1 of
+  // stage q_src) before each group of 4
+  auto mma_dma = [&](auto fast_tag, const RingFrag& f, uint4* Ldst, const StageSrc& qs, int j0)
+                     __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (decltype(fast_tag)::value) {
+        issue_one_s(Ldst, qs, j0 + 2 * q);
+        issue_one_s(Ldst, qs, j0 + 2 * q + 1);
+      } else {
+        issue_one(Ldst, qs, j0 + 2 * q);
+        issue_one(Ldst, qs, j0 + 2 * q + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+        acc[q][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, f.a[q]), __builtin_bit_cast(bf16x8_t, f.b[fn]), acc[q][fn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step = [&](auto fast_tag, const uint4* Lc, uint4* Ln, uint4* Lrefill, int t) __attribute__((always_inline)) {
     // lgkmcnt(0) after each MFMA group: the reads issued before it have long
     // landed, and saying so keeps at most 8 reads outstanding (the counter
     // cannot express waits with more than 15 in flight).
     ring_load<AKM, BKM>(Lc, 1, wm, wn, lane, klo, f1);
-    if constexpr (!kmaj) __builtin_amdgcn_sched_barrier(0);
-    ring_mma(f0, acc);
-    if constexpr (kmaj) interleave_reads<16>();
     __builtin_amdgcn_sched_barrier(0);
+    // second half of stage t+1's fill, then the L2 prefetch of stage t+3
+    mma_dma(fast_tag, f0, Ln, stage_src(kb + min(t + 1, nk - 1) * BK), 8);
+    prefetch(kb + min(t + 3, nk - 1) * BK);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     ring_load<AKM, BKM>(Lc, 2, wm, wn, lane, klo, f0);
     if constexpr (!kmaj) __builtin_amdgcn_sched_barrier(0);
@@ -513,29 +583,25 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // the next stage's first fragments, then the refill DMA spread over the
-    // 16 MFMAs of step 3 (4 DMA instructions per 4 MFMAs) so that the wave
-    // never stalls issuing a burst of DMAs while the matrix unit idles
+    // the next stage's first fragments, then the first half of stage t+2's
+    // fill (into the buffer the barrier just freed) under step 3's MFMAs
     ring_load<AKM, BKM>(Ln, 0, wm, wn, lane, klo, f0);
     __builtin_amdgcn_sched_barrier(0);
-    const StageSrc src = stage_src(kb + min(t + 2, nk - 1) * BK);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      issue_four(Lrefill, src, 4 * q);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-        acc[q][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, f1.a[q]), __builtin_bit_cast(bf16x8_t, f1.b[fn]), acc[q][fn],
-            0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    prefetch(kb + min(t + 3, nk - 1) * BK);
+    mma_dma(fast_tag, f1, Lrefill, stage_src(kb + min(t + 2, nk - 1) * BK), 0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   };
-  for (int it = 0; it < nk; it += 2) {
-    step(L0, L1, L0, it);
-    step(L1, L0, L1, it + 1);
+  // wave-uniform choice of the fill path for the whole loop (both loops run
+  // the same barriers)
+  if (fast_tile) {
+    for (int it = 0; it < nk; it += 2) {
+      step(std::true_type{}, L0, L1, L0, it);
+      step(std::true_type{}, L1, L0, L1, it + 1);
+    }
+  } else {
+    for (int it = 0; it < nk; it += 2) {
+      step(std::false_type{}, L0, L1, L0, it);
+      step(std::false_type{}, L1, L0, L1, it + 1);
+    }
   }
 
   // Epilogue through LDS: each wave parks 32 rows x 128 columns of fp32 (16 KB)
