@@ -535,24 +535,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     ring_load<AKM, BKM>(L0, 0, wm, wn, lane, klo, f0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
-  // 16 MFMAs on fragments f, two DMA instructions (j0 + 2q, j0 + 2q + 1 of
-  // stage q_src) before each group of 4
+  // 16 MFMAs on fragments f with 8 DMA instructions (j0 .. j0 + 7 of the
+  // stage qs describes), one before every second MFMA: a DMA holds the
+  // wave's in-order issue for longer than one MFMA occupies the matrix pipe,
+  // so two MFMAs between DMAs keep the pipe fed
   auto mma_dma = [&](auto fast_tag, const RingFrag& f, uint4* Ldst, const StageSrc& qs, int j0)
                      __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (decltype(fast_tag)::value) {
-        issue_one_s(Ldst, qs, j0 + 2 * q);
-        issue_one_s(Ldst, qs, j0 + 2 * q + 1);
-      } else {
-        issue_one(Ldst, qs, j0 + 2 * q);
-        issue_one(Ldst, qs, j0 + 2 * q + 1);
+    for (int m = 0; m < 16; ++m) {
+      if (m % 2 == 0) {
+        if constexpr (decltype(fast_tag)::value) issue_one_s(Ldst, qs, j0 + m / 2);
+        else issue_one(Ldst, qs, j0 + m / 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-        acc[q][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, f.a[q]), __builtin_bit_cast(bf16x8_t, f.b[fn]), acc[q][fn], 0, 0, 0);
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, f.a[m >> 2]), __builtin_bit_cast(bf16x8_t, f.b[m & 3]), acc[m >> 2][m & 3], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -613,6 +610,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   float beta = (float)p.beta;
   if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
   const bool vec_ok = (p.ldc % 4 == 0) && (EPI != EPI_OUT_RESID || p.ldr % 4 == 0);
+  // tiles wholly inside C (nearly all of them) take straight-line code with
+  // no per-vector bounds checks (wave-uniform)
+  const bool full = vec_ok && m0 + BM <= p.M && n0 + BN <= p.N;
   // All 16 vector passes of a wave's 32-row block are one batch: its old C
   // (read-modify-write) or residual values are loaded before any of its
   // stores, so the 16 loads are in flight together.
@@ -628,6 +628,54 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         W[lr * 128 + fn * 32 + (lane & 31)] = acc[fm][fn][e];
       }
     __builtin_amdgcn_wave_barrier();
+    if (full) {
+      // rows m0 + wm 128 + fm 32 + 2 bq + l / 32, columns n0 + wn 128 + 4 (l % 32)
+      const int64_t rc0 = (int64_t)(m0 + wm * WT + fm * 32 + (lane >> 5));
+      const int c0 = n0 + wn * WT + (lane & 31) * 4;
+      float4 old[16];
+      if constexpr (EPI == EPI_F32_ACC) {
+        if (beta != 0.f) {
+#pragma unroll
+          for (int bq = 0; bq < 16; ++bq)
+            old[bq] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + (rc0 + 2 * bq) * p.ldc + c0);
+        } else {
+#pragma unroll
+          for (int bq = 0; bq < 16; ++bq) old[bq] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      } else if constexpr (EPI == EPI_OUT_RESID) {
+#pragma unroll
+        for (int bq = 0; bq < 16; ++bq) {
+          const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.R) + (rc0 + 2 * bq) * p.ldr + c0);
+          old[bq] = make_float4(bf2f((bf16_t)(r.x & 0xffff)), bf2f((bf16_t)(r.x >> 16)),
+                                bf2f((bf16_t)(r.y & 0xffff)), bf2f((bf16_t)(r.y >> 16)));
+        }
+      }
+#pragma unroll
+      for (int bq = 0; bq < 16; ++bq) {
+        const int lr = bq * 2 + (lane >> 5);
+        const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + (lane & 31) * 4]);
+        float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
+        const int64_t off = (rc0 + 2 * bq) * p.ldc + c0;
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_F32_ACC) {
+          const float4 o = old[bq];
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) =
+              make_float4(v[0] + beta * o.x, v[1] + beta * o.y, v[2] + beta * o.z, v[3] + beta * o.w);
+        } else {
+          if constexpr (EPI == EPI_OUT_RESID) {
+            v[0] += old[bq].x; v[1] += old[bq].y; v[2] += old[bq].z; v[3] += old[bq].w;
+          }
+          uint2 u;
+          u.x = pk_bf16(v[0], v[1]);
+          u.y = pk_bf16(v[2], v[3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.C) + off) = u;
+        }
+      }
+    } else
 #pragma unroll
     for (int it0 = 0; it0 < 16; it0 += BATCH) {
       float4 old[BATCH];
@@ -709,9 +757,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
       const int row = m0 + wm * WT + fm * 32 + lr;
       const int cbase = n0 + wn * WT + hq * 64;
       const float* Wr = &W[lr * 128 + hq * 64];
+      float m = -INFINITY, sx = 0.f;
+      if (full) {
+        // two passes over the 64 staged values (max, then the sum of
+        // exp(x - max)): no column checks and no data-dependent branches
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float4 q = *reinterpret_cast<const float4*>(Wr + ((j + lane) & 15) * 4);
+          m = fmaxf(m, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float4 q = *reinterpret_cast<const float4*>(Wr + ((j + lane) & 15) * 4);
+          sx += (__expf(q.x - m) + __expf(q.y - m)) + (__expf(q.z - m) + __expf(q.w - m));
+        }
+      } else
       // one pass, online: the running sum is rescaled when a float4 raises
       // the running max
-      float m = -INFINITY, sx = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int c4 = (j + lane) & 15;
