@@ -16,6 +16,9 @@ chunked algorithm:
 * ``lmhead.lmhead_ce``      -- LM head + softmax cross-entropy loss and
   gradients dH, dW (skill page, "Implementation": the per-token cross-entropy,
   the softmax-minus-one-hot logits gradient and the linear-layer gradients).
+* ``lmhead.lmhead_logprob`` -- forward-only per-token target log-probability
+  and log-sum-exp, the quantity GRPO and DPO weights are formed from (skill
+  page, "Practical Guidance", "Loss Objectives").
 * ``attention.attn_bwd``    -- causal GQA attention forward and backward.
 * ``layer.layer_bwd``       -- one pre-norm decoder layer, forward and
   backward by the chain rule.
@@ -29,11 +32,11 @@ central finite differences, against independent torch fp64 autograd, against
 closed forms and special cases, and against hand-derived golden values.
 No function here is "parity unpinned".
 """
-from .lmhead import lmhead_ce, lmhead_ce_rows
+from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_logprob, lmhead_logprob_rows
 from .attention import attn_fwd, attn_bwd, attn_bwd_sampled
 from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd
 from . import chunked
 
-__all__ = ["lmhead_ce", "lmhead_ce_rows", "attn_fwd", "attn_bwd",
+__all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
            "attn_bwd_sampled", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
            "rmsnorm_bwd", "chunked"]

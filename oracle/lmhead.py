@@ -31,6 +31,15 @@ Definitions, for tokens t with hidden row h_t, target y_t and weight w_t::
 
 N = 0 (every token ignored) gives L = 0, dH = 0, dW = 0 (reading; a plain
 mean would be 0/0).
+
+Forward-only per-token log-probability (``lmhead_logprob``).  The "Loss
+Objectives" item of "Practical Guidance" names GRPO and DPO beside SFT; both
+weight each token by a quantity formed from the log-probability the model
+assigns to that token (a policy ratio, a sequence log-likelihood), which is
+read here as the plain log-softmax of the logits at the target::
+
+    logprob_t = Z_{t, y_t} - lse_t  = -l_t          (y_t >= 0)
+    logprob_t = lse_t = 0                           (y_t < 0, by convention)
 """
 from __future__ import annotations
 
@@ -136,3 +145,39 @@ def lmhead_ce_rows(H, W, targets, weights, rows, N, reduction="mean_valid"):
         dZ = (c / n)[:, None] * P
     dZ[~valid] = 0.0
     return dZ @ W, ell, np.where(valid, lse, np.nan)
+
+
+def lmhead_logprob(H, W, targets, row_block=None):
+    """Per-token target log-probability and log-sum-exp, unchunked, fp64.
+
+    Returns ``(logprob, lse)``, both [T]: ``logprob[t] = Z_{t,y_t} - lse_t``
+    and ``lse[t] = log sum_v exp(Z_tv)`` for ``y_t >= 0``; both 0 for ignored
+    tokens.  ``row_block`` bounds host memory only (fixed blocks of complete
+    rows, as in ``lmhead_ce``).
+    """
+    H = _as64(H)
+    W = _as64(W)
+    T = H.shape[0]
+    y = np.asarray(targets).astype(np.int64)
+    valid = y >= 0
+    logprob = np.zeros(T)
+    lse_out = np.zeros(T)
+    rb = T if row_block is None else int(row_block)
+    for r0 in range(0, T, rb):
+        r1 = min(T, r0 + rb)
+        Z = H[r0:r1] @ W.T
+        lse = _logsumexp_rows(Z)
+        v = valid[r0:r1]
+        yr = np.where(v, y[r0:r1], 0)
+        z_y = Z[np.arange(r1 - r0), yr]
+        logprob[r0:r1] = np.where(v, z_y - lse, 0.0)
+        lse_out[r0:r1] = np.where(v, lse, 0.0)
+    return logprob, lse_out
+
+
+def lmhead_logprob_rows(H, W, targets, rows):
+    """``lmhead_logprob`` restricted to a sample of rows (each row needs only
+    its own logits), for full-size spot checks.  Returns ``(logprob, lse)``
+    for the given rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return lmhead_logprob(np.asarray(H)[rows], W, np.asarray(targets)[rows])

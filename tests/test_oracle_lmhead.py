@@ -160,3 +160,91 @@ def test_chunk_table_rule():
     for bad in ((5, 0), (5, 6)):
         with pytest.raises(ValueError):
             chunked.chunk_table(*bad)
+
+
+# ---------------------------------------------------------------------------
+# Forward-only per-token log-probability (GRPO / DPO front end)
+
+@pytest.mark.parametrize("case", [c["name"] for c in load_golden("lmhead_logprob_hand.json")["cases"]])
+def test_logprob_hand_worked_golden(case):
+    g = load_golden("lmhead_logprob_hand.json")
+    c = [c for c in g["cases"] if c["name"] == case][0]
+    lp, lse = oracle.lmhead_logprob(ev(g["H"]), ev(g["W"]), np.array(c["targets"]))
+    np.testing.assert_allclose(lp, ev(c["logprob"]), atol=1e-15)
+    np.testing.assert_allclose(lse, ev(c["lse"]), atol=1e-15)
+
+
+def test_logprob_normalises_over_the_vocabulary():
+    # every row's probabilities exp(logprob) over all V possible targets sum
+    # to one, and each is at most one
+    T, d, V = 5, 4, 9
+    rng = np.random.default_rng(21)
+    H = rng.normal(size=(T, d)) * 2.0
+    W = rng.normal(size=(V, d))
+    Hrep = np.repeat(H, V, axis=0)
+    y = np.tile(np.arange(V), T)
+    lp, lse = oracle.lmhead_logprob(Hrep, W, y)
+    assert (lp <= 0).all()
+    np.testing.assert_allclose(np.exp(lp).reshape(T, V).sum(axis=1), 1.0, atol=1e-14)
+    # lse does not depend on the target
+    assert np.ptp(lse.reshape(T, V), axis=1).max() < 1e-13
+
+
+def test_logprob_zero_weight_matrix_is_uniform():
+    T, d, V = 6, 3, 7
+    rng = np.random.default_rng(22)
+    y = rng.integers(0, V, size=T)
+    y[2] = -1
+    lp, lse = oracle.lmhead_logprob(rng.normal(size=(T, d)), np.zeros((V, d)), y)
+    v = y >= 0
+    np.testing.assert_allclose(lp[v], -math.log(V), atol=1e-15)
+    np.testing.assert_allclose(lse[v], math.log(V), atol=1e-15)
+    assert lp[2] == 0.0 and lse[2] == 0.0
+
+
+def test_logprob_against_torch_log_softmax():
+    H, W, y, _ = _rand(T=23, d=6, V=31, seed=23)
+    lp, lse = oracle.lmhead_logprob(H, W, y)
+    Z = torch.from_numpy(H) @ torch.from_numpy(W).T
+    ls = F.log_softmax(Z, dim=1)
+    v = y >= 0
+    ref = ls[torch.arange(len(y)), torch.from_numpy(np.where(v, y, 0))].numpy()
+    np.testing.assert_allclose(lp[v], ref[v], atol=1e-13)
+    np.testing.assert_allclose(lse[v], torch.logsumexp(Z, dim=1).numpy()[v], atol=1e-13)
+    assert (lp[~v] == 0).all() and (lse[~v] == 0).all()
+
+
+def test_logprob_shift_of_all_logits():
+    # a constant added to every logit of a row leaves the log-probability
+    # unchanged and moves lse by the constant: with a column of ones in H,
+    # adding k to that column of W adds k to every logit
+    H, W, y, _ = _rand(T=11, d=5, V=13, seed=24)
+    H[:, 0] = 1.0
+    W2 = W.copy()
+    W2[:, 0] += 3.25
+    lp, lse = oracle.lmhead_logprob(H, W, y)
+    lp2, lse2 = oracle.lmhead_logprob(H, W2, y)
+    v = y >= 0
+    np.testing.assert_allclose(lp2, lp, atol=1e-13)
+    np.testing.assert_allclose(lse2[v], lse[v] + 3.25, atol=1e-13)
+
+
+def test_logprob_is_minus_token_cross_entropy():
+    # the pinned cross-entropy oracle's per-token loss is -logprob
+    H, W, y, w = _rand(T=19, d=6, V=17, seed=25)
+    lp, lse = oracle.lmhead_logprob(H, W, y)
+    _, _, _, tl, lse_ce = oracle.lmhead_ce(H, W, y, w)
+    np.testing.assert_allclose(lp, -tl, atol=1e-14)
+    v = y >= 0
+    np.testing.assert_allclose(lse[v], lse_ce[v], atol=1e-14)
+
+
+def test_logprob_rows_and_blocking():
+    H, W, y, _ = _rand(T=29, d=6, V=19, seed=26)
+    lp, lse = oracle.lmhead_logprob(H, W, y)
+    lpb, lseb = oracle.lmhead_logprob(H, W, y, row_block=4)
+    assert np.abs(lp - lpb).max() < 1e-13 and np.abs(lse - lseb).max() < 1e-13
+    rows = np.array([0, 1, 4, 13, 28])
+    lpr, lser = oracle.lmhead_logprob_rows(H, W, y, rows)
+    np.testing.assert_allclose(lpr, lp[rows], atol=1e-15)
+    np.testing.assert_allclose(lser, lse[rows], atol=1e-15)
