@@ -14,6 +14,10 @@ dominant kernel (timed live with hipEvents on the launch stream through the
 library's kernel timer), and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+
+Workloads (--workload): 0..4 the LM-head, attention and layer configurations
+(1 is the default), 5 the forward-only per-token log-probability on the
+weighted LM-head shapes.
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "backward tokens/sec + peak HBM bytes vs seq len T; % of bf16 MFMA peak"
+METRIC_LOGPROB = "forward per-token log-prob tokens/sec; % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -109,6 +114,27 @@ def lmhead_setup(cfg, dev):
             rows += e - s
     flops = 6.0 * rows * V * d
     return step, flops, inp, n_valid
+
+
+def logprob_setup(cfg, dev):
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    inp = synthetic.workload_inputs(cfg["index"], T=cfg["T"])
+    H, W, tg = inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev)
+    T, d, V, D = cfg["T"], cfg["d"], cfg["V"], cfg["D"]
+    ws = torch.empty(sbp.lmhead_logprob_workspace_size(T, d, V, D, H.dtype), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        return sbp.lmhead_logprob(H, W, tg, D=D, lse=True, workspace=ws)
+
+    y = inp.targets
+    n_valid = int((y >= 0).sum())
+    # algorithmic flops: the logits GEMM, 2 N V d over the rows of chunks that
+    # hold a valid token (fully masked chunks are skipped)
+    rows = sum(e - s for s, e in sbp.chunk_table(T, D) if (y[s:e] >= 0).any())
+    return step, 2.0 * rows * V * d, inp, n_valid
 
 
 def attn_setup(cfg, dev):
@@ -217,6 +243,27 @@ def cpu_baseline_lmhead(inp, cfg, sample):
                       f"(fp64 NumPy, unchunked); {dt:.1f} s"}
 
 
+def cpu_baseline_logprob(inp, cfg, sample):
+    """The log-prob oracle, untouched, on `sample` tokens of the same input,
+    taken from the sequences' unmasked parts (the device skips only chunks
+    with no valid token)."""
+    import numpy as np
+    import torch
+    import oracle
+    import synthetic
+    threads = _blas_threads()
+    y = inp.targets.numpy()
+    rows = np.nonzero(y >= 0)[0][:sample]
+    H = synthetic.to_f64(inp.H[torch.from_numpy(rows)])
+    W = synthetic.to_f64(inp.W)
+    t0 = time.perf_counter()
+    oracle.lmhead_logprob(H, W, y[rows], row_block=1024)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {len(rows)} valid of {cfg['T']} tokens, full V={cfg['V']} and "
+                      f"d={cfg['d']} (fp64 NumPy, unchunked); {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +293,8 @@ def main():
     n_valid = None
     if cfg["kind"] == "lmhead":
         step, flops, inp, n_valid = lmhead_setup(cfg, dev)
+    elif cfg["kind"] == "logprob":
+        step, flops, inp, n_valid = logprob_setup(cfg, dev)
     elif cfg["kind"] == "attn":
         step, flops, inp = attn_setup(cfg, dev)
     else:
@@ -286,6 +335,8 @@ def main():
         for kname in ("gemm_logits", "gemm_dH", "gemm_dW"):
             if kname in prof:
                 prof[kname] = dict(prof[kname], flops=flops * args.steps / 3.0)
+    elif cfg["kind"] == "logprob" and "gemm_logits_lp" in prof:
+        prof["gemm_logits_lp"] = dict(prof["gemm_logits_lp"], flops=flops * args.steps)
     # dominant kernel and its roofline (live hipEvent timing inside the call)
     dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
     name, k = dom
@@ -310,7 +361,7 @@ def main():
                for n, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if cfg["kind"] != "logprob" else METRIC_LOGPROB,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -331,7 +382,9 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        if cfg["kind"] == "lmhead":
+        if cfg["kind"] == "logprob":
+            out["cpu_baseline"] = cpu_baseline_logprob(inp, cfg, args.cpu_sample or 8192)
+        elif cfg["kind"] == "lmhead":
             sample = args.cpu_sample or (4096 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
             out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
         elif cfg["kind"] == "attn":

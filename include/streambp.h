@@ -115,6 +115,33 @@ sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* ta
                                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * 1b. LM head, forward only: per-token target log-probability.
+ *
+ * Passage: skill page, "Practical Guidance", "Loss Objectives" -- StreamBP
+ * serves GRPO and DPO as well as SFT.  Their per-token weights (a policy
+ * ratio, a sequence log-likelihood) are formed from the log-probability the
+ * model gives each target token; the caller forms them from this call's
+ * output and passes them as `weights` to sbp_lmhead_ce_fwd_bwd.  Chunked as
+ * in (1): per chunk the [T_c, V] logits are reduced as they are produced
+ * and never stored whole (with bf16 and d % 128 == 0 they are not written to
+ * memory at all).
+ *
+ *   Z = H W^T,  lse_t = logsumexp(Z_t),  logprob_t = Z_{t,y_t} - lse_t
+ *
+ * H, W, targets  as in (1)
+ * logprob  [T]      fp32 out    logprob_t; 0 for ignored tokens (y_t < 0)
+ * lse      [T]      fp32 out or NULL  lse_t; 0 for ignored tokens
+ * Chunks with no valid token are skipped on the device.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_lmhead_logprob_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,
+                                             int32_t dtype, size_t* bytes);
+
+sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const int32_t* targets,
+                                  int64_t T, int64_t d, int64_t V, int32_t D, int32_t dtype,
+                                  float* logprob, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * 2. Causal GQA attention backward, chunked over queries.
  *
  * Passage: skill page, "Architecture Overview" (causal structure

@@ -9,6 +9,7 @@ not built, or a tensor is not on the GPU, the call raises.
 Names follow ``include/streambp.h``:
 
 * ``lmhead_ce``      -> ``sbp_lmhead_ce_fwd_bwd``
+* ``lmhead_logprob`` -> ``sbp_lmhead_logprob_fwd``
 * ``attn_bwd``       -> ``sbp_attn_bwd_chunked``
 * ``layer_bwd``      -> ``sbp_layer_bwd``
 """
@@ -25,7 +26,8 @@ from . import _lib
 from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, LayerDesc,
                    LayerGrads, LayerWeights, StreamBPError, check, load)
 
-__all__ = ["lmhead_ce", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
+__all__ = ["lmhead_ce", "lmhead_logprob", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
+           "lmhead_logprob_workspace_size",
            "attn_bwd_workspace_size", "layer_bwd_workspace_size", "profile", "load",
            "StreamBPError", "chunk_table"]
 
@@ -105,6 +107,36 @@ def lmhead_ce(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                                     dt, _RED[reduction], int(accumulate), _ptr(loss), _ptr(tl),
                                     _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev)))
     return loss, dH, dW, tl
+
+
+def lmhead_logprob_workspace_size(T, d, V, D, dtype=torch.bfloat16) -> int:
+    out = C.c_size_t(0)
+    check(load().sbp_lmhead_logprob_workspace_size(T, d, V, D, _DT[dtype], C.byref(out)))
+    return out.value
+
+
+def lmhead_logprob(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, D: int = 1,
+                   lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Chunked forward-only per-token target log-probability.
+
+    Returns ``(logprob, lse)``: fp32 [T] each (``lse`` is None unless asked);
+    both are 0 for ignored tokens (target < 0).
+    """
+    lib = load()
+    _dev(H, W, targets)
+    T, d = H.shape
+    V = W.shape[0]
+    if W.shape[1] != d or W.dtype != H.dtype or targets.shape != (T,) or targets.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch")
+    dt = _dtype(H)
+    dev = H.device
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    ls = torch.empty(T, dtype=torch.float32, device=dev) if lse else None
+    nb = lmhead_logprob_workspace_size(T, d, V, D, H.dtype)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
+    check(lib.sbp_lmhead_logprob_fwd(_ptr(H), _ptr(W), _ptr(targets), T, d, V, D, dt, _ptr(lp),
+                                     _ptr(ls), _ptr(ws), ws.numel(), _stream(dev)))
+    return lp, ls
 
 
 # ----------------------------------------------------------------------------

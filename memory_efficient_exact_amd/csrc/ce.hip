@@ -14,6 +14,8 @@
 //               row (wave64 shuffles, then LDS across waves) -> lse, l_t.
 //   ce_merge    the same from the (max, sum-exp) partials that the bf16
 //               logits GEMM writes per 64 columns (no pass over the row).
+//   lp_rows     forward only: logprob = z_y - lse (and lse) per row, from
+//               those partials and the GEMM's target logits, or from Z.
 //   ce_grad     64 x 128 tiles: dZ = (c_t/N)(exp(z - lse) - onehot), written
 //               twice in the GEMM operand layouts -- dZ [T_c, V] (K = V
 //               contiguous for dH = dZ W) and dZ^T [V, T_c] (K = T_c
@@ -97,27 +99,33 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mx;
 }
 
-__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ Z, int64_t ldz,
-                                                       const int32_t* __restrict__ targets,
-                                                       const float* __restrict__ weights, int64_t s0,
-                                                       int64_t V, float* __restrict__ lse_out,
-                                                       float* __restrict__ loss_part,
-                                                       float* __restrict__ token_loss) {
+// Merge the (max, sum-exp) pairs of a 256-thread block (wave64 shuffles, then
+// the four waves through LDS); the result is valid in thread 0.
+__device__ __forceinline__ void block_lse(float& m, float& s) {
   __shared__ float sm[4], ss[4];
-  const int r = blockIdx.x;
-  const int64_t t = s0 + r;
   const int tid = threadIdx.x;
-  const int y = targets[t];
-  if (y < 0) {
-    if (tid == 0) {
-      loss_part[t] = 0.f;
-      if (token_loss) token_loss[t] = 0.f;
-      lse_out[r] = 0.f;
-    }
-    return;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
   }
-  const float* z = Z + (int64_t)r * ldz;
-  float m = -INFINITY, s = 0.f;
+  if ((tid & 63) == 0) {
+    sm[tid >> 6] = m;
+    ss[tid >> 6] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    m = sm[0];
+    s = ss[0];
+    for (int w = 1; w < 4; ++w) lse_merge(m, s, sm[w], ss[w]);
+  }
+}
+
+// Online (max, sum-exp) of this thread's share of a length-V fp32 row.
+__device__ __forceinline__ void row_lse_partial(const float* __restrict__ z, int64_t V, float& m,
+                                                float& s) {
+  const int tid = threadIdx.x;
   const int64_t V4 = V & ~(int64_t)3;
   for (int64_t i = (int64_t)tid * 4; i < V4; i += 1024) {
     const float4 v = *reinterpret_cast<const float4*>(z + i);
@@ -136,21 +144,32 @@ __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__
     }
     s += __expf(v - m);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const float s2 = __shfl_xor(s, o, 64);
-    lse_merge(m, s, m2, s2);
+}
+
+__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ Z, int64_t ldz,
+                                                       const int32_t* __restrict__ targets,
+                                                       const float* __restrict__ weights, int64_t s0,
+                                                       int64_t V, float* __restrict__ lse_out,
+                                                       float* __restrict__ loss_part,
+                                                       float* __restrict__ token_loss) {
+  const int r = blockIdx.x;
+  const int64_t t = s0 + r;
+  const int tid = threadIdx.x;
+  const int y = targets[t];
+  if (y < 0) {
+    if (tid == 0) {
+      loss_part[t] = 0.f;
+      if (token_loss) token_loss[t] = 0.f;
+      lse_out[r] = 0.f;
+    }
+    return;
   }
-  if ((tid & 63) == 0) {
-    sm[tid >> 6] = m;
-    ss[tid >> 6] = s;
-  }
-  __syncthreads();
+  const float* z = Z + (int64_t)r * ldz;
+  float m = -INFINITY, s = 0.f;
+  row_lse_partial(z, V, m, s);
+  block_lse(m, s);
   if (tid == 0) {
-    float M = sm[0], S = ss[0];
-    for (int w = 1; w < 4; ++w) lse_merge(M, S, sm[w], ss[w]);
-    const float lse = M + __logf(S);
+    const float lse = m + __logf(s);
     const float ell = lse - z[y];
     const float w = weights ? weights[t] : 1.f;
     lse_out[r] = lse;
@@ -178,7 +197,6 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
                                                        float* __restrict__ lse_out,
                                                        float* __restrict__ loss_part,
                                                        float* __restrict__ token_loss) {
-  __shared__ float sm[4], ss[4];
   const int r = blockIdx.x;
   const int64_t t = s0 + r;
   const int tid = threadIdx.x;
@@ -196,21 +214,9 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
     const float2 q = parts[(int64_t)r * ldp + i];
     lse_merge(m, sx, q.x, q.y);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const float s2 = __shfl_xor(sx, o, 64);
-    lse_merge(m, sx, m2, s2);
-  }
-  if ((tid & 63) == 0) {
-    sm[tid >> 6] = m;
-    ss[tid >> 6] = sx;
-  }
-  __syncthreads();
+  block_lse(m, sx);
   if (tid == 0) {
-    float M = sm[0], S = ss[0];
-    for (int w = 1; w < 4; ++w) lse_merge(M, S, sm[w], ss[w]);
-    const float lse = M + __logf(S);
+    const float lse = m + __logf(sx);
     const float ell = lse - Z[(int64_t)r * ldz + y];
     const float w = weights ? weights[t] : 1.f;
     lse_out[r] = lse;
@@ -225,6 +231,62 @@ sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z
   ProfScope prof("ce_merge", st, 0.0, 8.0 * (double)Tc * nparts);
   hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts, Z, ldz,
                      targets, weights, s, lse, loss_part, token_loss);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+// Per-token target log-probability (forward only): one block per row.
+// PARTS: lse from the logits GEMM's per-64-column partials and the target
+// logit from its target output; otherwise both from the fp32 logits row.
+template <bool PARTS>
+__global__ __launch_bounds__(256) void lp_rows_kernel(const float2* __restrict__ parts, int64_t ldp,
+                                                      int nparts, const float* __restrict__ zt,
+                                                      const float* __restrict__ Z, int64_t ldz,
+                                                      int64_t V, const int32_t* __restrict__ targets,
+                                                      int64_t s0, float* __restrict__ logprob,
+                                                      float* __restrict__ lse_out) {
+  const int r = blockIdx.x;
+  const int64_t t = s0 + r;
+  const int tid = threadIdx.x;
+  const int y = targets[t];
+  if (y < 0) {
+    if (tid == 0) {
+      logprob[t] = 0.f;
+      if (lse_out) lse_out[t] = 0.f;
+    }
+    return;
+  }
+  float m = -INFINITY, sx = 0.f;
+  if constexpr (PARTS) {
+    for (int i = tid; i < nparts; i += 256) {
+      const float2 q = parts[(int64_t)r * ldp + i];
+      lse_merge(m, sx, q.x, q.y);
+    }
+  } else {
+    row_lse_partial(Z + (int64_t)r * ldz, V, m, sx);
+  }
+  block_lse(m, sx);
+  if (tid == 0) {
+    const float lse = m + __logf(sx);
+    const float zy = PARTS ? zt[r] : Z[(int64_t)r * ldz + y];
+    logprob[t] = zy - lse;
+    if (lse_out) lse_out[t] = lse;
+  }
+}
+
+sbp_status lp_rows(const float2* parts, int64_t ldp, int nparts, const float* zt, const float* Z,
+                   int64_t ldz, int64_t V, const int32_t* targets, int64_t s, int64_t Tc,
+                   float* logprob, float* lse_out, hipStream_t st) {
+  if (Tc <= 0) return SBP_OK;
+  if (parts) {
+    ProfScope prof("lp_rows", st, 0.0, 8.0 * (double)Tc * nparts);
+    hipLaunchKernelGGL(lp_rows_kernel<true>, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts,
+                       zt, Z, ldz, V, targets, s, logprob, lse_out);
+  } else {
+    ProfScope prof("lp_rows", st, 0.0, 4.0 * (double)Tc * V);
+    hipLaunchKernelGGL(lp_rows_kernel<false>, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts,
+                       zt, Z, ldz, V, targets, s, logprob, lse_out);
+  }
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

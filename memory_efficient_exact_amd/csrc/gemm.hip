@@ -628,7 +628,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         W[lr * 128 + fn * 32 + (lane & 31)] = acc[fm][fn][e];
       }
     __builtin_amdgcn_wave_barrier();
-    if (full) {
+    if constexpr (EPI == EPI_LSE_TGT) {
+      // statistics and target values only: C is not written
+    } else if (full) {
       // rows m0 + wm 128 + fm 32 + 2 bq + l / 32, columns n0 + wn 128 + 4 (l % 32)
       const int64_t rc0 = (int64_t)(m0 + wm * WT + fm * 32 + (lane >> 5));
       const int c0 = n0 + wn * WT + (lane & 31) * 4;
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         }
       }
     }
-    if constexpr (EPI == EPI_F32_LSE) {
+    if constexpr (EPI == EPI_F32_LSE || EPI == EPI_LSE_TGT) {
       // (max, sum-exp) of each row's 64-column quarters of the wave's block,
       // one lane per (row l % 32, quarter l / 32), read from the staged block
       // in a lane-rotated order (conflict-free); no cross-lane traffic.
@@ -789,6 +791,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         if (m != -INFINITY) sx += __expf(x0 - m) + __expf(x1 - m) + __expf(x2 - m) + __expf(x3 - m);
       }
       if (row < p.M) p.row_stats[(int64_t)row * p.ld_stats + 4 * tn + 2 * wn + hq] = make_float2(m, sx);
+      if constexpr (EPI == EPI_LSE_TGT) {
+        // the one lane whose quarter holds the row's target column
+        if (row < p.M) {
+          const int y = p.row_target[row];
+          if (y >= cbase && y < cbase + 64 && y < p.N) p.target_out[row] = Wr[y - cbase];
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -799,6 +808,9 @@ static void launch_bf16_ring_layout(int epi, const GemmParams& p, int grid, hipS
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
     case EPI_F32_LSE: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32_LSE, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_LSE_TGT:
+      if constexpr (!AKM) hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_LSE_TGT, false, false>), dim3(grid), dim3(256), 0, st, p);
+      break;
     case EPI_F32_ACC: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32_ACC, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
     case EPI_OUT: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_OUT, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
     case EPI_OUT_RESID: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_OUT_RESID, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
@@ -840,15 +852,18 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
   const double flops = 2.0 * p.M * p.N * (double)p.K;
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
   const double bytes = ((double)p.M * p.K + (double)p.N * p.K) * esz +
-                       (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : 4.0 * p.k_split);
-  // (the row statistics of EPI_F32_LSE add 8 bytes per 128 output columns)
+                       (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : epi == EPI_LSE_TGT ? 0.0 : 4.0 * p.k_split);
+  // (the row statistics of EPI_F32_LSE / EPI_LSE_TGT add 8 bytes per 64 output columns)
   ProfScope prof(name, st, flops, bytes);
   const bool ring_ok = dtype == SBP_BF16 && (p.K % 8 == 0 || p.a_kmajor) &&
                        p.k_per_split % 128 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
                        (!p.a_kmajor || p.lda >= round_up(p.M, 8)) &&
                        (!p.b_kmajor || p.ldb >= round_up(p.N, 8));
-  if (epi == EPI_F32_LSE && !(tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 && p.row_stats))
+  if ((epi == EPI_F32_LSE || epi == EPI_LSE_TGT) &&
+      !(tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 && p.row_stats))
     return set_error(SBP_ERR_UNSUPPORTED, "row-statistics epilogue needs the bf16 ring GEMM without split-K");
+  if (epi == EPI_LSE_TGT && (p.a_kmajor || !p.row_target || !p.target_out))
+    return set_error(SBP_ERR_UNSUPPORTED, "target-value epilogue needs row-major operands and its row arrays");
   if ((p.a_kmajor || p.b_kmajor) && !(tile == GEMM_TILE_RING && ring_ok && p.a_kmajor == p.b_kmajor))
     return set_error(SBP_ERR_UNSUPPORTED, "K-major GEMM operands need the bf16 ring GEMM, both K-major");
   if (dtype == SBP_BF16) {

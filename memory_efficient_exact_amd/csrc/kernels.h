@@ -8,7 +8,11 @@ namespace sbp {
 // ---------------------------------------------------------------- GEMM ----
 // EPI_F32_LSE: as EPI_F32, plus the (max, sum-exp) of every 64-column quarter
 // of a tile row (columns < N) into row_stats (ring kernel only, k_split 1).
-enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_F32_LSE = 5 };
+// EPI_LSE_TGT: the row statistics of EPI_F32_LSE and, for each row m with
+// 0 <= row_target[m] < N, its value at that column into target_out[m]; C is
+// not written (ring kernel only, k_split 1).
+enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_F32_LSE = 5,
+       EPI_LSE_TGT = 6 };
 enum { GEMM_TILE_128 = 0, GEMM_TILE_RING = 3 };
 
 struct GemmParams {
@@ -33,8 +37,10 @@ struct GemmParams {
   // between k-rows (rows are read in 8-element chunks up to that bound);
   // the two flags must be equal
   int a_kmajor = 0, b_kmajor = 0;
-  float2* row_stats = nullptr;     // EPI_F32_LSE: [M, ld_stats], entry 4 tn + quarter
+  float2* row_stats = nullptr;     // EPI_F32_LSE, EPI_LSE_TGT: [M, ld_stats], entry 4 tn + quarter
   int64_t ld_stats = 0;
+  const int32_t* row_target = nullptr;  // EPI_LSE_TGT: [M] column of each row (< 0: none)
+  float* target_out = nullptr;          // EPI_LSE_TGT: [M]
   int tiles_m = 0, tiles_n = 0;    // filled by the launcher
 };
 
@@ -67,6 +73,14 @@ sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* target
                    const float* weights, const float* inv_norm, const float* lse, int64_t s,
                    int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,
                    int64_t ldgt, int64_t Tcp, const int* active, hipStream_t st);
+// Per-token target log-probability of rows [s, s+Tc) of one chunk:
+// logprob[s+r] = z_r[y] - lse_r and (if lse_out is not NULL) lse_out[s+r] =
+// lse_r, both 0 where y = targets[s+r] < 0.  From the logits GEMM's
+// per-64-column partials and target logits zt[r] when parts is not NULL,
+// else from a pass over the fp32 logits Z [Tc, ldz] (V columns).
+sbp_status lp_rows(const float2* parts, int64_t ldp, int nparts, const float* zt, const float* Z,
+                   int64_t ldz, int64_t V, const int32_t* targets, int64_t s, int64_t Tc,
+                   float* logprob, float* lse_out, hipStream_t st);
 sbp_status loss_reduce(const float* loss_part, int64_t T, const float* inv_norm, float* loss,
                        hipStream_t st);
 

@@ -105,6 +105,33 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   return round_up((int64_t)P.off, 256);
 }
 
+// Forward-only log-probability call: per chunk either the statistics
+// partials and target logits of the logits GEMM (no logits written) or, where
+// that epilogue does not apply, the fp32 logits of the chunk.
+struct LpWs {
+  float* Z;       // [T_c, Vp] fp32, unfused path only
+  float2* parts;  // [T_c, nparts], fused path only
+  float* zt;      // [T_c] target logits, fused path only
+  LmPrep prep;
+};
+
+size_t lp_plan(const LmShape& s, char* base, LpWs* w) {
+  WsPlan P;
+  P.base = base;
+  LpWs x;
+  x.Z = s.fused_stats ? nullptr : (float*)P.take(sizeof(float) * s.Tcm * s.Vp);
+  x.parts = s.fused_stats ? (float2*)P.take(sizeof(float2) * s.Tcm * s.nparts) : nullptr;
+  x.zt = s.fused_stats ? (float*)P.take(sizeof(float) * s.Tcm) : nullptr;
+  x.prep.n_valid = (int*)P.take(sizeof(int));
+  x.prep.inv_norm = (float*)P.take(sizeof(float));
+  x.prep.none_active = (int*)P.take(sizeof(int));
+  x.prep.chunk_active = (int*)P.take(sizeof(int) * s.D);
+  x.prep.group_active = (int*)P.take(sizeof(int) * s.D);
+  x.prep.beta_zero = (int*)P.take(sizeof(int) * s.D);
+  if (w) *w = x;
+  return round_up((int64_t)P.off, 256);
+}
+
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 sbp_status lm_check_sizes(int64_t T, int64_t d, int64_t V, int32_t D, int32_t dtype) {
@@ -250,4 +277,68 @@ extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const 
   SBP_TRY(loss_reduce(w.loss_part, T, w.prep.inv_norm, loss, str));
 #undef SBP_TRY
   return SBP_OK;
+}
+
+extern "C" sbp_status sbp_lmhead_logprob_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,
+                                                       int32_t dtype, size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = lm_check_sizes(T, d, V, D, dtype);
+  if (st != SBP_OK) return st;
+  *bytes = lp_plan(lm_shape(T, d, V, D, dtype), nullptr, nullptr);
+  return SBP_OK;
+}
+
+// Per chunk c = [s, e): the logits Z_c = H_c W^T are formed by the GEMM and
+// reduced on the fly -- bf16 with d % 128 == 0: the GEMM epilogue writes only
+// the per-64-column (max, sum-exp) partials and each row's target logit, and
+// lp_rows merges them; otherwise Z_c is written in fp32 and lp_rows passes
+// over it.  Chunks without a valid token are skipped (their rows are zeros).
+extern "C" sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const int32_t* targets,
+                                             int64_t T, int64_t d, int64_t V, int32_t D,
+                                             int32_t dtype, float* logprob, float* lse, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  clear_error();
+  sbp_status st = lm_check_sizes(T, d, V, D, dtype);
+  if (st != SBP_OK) return st;
+  if (!H || !W || !targets || !logprob)
+    return set_error(SBP_ERR_INVALID_ARG, "H, W, targets and logprob must be non-NULL");
+  if (misaligned(H) || misaligned(W) || misaligned(targets) || misaligned(logprob) || misaligned(lse) ||
+      misaligned(ws))
+    return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const LmShape s = lm_shape(T, d, V, D, dtype);
+  const size_t need = lp_plan(s, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  LpWs w;
+  lp_plan(s, (char*)ws, &w);
+  hipStream_t str = (hipStream_t)stream;
+  const char* Hb = (const char*)H;
+  sbp_status r = lm_prep(targets, T, D, 1, SBP_SUM, 0, w.prep, str);
+  for (int32_t c = 0; c < D && r == SBP_OK; ++c) {
+    int64_t s0, e0;
+    chunk_bounds(T, D, c, &s0, &e0);
+    const int64_t Tc = e0 - s0;
+    GemmParams g;
+    g.A = Hb + s0 * d * s.esz; g.lda = d;
+    g.B = W; g.ldb = d;
+    g.M = (int)Tc; g.N = (int)V; g.K = (int)d;
+    g.active = w.prep.chunk_active + c;
+    g.m_fastest = 1;
+    if (s.fused_stats) {
+      g.row_stats = w.parts;
+      g.ld_stats = s.nparts;
+      g.row_target = targets + s0;
+      g.target_out = w.zt;
+      r = gemm_nt(dtype, EPI_LSE_TGT, g, GEMM_TILE_RING, str, "gemm_logits_lp");
+      if (r == SBP_OK)
+        r = lp_rows(w.parts, s.nparts, s.nparts, w.zt, nullptr, 0, V, targets, s0, Tc, logprob, lse, str);
+    } else {
+      g.C = w.Z; g.ldc = s.Vp;
+      r = gemm_nt(dtype, EPI_F32, g, GEMM_TILE_RING, str, "gemm_logits_lp");
+      if (r == SBP_OK)
+        r = lp_rows(nullptr, 0, 0, nullptr, w.Z, s.Vp, V, targets, s0, Tc, logprob, lse, str);
+    }
+  }
+  return r;
 }

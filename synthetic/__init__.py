@@ -162,7 +162,8 @@ def to_f64(t: Optional[torch.Tensor]):
 
 
 # ---------------------------------------------------------------------------
-# The five workloads (index 0..4), seed = 1000 + index.
+# The five workloads (index 0..4), seed = 1000 + index, and the forward-only
+# log-probability workload (index 5).
 # ---------------------------------------------------------------------------
 WORKLOADS = {
     0: dict(kind="lmhead", name="lmhead_ce_f32_T256_d64_V512_D4",
@@ -176,6 +177,11 @@ WORKLOADS = {
     4: dict(kind="lmhead", name="lmhead_ce_weighted_bf16_T131072x8seq_d3584_V152064_D32",
             T=131072, d=3584, V=152064, D=32, dtype="bf16", w_std=0.02,
             n_seq=8, masked_frac=0.25, weighted=True),
+    # forward-only per-token log-probability on the weighted workload's
+    # shapes (the front end that forms its token weights); not a backward
+    5: dict(kind="logprob", name="lmhead_logprob_bf16_T131072x8seq_d3584_V152064_D32",
+            T=131072, d=3584, V=152064, D=32, dtype="bf16", w_std=0.02,
+            n_seq=8, masked_frac=0.25),
 }
 
 
@@ -185,7 +191,7 @@ def workload_inputs(index: int, **override):
     cfg.update(override)
     seed = cfg.get("seed", 1000 + index)
     kind = cfg["kind"]
-    if kind == "lmhead":
+    if kind in ("lmhead", "logprob"):
         return lmhead_inputs(cfg["T"], cfg["d"], cfg["V"], cfg["dtype"], seed,
                              w_std=cfg.get("w_std"), n_seq=cfg.get("n_seq", 1),
                              masked_frac=cfg.get("masked_frac", 0.0),

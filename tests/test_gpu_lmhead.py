@@ -175,3 +175,90 @@ def test_full_size_weighted_T131072_V152064():
     rows = np.concatenate([[0, 4095, 4096, 16383, 16384 + 4096, 131071],
                            rng.integers(0, 131072, 26)])
     _full_size(4, rows)
+
+
+# ---- forward-only per-token log-probability (sbp_lmhead_logprob_fwd) -----
+def _lp_run(inp, D):
+    dev = torch.device("cuda:0")
+    lp, ls = sbp.lmhead_logprob(inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev), D=D, lse=True)
+    torch.cuda.synchronize()
+    return lp.cpu().numpy(), ls.cpu().numpy()
+
+
+def _lp_check(inp, D, dtype):
+    lp, ls = _lp_run(inp, D)
+    rlp, rls = oracle.lmhead_logprob(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                     inp.targets.numpy())
+    e_lp, e_ls = normwise(lp, rlp), normwise(ls, rls)
+    assert e_lp <= TOL[dtype], e_lp
+    assert e_ls <= TOL[dtype], e_ls
+    ign = inp.targets.numpy() < 0
+    assert (lp[ign] == 0).all() and (ls[ign] == 0).all()
+    return e_lp, e_ls
+
+
+@pytest.mark.parametrize("dtype,T,d,V,D", [
+    ("bf16", 1000, 256, 5000, 3),    # fused epilogue; ragged row and column tiles
+    ("bf16", 2048, 512, 8192, 8),    # whole tiles only
+    ("bf16", 517, 136, 2063, 1),     # d % 128 != 0: fp32 logits pass
+    ("bf16", 300, 128, 130, 300),    # D = T, V < one tile
+    ("f32", 333, 68, 1000, 3),
+    ("f32", 256, 64, 512, 4),
+])
+def test_logprob_parity(dtype, T, d, V, D):
+    inp = synthetic.lmhead_inputs(T, d, V, dtype, seed=7 * T + d + V + D,
+                                  w_std=0.05 if dtype == "bf16" else None, ignore_frac=0.1)
+    _lp_check(inp, D, dtype)
+
+
+def test_logprob_target_in_last_partial_column_block():
+    # every target in the last, partial 64-column quarter of the last tile
+    inp = synthetic.lmhead_inputs(640, 256, 1000, "bf16", seed=31, w_std=0.05)
+    inp.targets[:] = torch.randint(960, 1000, (640,), generator=torch.Generator().manual_seed(3),
+                                   dtype=torch.int32)
+    _lp_check(inp, 2, "bf16")
+
+
+def test_logprob_masked_chunks_and_D_invariance():
+    # packed sequences with masked prompts: D = 32 skips every fourth chunk
+    inp = synthetic.lmhead_inputs(8 * 128, 128, 3000, "bf16", seed=32, w_std=0.05, n_seq=8,
+                                  masked_frac=0.25)
+    lp32, ls32 = _lp_run(inp, 32)
+    _lp_check(inp, 32, "bf16")
+    lp1, ls1 = _lp_run(inp, 1)
+    # chunking changes only the GEMM's tile edges (and so the order in which
+    # a row's statistics are merged), not the result beyond fp32 rounding
+    assert normwise(lp32, lp1) <= 1e-5 and normwise(ls32, ls1) <= 1e-5
+
+
+def test_logprob_is_minus_token_loss():
+    inp = synthetic.lmhead_inputs(1024, 256, 4000, "bf16", seed=33, w_std=0.05, ignore_frac=0.1)
+    lp, _ = _lp_run(inp, 4)
+    _, _, _, tl = _run(inp, 4)
+    assert normwise(-lp, tl.cpu().numpy()) <= 1e-6
+
+
+def test_logprob_all_ignored():
+    inp = synthetic.lmhead_inputs(256, 128, 512, "bf16", seed=34, w_std=0.05)
+    inp.targets[:] = -1
+    lp, ls = _lp_run(inp, 4)
+    assert (lp == 0).all() and (ls == 0).all()
+
+
+def test_logprob_full_size_T131072_V152064():
+    # the forward log-prob workload at its full size and chunking, sampled rows
+    cfg = synthetic.WORKLOADS[5]
+    inp = synthetic.workload_inputs(5)
+    lp, ls = _lp_run(inp, cfg["D"])
+    y = inp.targets.numpy()
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([[0, 4095, 4096, 16383, 16384 + 4096, 131071],
+                           rng.integers(0, 131072, 26)])
+    rlp, rls = oracle.lmhead_logprob_rows(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W), y,
+                                          rows)
+    assert normwise(lp[rows], rlp) <= 2e-2
+    assert normwise(ls[rows], rls) <= 2e-2
+    valid = y >= 0
+    # a probability is at most one; ignored rows are zeros
+    assert lp[valid].max() <= 1e-4
+    assert (lp[~valid] == 0).all() and (ls[~valid] == 0).all()
