@@ -383,7 +383,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         if cfg["kind"] == "logprob":
-            out["cpu_baseline"] = cpu_baseline_logprob(inp, cfg, args.cpu_sample or 8192)
+            out["cpu_baseline"] = cpu_baseline_logprob(inp, cfg, args.cpu_sample or 12288)
         elif cfg["kind"] == "lmhead":
             sample = args.cpu_sample or (4096 if cfg["V"] * cfg["d"] > 1e8 else min(T, 4096))
             out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
