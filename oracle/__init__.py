@@ -19,7 +19,8 @@ chunked algorithm:
 * ``lmhead.lmhead_logprob`` -- forward-only per-token target log-probability
   and log-sum-exp, the quantity GRPO and DPO weights are formed from (skill
   page, "Practical Guidance", "Loss Objectives").
-* ``attention.attn_bwd``    -- causal GQA attention forward and backward.
+* ``attention.attn_bwd``    -- causal GQA attention forward and backward;
+  ``attn_bwd_packed`` the same over packed independent sequences.
 * ``layer.layer_bwd``       -- one pre-norm decoder layer, forward and
   backward by the chain rule.
 * ``chunked``               -- a separate fp64 *chunked* evaluation of the
@@ -33,10 +34,10 @@ closed forms and special cases, and against hand-derived golden values.
 No function here is "parity unpinned".
 """
 from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_logprob, lmhead_logprob_rows
-from .attention import attn_fwd, attn_bwd, attn_bwd_sampled
+from .attention import attn_fwd, attn_bwd, attn_bwd_sampled, attn_bwd_packed
 from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd
 from . import chunked
 
 __all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
-           "attn_bwd_sampled", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
+           "attn_bwd_sampled", "attn_bwd_packed", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
            "rmsnorm_bwd", "chunked"]

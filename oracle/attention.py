@@ -21,6 +21,13 @@ Definitions, per batch row b and query head h with kv = h // G, scale s::
     dK_kv += s dS^T Q_h
 
 Layout: token-major, Q/dO/dQ [B, T, Hq, dh], K/V/dK/dV [B, T, Hkv, dh].
+
+Packed sequences (``attn_bwd_packed``): several independent sequences laid
+end to end in one row of T tokens, sequence n holding tokens
+[cu[n], cu[n+1]).  "Practical Guidance" asks that attention masks hold
+across chunk boundaries; the reading for packed data is that a query sees
+only keys of its own sequence at or before it, so the packed result is,
+sequence by sequence, the causal attention above on that sequence alone.
 """
 from __future__ import annotations
 
@@ -153,3 +160,31 @@ def attn_bwd_sampled(Q, K, V, dO, scale, b, h_list, q_rows, k_rows):
         dK_s[kv] = dKs
         dV_s[kv] = dVs
     return dQ_s, dK_s, dV_s
+
+
+def attn_bwd_packed(Q, K, V, dO, scale, cu_seqlens):
+    """Causal GQA attention over packed sequences (one batch row).
+
+    ``cu_seqlens`` holds the sequence boundaries 0 = cu[0] <= ... <= cu[n] = T;
+    query i sees key j iff both lie in the same sequence and j <= i.  Each
+    sequence is an independent causal attention, so the result is
+    ``attn_bwd`` of every slice [cu[n], cu[n+1]) placed back in the row.
+    Returns ``(dQ, dK, dV, O, LSE)`` like ``attn_bwd``.
+    """
+    Q, K, V, dO = _as64(Q), _as64(K), _as64(V), _as64(dO)
+    B, T, Hq, Hkv, dh, G = _check(Q, K, V)
+    cu = [int(c) for c in cu_seqlens]
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("packed attention needs B = 1 and 0 = cu[0] <= ... <= cu[-1] = T")
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    O = np.zeros_like(Q)
+    LSE = np.zeros((B, T, Hq))
+    for a, b in zip(cu, cu[1:]):
+        if b == a:
+            continue
+        sl = slice(a, b)
+        r = attn_bwd(Q[:, sl], K[:, sl], V[:, sl], dO[:, sl], scale)
+        dQ[:, sl], dK[:, sl], dV[:, sl], O[:, sl], LSE[:, sl] = r
+    return dQ, dK, dV, O, LSE

@@ -133,3 +133,80 @@ def test_sampled_matches_full():
     for kv in (0, 1):
         np.testing.assert_allclose(dKs[kv], dK[1, kr, kv], atol=1e-13)
         np.testing.assert_allclose(dVs[kv], dV[1, kr, kv], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Packed independent sequences (block-diagonal causal mask)
+
+def _packed_mask(cu, T):
+    seq = np.zeros(T, dtype=np.int64)
+    for n, (a, b) in enumerate(zip(cu, cu[1:])):
+        seq[a:b] = n
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (j <= i) & (seq[:, None] == seq[None, :])
+
+
+@pytest.mark.parametrize("cu,Hq,Hkv", [([0, 5, 6, 13, 19], 4, 2), ([0, 19], 2, 2),
+                                        ([0, 1, 2, 3, 10, 19], 3, 1), ([0, 4, 4, 19], 4, 4)])
+def test_packed_against_torch_sdpa_with_block_mask(cu, Hq, Hkv):
+    Q, K, V, dO = _rand(B=1, T=19, Hq=Hq, Hkv=Hkv, dh=8, seed=len(cu) + Hq)
+    s = 0.41
+    mask = torch.tensor(_packed_mask(cu, 19))
+    tq, tk, tv = (torch.tensor(a.transpose(0, 2, 1, 3), requires_grad=True) for a in (Q, K, V))
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=s,
+                                         enable_gqa=(Hq != Hkv))
+    out.backward(torch.tensor(dO.transpose(0, 2, 1, 3)))
+    dQ, dK, dV, O, _ = oracle.attn_bwd_packed(Q, K, V, dO, s, cu)
+    tr = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(O, tr(out), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dQ, tr(tq.grad), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dK, tr(tk.grad), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dV, tr(tv.grad), rtol=1e-11, atol=1e-12)
+
+
+def test_packed_finite_differences():
+    cu = [0, 3, 4, 9]
+    Q, K, V, dO = _rand(B=1, T=9, Hq=2, Hkv=1, dh=3, seed=41)
+    s = 0.6
+    dQ, dK, dV, _, _ = oracle.attn_bwd_packed(Q, K, V, dO, s, cu)
+    mask = _packed_mask(cu, 9)
+
+    def f(q, k, v):
+        # <dO, O> with the block-diagonal causal mask written out directly
+        tot = 0.0
+        for h in range(2):
+            S = s * (q[0, :, h] @ k[0, :, 0].T)
+            S = np.where(mask, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            tot += float(((P @ v[0, :, 0]) * dO[0, :, h]).sum())
+        return tot
+
+    h = 1e-6
+    for which, A, G in ((0, Q, dQ), (1, K, dK), (2, V, dV)):
+        fd = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            ap, am = [Q, K, V], [Q, K, V]
+            Ap, Am = A.copy(), A.copy()
+            Ap[idx] += h
+            Am[idx] -= h
+            ap[which], am[which] = Ap, Am
+            fd[idx] = (f(*ap) - f(*am)) / (2 * h)
+        assert np.abs(fd - G).max() <= 1e-7 * max(1.0, np.abs(G).max())
+
+
+def test_packed_one_sequence_is_causal_and_cross_sequence_independent():
+    Q, K, V, dO = _rand(B=1, T=12, seed=42)
+    a = oracle.attn_bwd_packed(Q, K, V, dO, 0.5, [0, 12])
+    b = oracle.attn_bwd(Q, K, V, dO, 0.5)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # changing the second sequence leaves the first one's gradients alone
+    cu = [0, 5, 12]
+    r1 = oracle.attn_bwd_packed(Q, K, V, dO, 0.5, cu)
+    K2 = K.copy()
+    K2[:, 5:] += 1.0
+    r2 = oracle.attn_bwd_packed(Q, K2, V, dO, 0.5, cu)
+    for x, y in zip(r1[:3], r2[:3]):
+        np.testing.assert_array_equal(x[:, :5], y[:, :5])
