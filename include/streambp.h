@@ -175,6 +175,40 @@ sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const void* V, con
                                 float* dV, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 2b. Causal GQA attention backward over packed independent sequences.
+ *
+ * Passage: skill page, "Practical Guidance" -- attention masks must hold
+ * across chunk boundaries; with several sequences packed end to end in one
+ * row (the packed-batch layout of long-sequence training) the reading is
+ * that a query sees only keys of its own sequence at or before it.  Same
+ * computation, chunking and outputs as (2) with B = 1, and the mask
+ *
+ *   key j visible to query i  iff  cu[n] <= j <= i  for the n with
+ *                                  cu[n] <= i < cu[n+1]
+ *
+ * Key blocks that no query of a chunk sees are skipped, so the work falls
+ * with the sequence lengths (block-diagonal, not full causal).
+ *
+ * cu_seqlens [nseq+1] int32 (device)  sequence boundaries,
+ *                               0 = cu[0] <= cu[1] <= ... <= cu[nseq] = T;
+ *                               empty sequences are allowed.  Other
+ *                               contents are a caller error, not checked:
+ *                               results are then unspecified, but every
+ *                               access stays in bounds.
+ * nseq     number of sequences, >= 1
+ * Q, K, V, dO, O, lse, dQ, dK, dV   as in (2) with B = 1
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_attn_bwd_packed_workspace_size(int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
+                                              int32_t D, int32_t dtype, size_t* bytes);
+
+sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V, const void* dO,
+                               const void* O, const float* lse, const int32_t* cu_seqlens,
+                               int32_t nseq, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
+                               float scale, int32_t D, int32_t dtype, int32_t accumulate,
+                               void* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * 3. One pre-norm decoder layer, streamed backward.
  *
  * Passage: skill page, "Implementation" -- the streaming layer backward

@@ -10,7 +10,7 @@ Names follow ``include/streambp.h``:
 
 * ``lmhead_ce``      -> ``sbp_lmhead_ce_fwd_bwd``
 * ``lmhead_logprob`` -> ``sbp_lmhead_logprob_fwd``
-* ``attn_bwd``       -> ``sbp_attn_bwd_chunked``
+* ``attn_bwd``       -> ``sbp_attn_bwd_chunked`` (``sbp_attn_bwd_packed`` with ``cu_seqlens``)
 * ``layer_bwd``      -> ``sbp_layer_bwd``
 """
 from __future__ import annotations
@@ -27,7 +27,7 @@ from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, Laye
                    LayerGrads, LayerWeights, StreamBPError, check, load)
 
 __all__ = ["lmhead_ce", "lmhead_logprob", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
-           "lmhead_logprob_workspace_size",
+           "lmhead_logprob_workspace_size", "attn_bwd_packed_workspace_size",
            "attn_bwd_workspace_size", "layer_bwd_workspace_size", "profile", "load",
            "StreamBPError", "chunk_table"]
 
@@ -146,19 +146,33 @@ def attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, dtype=torch.bfloat16) -> int:
     return out.value
 
 
+def attn_bwd_packed_workspace_size(T, Hq, Hkv, dh, D, dtype=torch.bfloat16) -> int:
+    out = C.c_size_t(0)
+    check(load().sbp_attn_bwd_packed_workspace_size(T, Hq, Hkv, dh, D, _DT[dtype], C.byref(out)))
+    return out.value
+
+
 def attn_bwd(Q, K, V, dO, D: int = 1, scale: Optional[float] = None, O=None, lse=None,
              dK: Optional[torch.Tensor] = None, dV: Optional[torch.Tensor] = None,
-             accumulate: bool = False, workspace: Optional[torch.Tensor] = None):
+             accumulate: bool = False, workspace: Optional[torch.Tensor] = None,
+             cu_seqlens: Optional[torch.Tensor] = None):
     """Chunked causal GQA attention backward.  Returns ``(dQ, dK, dV)``;
-    dK/dV are fp32.  Layout [B, T, heads, dh]."""
+    dK/dV are fp32.  Layout [B, T, heads, dh].
+
+    ``cu_seqlens`` (int32 [nseq + 1] on the GPU, B = 1): packed independent
+    sequences [cu[n], cu[n+1]); a query then sees only keys of its own
+    sequence (``sbp_attn_bwd_packed``)."""
     lib = load()
-    _dev(Q, K, V, dO, O, lse, dK, dV)
+    _dev(Q, K, V, dO, O, lse, dK, dV, cu_seqlens)
     B, T, Hq, dh = Q.shape
     Hkv = K.shape[2]
     if K.shape != (B, T, Hkv, dh) or V.shape != K.shape or dO.shape != Q.shape:
         raise ValueError("shape mismatch")
     if not (Q.dtype == K.dtype == V.dtype == dO.dtype):
         raise ValueError("dtype mismatch")
+    if cu_seqlens is not None and (B != 1 or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                                   or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be int32 [nseq + 1] with B = 1")
     dt = _dtype(Q)
     dev = Q.device
     if scale is None:
@@ -168,11 +182,21 @@ def attn_bwd(Q, K, V, dO, D: int = 1, scale: Optional[float] = None, O=None, lse
         dK = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
     if dV is None:
         dV = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
-    nb = attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype)
+    if cu_seqlens is None:
+        nb = attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype)
+    else:
+        nb = attn_bwd_packed_workspace_size(T, Hq, Hkv, dh, D, Q.dtype)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
-    check(lib.sbp_attn_bwd_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(O), _ptr(lse), B, T,
-                                   Hq, Hkv, dh, float(scale), D, dt, int(accumulate), _ptr(dQ),
-                                   _ptr(dK), _ptr(dV), _ptr(ws), ws.numel(), _stream(dev)))
+    if cu_seqlens is None:
+        check(lib.sbp_attn_bwd_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(O), _ptr(lse), B,
+                                       T, Hq, Hkv, dh, float(scale), D, dt, int(accumulate),
+                                       _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), ws.numel(),
+                                       _stream(dev)))
+    else:
+        check(lib.sbp_attn_bwd_packed(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(O), _ptr(lse),
+                                      _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, Hq, Hkv, dh,
+                                      float(scale), D, dt, int(accumulate), _ptr(dQ), _ptr(dK),
+                                      _ptr(dV), _ptr(ws), ws.numel(), _stream(dev)))
     return dQ, dK, dV
 
 

@@ -44,6 +44,9 @@ SIGNATURES = {
     "sbp_attn_bwd_workspace_size": (i32, [i64, i64, i32, i32, i32, i32, i32, C.POINTER(sz)]),
     "sbp_attn_bwd_chunked": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,
                                    i32, i32, vp, vp, vp, vp, sz, vp]),
+    "sbp_attn_bwd_packed_workspace_size": (i32, [i64, i32, i32, i32, i32, i32, C.POINTER(sz)]),
+    "sbp_attn_bwd_packed": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
+                                  i32, i32, vp, vp, vp, vp, sz, vp]),
     "sbp_layer_bwd_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
     "sbp_layer_bwd": (i32, [C.POINTER(LayerDesc), vp, vp, C.POINTER(LayerWeights), i32, i32,
                             vp, C.POINTER(LayerGrads), vp, sz, vp]),

@@ -34,6 +34,12 @@ struct AttnArgs {
   int s, e;          // chunk [s, e)
   float scale;
   int beta;          // dK/dV: 1 = add into, 0 = overwrite
+  // Packed independent sequences (B = 1 only): token t belongs to the
+  // sequence [seq_lo[t], seq_hi[t]) (seq_lo[t] <= t < seq_hi[t] <= T), and
+  // query i sees key j iff seq_lo[i] <= j <= i.  NULL: the whole row is one
+  // sequence.
+  const int* seq_lo = nullptr;
+  const int* seq_hi = nullptr;
 };
 
 // Per query chunk [a.s, a.e): forward statistics (LSE always; Delta when
@@ -49,5 +55,9 @@ sbp_status attn_delta(const AttnArgs& a, const void* O, const float* lse_src, in
 // so that a 64-row fetch starting at any 64-aligned row stays in bounds.
 inline int64_t attn_stats_pitch(int64_t Tcm) { return round_up(Tcm, 64) + 64; }
 sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st);
+// seq_lo / seq_hi [T] of packed sequences from their boundaries cu[0..nseq]
+// (clamped so that seq_lo[t] <= t < seq_hi[t] <= T whatever cu holds).
+sbp_status attn_seq_bounds(const int32_t* cu, int nseq, int64_t T, int* seq_lo, int* seq_hi,
+                           hipStream_t st);
 
 }  // namespace sbp

@@ -192,6 +192,30 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
   return *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + ks * 16 + g * 8);
 }
 
+// Key range of a wave of 32 queries [qw, qw + 32) (forward and dQ):
+// kfirst is the first key any query of the block sees, klo this lane's own
+// first key, [wlo, whi] the first keys of the wave's first and last query.
+// kind(k0) classifies the 64-key tile [k0, k0 + 64) for the wave: 0 none of
+// its keys is seen, 1 every query sees every key, 2 a mask is needed.
+struct SeqRange {
+  int kfirst, klo, wlo, whi, qw;
+  __device__ __forceinline__ int kind(int k0) const {
+    if (k0 > qw + 31 || k0 + 63 < wlo) return 0;
+    return (k0 + 63 <= qw && k0 >= whi) ? 1 : 2;
+  }
+};
+__device__ __forceinline__ SeqRange seq_range(const AttnArgs& a, int q0, int qw, int qcol) {
+  SeqRange r{0, 0, 0, 0, qw};
+  if (a.seq_lo) {
+    const int last = a.e - 1;  // rows past the chunk take its last query's bounds
+    r.kfirst = a.seq_lo[min(q0, last)];
+    r.klo = a.seq_lo[min(qcol, last)];
+    r.wlo = a.seq_lo[min(qw, last)];
+    r.whi = a.seq_lo[min(qw + 31, last)];
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Forward statistics.  Block: 4 waves, 128 queries (32 per wave), one q head.
 // Key/value tiles of 64 rows are double-buffered in two distinct LDS arrays
@@ -199,9 +223,9 @@ __device__ __forceinline__ uint4 glb_frag(const bf16_t* __restrict__ p, int64_t 
 // tile t+1 is fetched while tile t is used.
 // ---------------------------------------------------------------------------
 template <int DH, bool MASK>
-__device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
-                                         float c2, const uint4 (&qf)[DH / 16], float& m, float& l,
-                                         f32x16_t (&ot)[DH / 32]) {
+__device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol,
+                                         int klo, int lane, float c2, const uint4 (&qf)[DH / 16], float& m,
+                                         float& l, f32x16_t (&ot)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
   f32x16_t st[2];
 #pragma unroll
@@ -210,14 +234,15 @@ __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, c
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) st[kb] = mma(lo.row_frag(kt, kb * 32, ks), qf[ks], st[kb]);
   }
-  // scale, mask (key > query), online softmax along the keys (rows)
+  // scale, mask (key > query, or key before the query's sequence start klo),
+  // online softmax along the keys (rows)
   float mt = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + kb * 32 + crow(e, lane);
-      const float v = (!MASK || key <= qcol) ? st[kb][e] * c2 : -INFINITY;
+      const float v = (!MASK || (key <= qcol && key >= klo)) ? st[kb][e] * c2 : -INFINITY;
       st[kb][e] = v;
       mt = fmaxf(mt, v);
     }
@@ -225,7 +250,9 @@ __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, c
   // Lazy rescale: the running max m only moves (and O, l are rescaled) when
   // some lane's tile max exceeds it by more than 8 (base 2); otherwise P is
   // taken against the stale m and stays <= 2^8 (exact in the fp32 sums, the
-  // same relative precision in bf16).  LSE = m + log2 l either way.
+  // same relative precision in bf16).  LSE = m + log2 l either way.  m starts
+  // finite (-1e30), so a query none of whose keys a tile shows (packed
+  // sequences) gets p = exp2(-inf) = 0, not NaN.
   const bool raise = __ballot(mt > m + 8.f) != 0;
   float ls = 0.f;
   if (raise) {  // wave-uniform
@@ -287,29 +314,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   f32x16_t ot[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) ot[i] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
+  float m = -1e30f, l = 0.f;
   const float c2 = a.scale * kLog2e;
 
-  const int kend = min(q0 + 128, a.e);              // keys [0, kend)
-  const int ntiles = (kend + 63) / 64;
+  // keys [kfirst, kend): packed sequences start at the sequence of the
+  // block's first query; klo is this lane's own lower key bound, [wlo, whi]
+  // the range of the wave's (seq_lo is non-decreasing)
+  const SeqRange sr = seq_range(a, q0, qw, qcol);
+  const int kend = min(q0 + 128, a.e);
+  const int ntiles = (kend + 63) / 64, t0 = sr.kfirst / 64;
   auto issue = [&](char* kd, char* vd, int t) {
     const int k0 = t * 64;
     dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
     dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
   };
-  issue(K0, V0, 0);
-  for (int t = 0; t < ntiles; t += 2) {
+  issue(K0, V0, t0);
+  for (int t = t0; t < ntiles; t += 2) {
     dma_barrier();  // tile t landed; everyone is done with the other buffer
     issue(K1, V1, min(t + 1, ntiles - 1));
-    // only tiles that reach past the wave's first query need the causal mask
-    if (t * 64 + 63 <= qw) fwd_tile<DH, false>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
-    else if (t * 64 <= qw + 31) fwd_tile<DH, true>(lo, K0, V0, t * 64, qcol, lane, c2, qf, m, l, ot);
+    // only tiles that reach past the wave's first query (or, packed, start
+    // before its last query's sequence) need the mask
+    switch (sr.kind(t * 64)) {
+      case 1: fwd_tile<DH, false>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, qf, m, l, ot); break;
+      case 2: fwd_tile<DH, true>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, qf, m, l, ot); break;
+      default: break;
+    }
     dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
-    if (t + 1 < ntiles && (t + 1) * 64 + 63 <= qw)
-      fwd_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
-    else if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      fwd_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, qf, m, l, ot);
+    if (t + 1 < ntiles) switch (sr.kind((t + 1) * 64)) {
+      case 1: fwd_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, qf, m, l, ot); break;
+      case 2: fwd_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, qf, m, l, ot); break;
+      default: break;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   if (qcol >= a.e) return;
@@ -412,7 +448,7 @@ __device__ __forceinline__ void dma_tile64_w8(char* lds, const bf16_t* __restric
 template <int DH>
 __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int krow,
                                           const char* qt, const char* ot, const float* ls,
-                                          const float* dl, int qrow, int q0, int kcol, int e, int lane,
+                                          const float* dl, int qrow, int q0, int kcol, int qlim, int lane,
                                           float c2, bool mask, f32x16_t (&dk)[DH / 32],
                                           f32x16_t (&dv)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
@@ -452,9 +488,10 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, 
       if (mask) {  // wave-uniform: a scalar branch
         asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
         // statistics rows past the chunk are padding (any value): select, do
-        // not multiply, so that they cannot leak in
+        // not multiply, so that they cannot leak in.  qlim: the end of the
+        // chunk or of the key's sequence, whichever comes first
         const int q = q0 + r0 + i;
-        const bool on = kcol <= q && q < e;
+        const bool on = kcol <= q && q < qlim;
         p = on ? p : 0.f;
         g = on ? g : 0.f;
       }
@@ -517,10 +554,17 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
     dv[i] = f32x16_t{};
   }
   const float c2 = a.scale * kLog2e;
+  // Queries that see a key j: [j, qlim(j)), qlim the end of the chunk or,
+  // packed, of j's sequence (non-decreasing in j).  qlim of this lane's key,
+  // and of the wave's first and last key.
+  auto qlim_of = [&](int j) { return a.seq_hi ? min(a.e, a.seq_hi[min(j, a.T - 1)]) : a.e; };
+  const int qlim = qlim_of(kcol), wq_lo = qlim_of(kw), wq_hi = qlim_of(kw + 31);
   // query tiles s + 64 j that reach the block's keys (queries >= kbase)
   const int j0 = kbase > a.s ? (kbase - a.s) / 64 : 0;
-  const int nqt = (a.e - a.s + 63) / 64 - j0;
+  const int nqt = (qlim_of(kbase + 127) - a.s + 63) / 64 - j0;
   const int n = nqt > 0 ? nqt * a.G : 0;
+  // a block whose keys no query of the chunk sees has nothing to add
+  if (n == 0 && a.beta) return;
   // K, V of the block's keys (rows past T fetch row T - 1; those keys are
   // masked and never written)
   const int kvalid = a.T - kbase;
@@ -545,11 +589,12 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
   auto qstart = [&](int it) { return a.s + (j0 + it % nqt) * 64; };
   auto tile = [&](const char* qt, const char* ot, const float* ls, const float* dl, int it) {
     const int q0 = qstart(it), qw = q0 + qrow;
-    // only the wave's queries at or after its keys; those wholly after them
-    // and inside the chunk need no mask
-    if (qw + 31 >= kw)
-      dkdv_tile<DH>(lo, Kt, Vt, kg * 32, qt, ot, ls, dl, qrow, q0, kcol, a.e, lane, c2,
-                    !(qw >= kw + 31 && qw + 32 <= a.e), dk, dv);
+    // only the wave's queries at or after its keys and before the last
+    // key's limit; those wholly after the keys and before every key's limit
+    // need no mask
+    if (qw + 31 >= kw && qw < wq_hi)
+      dkdv_tile<DH>(lo, Kt, Vt, kg * 32, qt, ot, ls, dl, qrow, q0, kcol, qlim, lane, c2,
+                    !(qw >= kw + 31 && qw + 32 <= wq_lo), dk, dv);
   };
   if (n > 0) issue(Q0, O0, L0, E0, 0);
   for (int it = 0; it < n; it += 2) {
@@ -614,8 +659,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
 // 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
 template <int DH, bool MASK>
-__device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol, int lane,
-                                        float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
+__device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol,
+                                        int klo, int lane, float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
                                         const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32]) {
   constexpr int NB = DH / 32, KS = DH / 16;
   f32x16_t st[2], dpt[2];
@@ -634,7 +679,7 @@ __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, co
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0 + kb * 32 + crow(e, lane);
-      const float p = (!MASK || key <= qcol) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
+      const float p = (!MASK || (key <= qcol && key >= klo)) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
       dpt[kb][e] = p * (dpt[kb][e] - dl);
     }
   // dQ[q, dh] += dS[q, key] K[key, dh]
@@ -683,25 +728,30 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NB; ++i) dq[i] = f32x16_t{};
 
+  const SeqRange sr = seq_range(a, q0, qw, qcol);
   const int kend = min(q0 + 128, a.e);
-  const int ntiles = (kend + 63) / 64;
+  const int ntiles = (kend + 63) / 64, t0 = sr.kfirst / 64;
   auto issue = [&](char* kd, char* vd, int t) {
     const int k0 = t * 64;
     dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
     dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
   };
-  issue(K0, V0, 0);
-  for (int t = 0; t < ntiles; t += 2) {
+  issue(K0, V0, t0);
+  for (int t = t0; t < ntiles; t += 2) {
     dma_barrier();
     issue(K1, V1, min(t + 1, ntiles - 1));
-    if (t * 64 + 63 <= qw) dq_tile<DH, false>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
-    else if (t * 64 <= qw + 31) dq_tile<DH, true>(lo, K0, V0, t * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    switch (sr.kind(t * 64)) {
+      case 1: dq_tile<DH, false>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      case 2: dq_tile<DH, true>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      default: break;
+    }
     dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
-    if (t + 1 < ntiles && (t + 1) * 64 + 63 <= qw)
-      dq_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
-    else if (t + 1 < ntiles && (t + 1) * 64 <= qw + 31)
-      dq_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, lane, c2, lse2, dl, qf, of, dq);
+    if (t + 1 < ntiles) switch (sr.kind((t + 1) * 64)) {
+      case 1: dq_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      case 2: dq_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      default: break;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries
@@ -773,6 +823,34 @@ sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st) {
   return SBP_OK;
 }
 
+// seq_lo[t], seq_hi[t]: bounds of the packed sequence holding token t, the
+// last n with cu[n] <= t by bisection over cu[0 .. nseq - 1]; clamped so
+// that seq_lo[t] <= t < seq_hi[t] <= T for any cu.
+__global__ __launch_bounds__(256) void seq_bounds_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                         int64_t T, int* __restrict__ lo,
+                                                         int* __restrict__ hi) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int a = 0, b = nseq;  // the answer lies in [a, b)
+  while (b - a > 1) {
+    const int m = (a + b) >> 1;
+    if (cu[m] <= t) a = m;
+    else b = m;
+  }
+  const int64_t l = cu[a], h = cu[a + 1];
+  lo[t] = (int)(l < 0 ? 0 : (l > t ? t : l));
+  hi[t] = (int)(h <= t ? t + 1 : (h > T ? T : h));
+}
+
+sbp_status attn_seq_bounds(const int32_t* cu, int nseq, int64_t T, int* seq_lo, int* seq_hi,
+                           hipStream_t st) {
+  ProfScope prof("attn_seq_bounds", st, 0.0, 8.0 * T);
+  hipLaunchKernelGGL(seq_bounds_kernel, dim3((unsigned)cdiv(T, 256)), dim3(256), 0, st, cu, nseq, T,
+                     seq_lo, seq_hi);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
 namespace {
 
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
@@ -800,6 +878,72 @@ size_t attn_ws(int64_t B, int64_t T, int32_t Hq, int32_t dh, int32_t D, int32_t 
   return round_up((int64_t)P.off, 256);
 }
 
+// as attn_ws for B = 1, then seq_lo and seq_hi [T] int32, each 256-aligned
+size_t packed_ws(int64_t T, int32_t Hq, int32_t dh, int32_t D, int32_t dtype) {
+  return attn_ws(1, T, Hq, dh, D, dtype) + 2 * round_up((int64_t)sizeof(int) * T, 256);
+}
+
+// Both entry points: argument checks, then per query chunk in reverse order
+// the forward statistics (or Delta from a given O) and the backward.
+sbp_status attn_run(const void* Q, const void* K, const void* V, const void* dO, const void* O,
+                    const float* lse, const int32_t* cu, int32_t nseq, int64_t B, int64_t T,
+                    int32_t Hq, int32_t Hkv, int32_t dh, float scale, int32_t D, int32_t dtype,
+                    int32_t accumulate, void* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                    hipStream_t str) {
+  sbp_status st = attn_check(B, T, Hq, Hkv, dh, D, dtype);
+  if (st != SBP_OK) return st;
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
+    return set_error(SBP_ERR_INVALID_ARG, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
+  if ((O == nullptr) != (lse == nullptr))
+    return set_error(SBP_ERR_INVALID_ARG, "O and lse must be given together or not at all");
+  if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) || misaligned(O) ||
+      misaligned(lse) || misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(ws))
+    return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return set_error(SBP_ERR_INVALID_ARG, "scale must be positive and finite");
+  const size_t need = cu ? packed_ws(T, Hq, dh, D, dtype) : attn_ws(B, T, Hq, dh, D, dtype);
+  if (!ws || ws_bytes < need)
+    return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  const int64_t Lp = attn_stats_pitch(max_chunk_len(T, D));
+  WsPlan P;
+  P.base = (char*)ws;
+  float* w_lse = (float*)P.take(sizeof(float) * B * Lp * Hq);
+  float* w_dl = (float*)P.take(sizeof(float) * B * Lp * Hq);
+  int* seq_lo = nullptr;
+  int* seq_hi = nullptr;
+  if (cu) {
+    seq_lo = (int*)P.take(sizeof(int) * T);
+    seq_hi = (int*)P.take(sizeof(int) * T);
+    st = attn_seq_bounds(cu, nseq, T, seq_lo, seq_hi, str);
+    if (st != SBP_OK) return st;
+  }
+  for (int32_t c = D - 1; c >= 0; --c) {
+    int64_t s0, e0;
+    chunk_bounds(T, D, c, &s0, &e0);
+    AttnArgs a;
+    a.Q = (const bf16_t*)Q; a.K = (const bf16_t*)K; a.V = (const bf16_t*)V;
+    a.dO = (const bf16_t*)dO; a.O = nullptr; a.dQ = (bf16_t*)dQ; a.dK = dK; a.dV = dV;
+    a.ldq = (int64_t)Hq * dh; a.lddq = a.ldq; a.q_bs = T * a.ldq; a.qoff = 0;
+    a.T = (int)T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.s = (int)s0; a.e = (int)e0;
+    a.scale = scale;
+    // the last chunk (processed first) reaches every key: it overwrites
+    a.beta = (accumulate || c != D - 1) ? 1 : 0;
+    a.delta = w_dl; a.dl_sb = (int64_t)Hq * Lp; a.dl_sh = Lp; a.dl_st = 1;
+    a.lse = w_lse; a.lse_sb = (int64_t)Hq * Lp; a.lse_sh = Lp; a.lse_st = 1;
+    a.seq_lo = seq_lo; a.seq_hi = seq_hi;
+    if (lse) {
+      // caller's O and LSE ([B, T, Hq]): Delta, and LSE copied into the chunk layout
+      st = attn_delta(a, O, lse, T * Hq, Hq, dh, (int)B, str);
+    } else {
+      st = attn_fwd(a, dh, (int)B, str);
+    }
+    if (st != SBP_OK) return st;
+    st = attn_bwd_chunk(a, dh, (int)B, str);
+    if (st != SBP_OK) return st;
+  }
+  return SBP_OK;
+}
+
 }  // namespace
 }  // namespace sbp
 
@@ -823,48 +967,32 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
                                            int32_t accumulate, void* dQ, float* dK, float* dV,
                                            void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  sbp_status st = attn_check(B, T, Hq, Hkv, dh, D, dtype);
+  return attn_run(Q, K, V, dO, O, lse, nullptr, 0, B, T, Hq, Hkv, dh, scale, D, dtype, accumulate,
+                  dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" sbp_status sbp_attn_bwd_packed_workspace_size(int64_t T, int32_t Hq, int32_t Hkv,
+                                                         int32_t dh, int32_t D, int32_t dtype,
+                                                         size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = attn_check(1, T, Hq, Hkv, dh, D, dtype);
   if (st != SBP_OK) return st;
-  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
-    return set_error(SBP_ERR_INVALID_ARG, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
-  if ((O == nullptr) != (lse == nullptr))
-    return set_error(SBP_ERR_INVALID_ARG, "O and lse must be given together or not at all");
-  if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) || misaligned(O) ||
-      misaligned(lse) || misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(ws))
-    return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  if (!(scale > 0.f) || !(scale < 1e30f)) return set_error(SBP_ERR_INVALID_ARG, "scale must be positive and finite");
-  const size_t need = attn_ws(B, T, Hq, dh, D, dtype);
-  if (!ws || ws_bytes < need)
-    return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-  hipStream_t str = (hipStream_t)stream;
-  const int64_t Lp = attn_stats_pitch(max_chunk_len(T, D));
-  WsPlan P;
-  P.base = (char*)ws;
-  float* w_lse = (float*)P.take(sizeof(float) * B * Lp * Hq);
-  float* w_dl = (float*)P.take(sizeof(float) * B * Lp * Hq);
-  for (int32_t c = D - 1; c >= 0; --c) {
-    int64_t s0, e0;
-    chunk_bounds(T, D, c, &s0, &e0);
-    AttnArgs a;
-    a.Q = (const bf16_t*)Q; a.K = (const bf16_t*)K; a.V = (const bf16_t*)V;
-    a.dO = (const bf16_t*)dO; a.O = nullptr; a.dQ = (bf16_t*)dQ; a.dK = dK; a.dV = dV;
-    a.ldq = (int64_t)Hq * dh; a.lddq = a.ldq; a.q_bs = T * a.ldq; a.qoff = 0;
-    a.T = (int)T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
-    a.s = (int)s0; a.e = (int)e0;
-    a.scale = scale;
-    // the last chunk (processed first) reaches every key: it overwrites
-    a.beta = (accumulate || c != D - 1) ? 1 : 0;
-    a.delta = w_dl; a.dl_sb = (int64_t)Hq * Lp; a.dl_sh = Lp; a.dl_st = 1;
-    a.lse = w_lse; a.lse_sb = (int64_t)Hq * Lp; a.lse_sh = Lp; a.lse_st = 1;
-    if (lse) {
-      // caller's O and LSE ([B, T, Hq]): Delta, and LSE copied into the chunk layout
-      st = attn_delta(a, O, lse, T * Hq, Hq, dh, (int)B, str);
-    } else {
-      st = attn_fwd(a, dh, (int)B, str);
-    }
-    if (st != SBP_OK) return st;
-    st = attn_bwd_chunk(a, dh, (int)B, str);
-    if (st != SBP_OK) return st;
-  }
+  *bytes = packed_ws(T, Hq, dh, D, dtype);
   return SBP_OK;
+}
+
+extern "C" sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V,
+                                          const void* dO, const void* O, const float* lse,
+                                          const int32_t* cu_seqlens, int32_t nseq, int64_t T,
+                                          int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                                          int32_t D, int32_t dtype, int32_t accumulate, void* dQ,
+                                          float* dK, float* dV, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  clear_error();
+  if (!cu_seqlens) return set_error(SBP_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
+  if (nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (misaligned(cu_seqlens)) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  return attn_run(Q, K, V, dO, O, lse, cu_seqlens, nseq, 1, T, Hq, Hkv, dh, scale, D, dtype,
+                  accumulate, dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
 }

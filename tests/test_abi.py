@@ -159,3 +159,66 @@ def test_layer_workspace_is_chunk_sized():
         sizes.append(out.value)
     # MLP activations are per chunk: D = 16 needs far less than D = 1
     assert sizes[1] < sizes[0] / 3
+
+
+def _packed_call(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dO=FAKE, O=None, lse=None, cu=FAKE, nseq=3, T=64, Hq=4,
+             Hkv=2, dh=64, scale=0.125, D=2, dt=1, acc=0, dQ=FAKE, dK=FAKE, dV=FAKE, ws=FAKE,
+             wsb=1 << 40, st=None)
+    a.update(kw)
+    return sbp.load().sbp_attn_bwd_packed(a["Q"], a["K"], a["V"], a["dO"], a["O"], a["lse"],
+                                          a["cu"], a["nseq"], a["T"], a["Hq"], a["Hkv"], a["dh"],
+                                          a["scale"], a["D"], a["dt"], a["acc"], a["dQ"], a["dK"],
+                                          a["dV"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(cu=MIS), _lib.SBP_ERR_INVALID_ARG),
+    (dict(nseq=0), _lib.SBP_ERR_INVALID_ARG),
+    (dict(D=0), _lib.SBP_ERR_INVALID_ARG),
+    (dict(dh=80), _lib.SBP_ERR_UNSUPPORTED),
+    (dict(lse=FAKE), _lib.SBP_ERR_INVALID_ARG),    # lse without O
+    (dict(dV=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(wsb=16), _lib.SBP_ERR_WORKSPACE),
+])
+def test_packed_attn_argument_errors(kw, code):
+    assert _packed_call(**kw) == code
+
+
+def test_packed_attn_workspace_adds_the_sequence_bounds():
+    lib = sbp.load()
+    st, w = _ws(lib.sbp_attn_bwd_workspace_size, 1, 16384, 32, 8, 128, 8, 1)
+    stp, wp = _ws(lib.sbp_attn_bwd_packed_workspace_size, 16384, 32, 8, 128, 8, 1)
+    assert st == stp == 0
+    assert wp == w + 2 * 16384 * 4
+
+
+def _logprob_call(**kw):
+    a = dict(H=FAKE, W=FAKE, tg=FAKE, T=64, d=64, V=100, D=2, dt=1, lp=FAKE, lse=None, ws=FAKE,
+             wsb=1 << 40, st=None)
+    a.update(kw)
+    return sbp.load().sbp_lmhead_logprob_fwd(a["H"], a["W"], a["tg"], a["T"], a["d"], a["V"],
+                                             a["D"], a["dt"], a["lp"], a["lse"], a["ws"], a["wsb"],
+                                             a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lp=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(tg=None), _lib.SBP_ERR_INVALID_ARG),
+    (dict(lse=MIS), _lib.SBP_ERR_INVALID_ARG),
+    (dict(D=65), _lib.SBP_ERR_INVALID_ARG),
+    (dict(d=60), _lib.SBP_ERR_UNSUPPORTED),
+    (dict(dt=7), _lib.SBP_ERR_INVALID_ARG),
+    (dict(wsb=0), _lib.SBP_ERR_WORKSPACE),
+])
+def test_logprob_argument_errors(kw, code):
+    assert _logprob_call(**kw) == code
+
+
+def test_logprob_workspace_holds_no_logits():
+    lib = sbp.load()
+    # fused bf16 path: per-chunk row partials only, far below one chunk's logits
+    st, w = _ws(lib.sbp_lmhead_logprob_workspace_size, 131072, 3584, 152064, 32, 1)
+    assert st == 0
+    assert w < 4096 * 152064 * 4 / 25

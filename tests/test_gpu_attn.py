@@ -101,3 +101,97 @@ def test_full_size_T16384_sampled():
         assert normwise(dVc[0, k_rows, kv], dVs[kv]) <= TOL, kv
     colsum = np.abs(dK.double().sum(1).cpu().numpy()).max()
     assert colsum <= 1e-2 * np.abs(dKc).max() * math.sqrt(T), colsum
+
+
+# ---- packed independent sequences (sbp_attn_bwd_packed) -------------------
+def _cu(T, cuts):
+    return [0] + list(cuts) + [T]
+
+
+def _gpu_packed(inp, D, cu, **kw):
+    c = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    return _gpu(inp, D, cu_seqlens=c, **kw)
+
+
+def _ref_packed(inp, scale, cu):
+    return oracle.attn_bwd_packed(synthetic.to_f64(inp.Q), synthetic.to_f64(inp.K),
+                                  synthetic.to_f64(inp.V), synthetic.to_f64(inp.dO), scale, cu)
+
+
+def _random_cuts(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(np.arange(1, T), size=n, replace=False).tolist())
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,dh,D,cuts", [
+    (300, 4, 2, 64, 3, [37, 38, 150, 151]),      # length-1 sequences; cuts inside tiles and chunks
+    (700, 8, 2, 128, 4, _random_cuts(700, 6, 1)),
+    (512, 4, 1, 64, 1, [128, 256, 384]),         # tile-aligned sequences, MQA
+    (200, 4, 4, 128, 3, [50, 50, 199]),          # an empty sequence; a last sequence of 1
+    (300, 2, 2, 64, 300, [100, 101]),            # D = T
+    (1000, 4, 2, 128, 7, []),                    # one sequence
+    (1500, 4, 2, 128, 5, _random_cuts(1500, 3, 2)),
+])
+def test_packed_parity(T, Hq, Hkv, dh, D, cuts):
+    inp = synthetic.attn_inputs(1, T, Hq, Hkv, dh, "bf16", seed=3 * T + Hq + dh + D)
+    s = 1.0 / math.sqrt(dh)
+    cu = _cu(T, cuts)
+    dQ, dK, dV = _gpu_packed(inp, D, cu)
+    rQ, rK, rV, _, _ = _ref_packed(inp, s, cu)
+    eq = normwise(dQ.float().cpu().numpy(), rQ)
+    ek = normwise(dK.cpu().numpy(), rK)
+    ev = normwise(dV.cpu().numpy(), rV)
+    assert eq <= TOL and ek <= TOL and ev <= TOL, (eq, ek, ev)
+    # every sequence on its own, so that a leak into a short sequence shows
+    # (a sequence of one token has dK = 0 exactly: its floor is a hundredth
+    # of the whole tensor's scale)
+    gk = dK.cpu().numpy()
+    floor = 1e-2 * np.abs(rK).max()
+    for a, b in zip(cu, cu[1:]):
+        if b > a:
+            err = np.abs(gk[:, a:b] - rK[:, a:b]).max()
+            assert err <= TOL * max(np.abs(rK[:, a:b]).max(), floor), (a, b, err)
+
+
+def test_packed_one_sequence_equals_causal_call():
+    inp = synthetic.attn_inputs(1, 777, 4, 2, 128, "bf16", seed=21)
+    a = _gpu(inp, 3)
+    b = _gpu_packed(inp, 3, [0, 777])
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_packed_given_forward_statistics_and_accumulate():
+    T, Hq, Hkv, dh, D = 640, 4, 2, 64, 4
+    cu = _cu(T, [90, 91, 333])
+    inp = synthetic.attn_inputs(1, T, Hq, Hkv, dh, "bf16", seed=22)
+    s = 1.0 / math.sqrt(dh)
+    rQ, rK, rV, rO, rL = _ref_packed(inp, s, cu)
+    dev = torch.device("cuda:0")
+    O = torch.from_numpy(rO).to(torch.bfloat16).to(dev)
+    L = torch.from_numpy(rL).to(torch.float32).to(dev).contiguous()
+    dQ, dK, dV = _gpu_packed(inp, D, cu, O=O, lse=L)
+    assert normwise(dQ.float().cpu().numpy(), rQ) <= TOL
+    assert normwise(dK.cpu().numpy(), rK) <= TOL
+    assert normwise(dV.cpu().numpy(), rV) <= TOL
+    _, dK2, dV2 = _gpu_packed(inp, 2, cu, dK=dK.clone(), dV=dV.clone(), accumulate=True)
+    assert normwise(dK2.cpu().numpy(), 2 * rK) <= TOL
+    assert normwise(dV2.cpu().numpy(), 2 * rV) <= TOL
+
+
+def test_packed_full_size_T16384_sampled_sequences():
+    # the attention workload's shape with 8 packed sequences of random
+    # lengths, at its chunking; three sequences checked against the oracle
+    cfg = synthetic.WORKLOADS[2]
+    T, D = cfg["T"], cfg["D"]
+    inp = synthetic.workload_inputs(2)
+    cu = _cu(T, _random_cuts(T, 7, 3))
+    dQ, dK, dV = _gpu_packed(inp, D, cu)
+    s = 1.0 / math.sqrt(cfg["dh"])
+    for n in (0, 3, 7):
+        a, b = cu[n], cu[n + 1]
+        sub = synthetic.AttnInputs(inp.Q[:, a:b], inp.K[:, a:b], inp.V[:, a:b], inp.dO[:, a:b])
+        rQ, rK, rV, _, _ = _ref_packed(sub, s, [0, b - a])
+        assert normwise(dQ[:, a:b].float().cpu().numpy(), rQ) <= TOL, n
+        assert normwise(dK[:, a:b].cpu().numpy(), rK) <= TOL, n
+        assert normwise(dV[:, a:b].cpu().numpy(), rV) <= TOL, n
