@@ -162,6 +162,26 @@ def attn_bwd_sampled(Q, K, V, dO, scale, b, h_list, q_rows, k_rows):
     return dQ_s, dK_s, dV_s
 
 
+def _packed_cu(cu_seqlens, B, T):
+    cu = [int(c) for c in cu_seqlens]
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("packed attention needs B = 1 and 0 = cu[0] <= ... <= cu[-1] = T")
+    return cu
+
+
+def attn_fwd_packed(Q, K, V, scale, cu_seqlens):
+    """Forward of ``attn_bwd_packed``: ``(O, LSE)``, each sequence alone."""
+    Q, K, V = _as64(Q), _as64(K), _as64(V)
+    B, T, Hq, Hkv, dh, G = _check(Q, K, V)
+    cu = _packed_cu(cu_seqlens, B, T)
+    O = np.zeros_like(Q)
+    LSE = np.zeros((B, T, Hq))
+    for a, b in zip(cu, cu[1:]):
+        if b > a:
+            O[:, a:b], LSE[:, a:b] = attn_fwd(Q[:, a:b], K[:, a:b], V[:, a:b], scale)
+    return O, LSE
+
+
 def attn_bwd_packed(Q, K, V, dO, scale, cu_seqlens):
     """Causal GQA attention over packed sequences (one batch row).
 
@@ -173,9 +193,7 @@ def attn_bwd_packed(Q, K, V, dO, scale, cu_seqlens):
     """
     Q, K, V, dO = _as64(Q), _as64(K), _as64(V), _as64(dO)
     B, T, Hq, Hkv, dh, G = _check(Q, K, V)
-    cu = [int(c) for c in cu_seqlens]
-    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
-        raise ValueError("packed attention needs B = 1 and 0 = cu[0] <= ... <= cu[-1] = T")
+    cu = _packed_cu(cu_seqlens, B, T)
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)

@@ -32,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attn_bwd, attn_fwd
+from .attention import attn_bwd, attn_bwd_packed, attn_fwd, attn_fwd_packed
 
 
 def _as64(a):
@@ -61,8 +61,10 @@ def _sigmoid(u):
     return 1.0 / (1.0 + np.exp(-u))
 
 
-def layer_fwd(x, w, Hq, Hkv, dh, eps):
-    """Forward of the layer; returns ``(y, cache)``."""
+def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None):
+    """Forward of the layer; returns ``(y, cache)``.  ``cu_seqlens``: the
+    tokens are packed independent sequences (attention stays inside each;
+    every other step is token-wise)."""
     x = _as64(x)
     W = {k: _as64(v) for k, v in w.items()}
     T = x.shape[0]
@@ -71,8 +73,11 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps):
     k = h1 @ W["Wk"].T
     v = h1 @ W["Wv"].T
     scale = 1.0 / np.sqrt(dh)
-    o4, lse = attn_fwd(q.reshape(1, T, Hq, dh), k.reshape(1, T, Hkv, dh),
-                       v.reshape(1, T, Hkv, dh), scale)
+    q4, k4, v4 = q.reshape(1, T, Hq, dh), k.reshape(1, T, Hkv, dh), v.reshape(1, T, Hkv, dh)
+    if cu_seqlens is None:
+        o4, lse = attn_fwd(q4, k4, v4, scale)
+    else:
+        o4, lse = attn_fwd_packed(q4, k4, v4, scale, cu_seqlens)
     o = o4.reshape(T, Hq * dh)
     a = x + o @ W["Wo"].T
     n2, _, _ = rmsnorm_fwd(a, W["g2"], eps)
@@ -85,14 +90,15 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps):
     return y, cache
 
 
-def layer_bwd(x, dy, w, Hq, Hkv, dh, eps):
+def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None):
     """Full (unchunked) backward.  Returns ``(dx, grads, y)``; ``grads`` maps
-    every name of ``w`` (g1, Wq, Wk, Wv, Wo, g2, W1, W3, W2) to its gradient."""
+    every name of ``w`` (g1, Wq, Wk, Wv, Wo, g2, W1, W3, W2) to its gradient.
+    ``cu_seqlens`` as in ``layer_fwd``."""
     x = _as64(x)
     dy = _as64(dy)
     W = {k: _as64(v) for k, v in w.items()}
     T = x.shape[0]
-    y, c = layer_fwd(x, W, Hq, Hkv, dh, eps)
+    y, c = layer_fwd(x, W, Hq, Hkv, dh, eps, cu_seqlens)
     gr = {}
     # MLP: y = a + m W2^T
     gr["W2"] = dy.T @ c["m"]
@@ -111,10 +117,12 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps):
     gr["Wo"] = da.T @ c["o"]
     do = da @ W["Wo"]
     scale = 1.0 / np.sqrt(dh)
-    dq4, dk4, dv4, _, _ = attn_bwd(c["q"].reshape(1, T, Hq, dh),
-                                   c["k"].reshape(1, T, Hkv, dh),
-                                   c["v"].reshape(1, T, Hkv, dh),
-                                   do.reshape(1, T, Hq, dh), scale)
+    args = (c["q"].reshape(1, T, Hq, dh), c["k"].reshape(1, T, Hkv, dh),
+            c["v"].reshape(1, T, Hkv, dh), do.reshape(1, T, Hq, dh), scale)
+    if cu_seqlens is None:
+        dq4, dk4, dv4, _, _ = attn_bwd(*args)
+    else:
+        dq4, dk4, dv4, _, _ = attn_bwd_packed(*args, cu_seqlens)
     dq = dq4.reshape(T, Hq * dh)
     dk = dk4.reshape(T, Hkv * dh)
     dv = dv4.reshape(T, Hkv * dh)

@@ -126,3 +126,53 @@ def test_chunked_equals_unchunked(D):
     assert np.abs(dx - dx2).max() < 1e-12
     for k in NAMES:
         assert np.abs(gr[k] - gr2[k]).max() < 1e-12, k
+
+
+# ---------------------------------------------------------------------------
+# Packed independent sequences
+
+def _torch_layer_masked(x, w, Hq, Hkv, dh, eps, mask):
+    T, d = x.shape
+    h1 = F.rms_norm(x, (d,), weight=w["g1"], eps=eps)
+    q = (h1 @ w["Wq"].T).reshape(T, Hq, dh).transpose(0, 1)[None]
+    k = (h1 @ w["Wk"].T).reshape(T, Hkv, dh).transpose(0, 1)[None]
+    v = (h1 @ w["Wv"].T).reshape(T, Hkv, dh).transpose(0, 1)[None]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=dh ** -0.5,
+                                       enable_gqa=(Hq != Hkv))
+    o = o[0].transpose(0, 1).reshape(T, Hq * dh)
+    a = x + o @ w["Wo"].T
+    n2 = F.rms_norm(a, (d,), weight=w["g2"], eps=eps)
+    m = F.silu(n2 @ w["W1"].T) * (n2 @ w["W3"].T)
+    return a + m @ w["W2"].T
+
+
+def test_packed_against_torch_autograd_with_block_mask():
+    T, d, Hq, Hkv, dh, Fw, eps = 13, 16, 4, 2, 4, 24, 1e-6
+    cu = [0, 4, 5, 13]
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=17)
+    seq = np.repeat(np.arange(3), np.diff(cu))
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    mask = torch.tensor((j <= i) & (seq[:, None] == seq[None, :]))
+    xt = torch.tensor(x, requires_grad=True)
+    wt = {k: torch.tensor(v, requires_grad=True) for k, v in w.items()}
+    yt = _torch_layer_masked(xt, wt, Hq, Hkv, dh, eps, mask)
+    yt.backward(torch.tensor(dy))
+    dx, gr, y = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=cu)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for k in NAMES:
+        np.testing.assert_allclose(gr[k], wt[k].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+
+
+def test_packed_sequences_are_independent():
+    # no upstream gradient on the second sequence: its dx is exactly zero and
+    # every weight gradient is that of the first sequence on its own
+    T, d, Hq, Hkv, dh, Fw, eps = 10, 8, 2, 1, 4, 12, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=18)
+    dy[6:] = 0.0
+    dx, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=[0, 6, 10])
+    dx1, gr1, _ = oracle.layer_bwd(x[:6], dy[:6], w, Hq, Hkv, dh, eps)
+    assert (dx[6:] == 0).all()
+    np.testing.assert_allclose(dx[:6], dx1, rtol=1e-13, atol=1e-15)
+    for k in NAMES:
+        np.testing.assert_allclose(gr[k], gr1[k], rtol=1e-12, atol=1e-15, err_msg=k)
