@@ -17,7 +17,8 @@ library's kernel timer), and the CPU oracle timed on a bounded sample.
 
 Workloads (--workload): 0..4 the LM-head, attention and layer configurations
 (1 is the default), 5 the forward-only per-token log-probability on the
-weighted LM-head shapes.
+weighted LM-head shapes, 6 and 7 the attention and layer workloads over 8
+packed sequences of random lengths.
 """
 from __future__ import annotations
 
@@ -146,16 +147,28 @@ def attn_setup(cfg, dev):
     B, T, Hq, Hkv, dh, D = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["dh"], cfg["D"]
     dK = torch.empty(B, T, Hkv, dh, dtype=torch.float32, device=dev)
     dV = torch.empty_like(dK)
-    ws = torch.empty(sbp.attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype), dtype=torch.uint8,
-                     device=dev)
+    cu = synthetic.workload_cu(cfg["index"], T)
+    if cu is None:
+        nb = sbp.attn_bwd_workspace_size(B, T, Hq, Hkv, dh, D, Q.dtype)
+        cut = None
+    else:
+        nb = sbp.attn_bwd_packed_workspace_size(T, Hq, Hkv, dh, D, Q.dtype)
+        cut = torch.tensor(cu, dtype=torch.int32, device=dev)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     def step():
-        return sbp.attn_bwd(Q, K, V, dO, D=D, dK=dK, dV=dV, workspace=ws)
+        return sbp.attn_bwd(Q, K, V, dO, D=D, dK=dK, dV=dV, workspace=ws, cu_seqlens=cut)
 
     # algorithmic work: 7 causal units of 2*Hq*dh*T(T+1)/2*B (forward
-    # recompute 2, backward 5)
-    unit = 2.0 * Hq * dh * T * (T + 1) / 2 * B
-    return step, 7.0 * unit, inp
+    # recompute 2, backward 5); packed: the pairs of each sequence only
+    return step, 7.0 * attn_unit(Hq, dh, T, B, cu), inp
+
+
+def attn_unit(Hq, dh, T, B=1, cu=None):
+    """One attention unit: 2 Hq dh flops per visible (query, key) pair."""
+    if cu is None:
+        return 2.0 * Hq * dh * T * (T + 1) / 2 * B
+    return sum(2.0 * Hq * dh * (b - a) * (b - a + 1) / 2 for a, b in zip(cu, cu[1:]))
 
 
 def layer_setup(cfg, dev):
@@ -167,17 +180,23 @@ def layer_setup(cfg, dev):
     w = {k: v.to(dev) for k, v in L.w.items()}
     T, d, Hq, Hkv, dh, F, D = (cfg[k] for k in ("T", "d", "Hq", "Hkv", "dh", "F", "D"))
     grads = {k: torch.empty(v.shape, dtype=torch.float32, device=dev) for k, v in w.items()}
-    ws = torch.empty(sbp.layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, x.dtype, L.eps),
-                     dtype=torch.uint8, device=dev)
+    cu = synthetic.workload_cu(cfg["index"], T)
+    if cu is None:
+        nb = sbp.layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, x.dtype, L.eps)
+        cut = None
+    else:
+        nb = sbp.layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, x.dtype, L.eps)
+        cut = torch.tensor(cu, dtype=torch.int32, device=dev)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     def step():
-        return sbp.layer_bwd(x, dy, w, Hq, Hkv, dh, L.eps, D=D, grads=grads, workspace=ws)
+        return sbp.layer_bwd(x, dy, w, Hq, Hkv, dh, L.eps, D=D, grads=grads, workspace=ws,
+                             cu_seqlens=cut)
 
     # algorithmic work: 6 P T for the linear maps (forward recompute 2, backward
-    # 4; P = number of projection weights) plus 7 causal attention units
+    # 4; P = number of projection weights) plus 7 attention units
     P = (Hq * dh) * d + 2 * (Hkv * dh) * d + d * (Hq * dh) + 3 * F * d
-    unit = 2.0 * Hq * dh * T * (T + 1) / 2
-    return step, 6.0 * P * T + 7.0 * unit, L
+    return step, 6.0 * P * T + 7.0 * attn_unit(Hq, dh, T, 1, cu), L
 
 
 def cpu_baseline_layer(L, cfg, sample):
@@ -187,8 +206,11 @@ def cpu_baseline_layer(L, cfg, sample):
     w = {k: synthetic.to_f64(v) for k, v in L.w.items()}
     x = synthetic.to_f64(L.x[:sample])
     dy = synthetic.to_f64(L.dy[:sample])
+    cu = synthetic.workload_cu(cfg["index"], cfg["T"])
+    if cu is not None:  # the sequences that fall inside the sample
+        cu = [c for c in cu if c < sample] + [sample]
     t0 = time.perf_counter()
-    oracle.layer_bwd(x, dy, w, L.Hq, L.Hkv, L.dh, L.eps)
+    oracle.layer_bwd(x, dy, w, L.Hq, L.Hkv, L.dh, L.eps, cu_seqlens=cu)
     dt = time.perf_counter() - t0
     return {"value": sample / dt, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"first {sample} of {cfg['T']} tokens with the full weights (fp64 NumPy, "
@@ -206,8 +228,12 @@ def cpu_baseline_attn(inp, cfg, sample_heads=1):
     K = synthetic.to_f64(inp.K[:, :, :1])
     V = synthetic.to_f64(inp.V[:, :, :1])
     dO = synthetic.to_f64(inp.dO[:, :, :sample_heads])
+    cu = synthetic.workload_cu(cfg["index"], cfg["T"])
     t0 = time.perf_counter()
-    oracle.attn_bwd(Q, K, V, dO, 1.0 / math.sqrt(cfg["dh"]))
+    if cu is None:
+        oracle.attn_bwd(Q, K, V, dO, 1.0 / math.sqrt(cfg["dh"]))
+    else:
+        oracle.attn_bwd_packed(Q, K, V, dO, 1.0 / math.sqrt(cfg["dh"]), cu)
     dt = time.perf_counter() - t0
     scale = cfg["Hq"] / sample_heads
     tokens = cfg["B"] * cfg["T"]
@@ -374,7 +400,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {k: v for k, v in cfg.items() if k not in ("kind", "name", "index", "dtype")}
-                  | {"workload": cfg["name"]} | ({"valid_tokens": n_valid} if n_valid else {}),
+                  | {"workload": cfg["name"]} | ({"valid_tokens": n_valid} if n_valid else {})
+                  | ({"cu_seqlens": cu} if (cu := synthetic.workload_cu(idx, T)) else {}),
         "peak_hbm_bytes": int(peak),
         "peak_hbm_bytes_call": int(peak - base_mem),
         "mfma_frac_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),

@@ -256,6 +256,23 @@ sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, const void* 
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * 3b. Decoder-layer backward over packed independent sequences.
+ *
+ * As (3) with the tokens [0, T) being several sequences laid end to end,
+ * sequence n holding tokens [cu[n], cu[n+1]): attention stays inside each
+ * sequence (the mask of 2b); RMSNorm, the projections and the MLP are
+ * token-wise and unchanged.  cu_seqlens / nseq as in 2b.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_layer_bwd_packed_workspace_size(const sbp_layer_desc* desc, int32_t D,
+                                               size_t* bytes);
+
+sbp_status sbp_layer_bwd_packed(const sbp_layer_desc* desc, const int32_t* cu_seqlens,
+                                int32_t nseq, const void* x, const void* dy,
+                                const sbp_layer_weights* weights, int32_t D, int32_t accumulate,
+                                void* dx, sbp_layer_grads* grads, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ---------------------------------------------------------------------- */
 const char* sbp_status_string(int32_t status);

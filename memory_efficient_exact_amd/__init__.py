@@ -11,7 +11,7 @@ Names follow ``include/streambp.h``:
 * ``lmhead_ce``      -> ``sbp_lmhead_ce_fwd_bwd``
 * ``lmhead_logprob`` -> ``sbp_lmhead_logprob_fwd``
 * ``attn_bwd``       -> ``sbp_attn_bwd_chunked`` (``sbp_attn_bwd_packed`` with ``cu_seqlens``)
-* ``layer_bwd``      -> ``sbp_layer_bwd``
+* ``layer_bwd``      -> ``sbp_layer_bwd`` (``sbp_layer_bwd_packed`` with ``cu_seqlens``)
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, Laye
 
 __all__ = ["lmhead_ce", "lmhead_logprob", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
            "lmhead_logprob_workspace_size", "attn_bwd_packed_workspace_size",
+           "layer_bwd_packed_workspace_size",
            "attn_bwd_workspace_size", "layer_bwd_workspace_size", "profile", "load",
            "StreamBPError", "chunk_table"]
 
@@ -212,13 +213,27 @@ def layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=
     return out.value
 
 
+def layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16,
+                                    eps=1e-6) -> int:
+    out = C.c_size_t(0)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype)
+    check(load().sbp_layer_bwd_packed_workspace_size(C.byref(desc), D, C.byref(out)))
+    return out.value
+
+
 def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
               eps: float = 1e-6, D: int = 1, grads: Optional[Dict[str, torch.Tensor]] = None,
-              accumulate: bool = False, workspace: Optional[torch.Tensor] = None):
+              accumulate: bool = False, workspace: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None):
     """Streamed backward of one pre-norm decoder layer.  Returns ``(dx, grads)``
-    with fp32 weight/gain gradients keyed like ``weights``."""
+    with fp32 weight/gain gradients keyed like ``weights``.  ``cu_seqlens``
+    (int32 [nseq + 1] on the GPU): packed independent sequences
+    (``sbp_layer_bwd_packed``)."""
     lib = load()
-    _dev(x, dy, *weights.values())
+    _dev(x, dy, cu_seqlens, *weights.values())
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                                   or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be int32 [nseq + 1]")
     T, d = x.shape
     F = weights["W1"].shape[0]
     dev = x.device
@@ -233,10 +248,20 @@ def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: in
     desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt)
     wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
     gst = LayerGrads(*[grads[n].data_ptr() for n in LAYER_NAMES])
-    nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
+    if cu_seqlens is None:
+        nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
+    else:
+        nb = layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
-    check(lib.sbp_layer_bwd(C.byref(desc), _ptr(x), _ptr(dy), C.byref(wst), D, int(accumulate),
-                            _ptr(dx), C.byref(gst), _ptr(ws), ws.numel(), _stream(dev)))
+    if cu_seqlens is None:
+        check(lib.sbp_layer_bwd(C.byref(desc), _ptr(x), _ptr(dy), C.byref(wst), D,
+                                int(accumulate), _ptr(dx), C.byref(gst), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    else:
+        check(lib.sbp_layer_bwd_packed(C.byref(desc), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+                                       _ptr(x), _ptr(dy), C.byref(wst), D, int(accumulate),
+                                       _ptr(dx), C.byref(gst), _ptr(ws), ws.numel(),
+                                       _stream(dev)))
     return dx, grads
 
 

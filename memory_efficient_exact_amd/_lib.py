@@ -50,6 +50,9 @@ SIGNATURES = {
     "sbp_layer_bwd_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
     "sbp_layer_bwd": (i32, [C.POINTER(LayerDesc), vp, vp, C.POINTER(LayerWeights), i32, i32,
                             vp, C.POINTER(LayerGrads), vp, sz, vp]),
+    "sbp_layer_bwd_packed_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
+    "sbp_layer_bwd_packed": (i32, [C.POINTER(LayerDesc), vp, i32, vp, vp, C.POINTER(LayerWeights),
+                                   i32, i32, vp, C.POINTER(LayerGrads), vp, sz, vp]),
     "sbp_status_string": (C.c_char_p, [i32]),
     "sbp_last_error": (C.c_char_p, []),
     "sbp_version": (i32, []),

@@ -6,7 +6,8 @@
 // gradient) and "Architecture Overview" (layer-wise application, causal
 // structure).  Layer (no bias, no rotary embedding):
 //   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T
-//   o = causal GQA attention; a = x + o Wo^T
+//   o = causal GQA attention (packed sequences: inside each sequence only);
+//   a = x + o Wo^T
 //   n2 = RMSNorm(a; g2); [u | g] = n2 [W1; W3]^T; m = silu(u) g; y = a + m W2^T
 //
 // Pass F: h1 and k, v for every token, chunk by chunk (the causal prefix
@@ -61,9 +62,10 @@ struct LayerWs {
   bf16_t *W2T, *W13T, *WoT, *WqkvT;
   bf16_t *h1, *q, *o, *a, *n2, *ug, *mdm, *dudg, *da, *dov, *dqkv;
   float *dn, *rinv1, *rinv2, *lse, *delta, *gpart;
+  int *seq_lo, *seq_hi;  // packed sequences only
 };
 
-size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
+size_t layer_plan(const LayerShape& s, bool packed, char* base, LayerWs* w) {
   WsPlan P;
   P.base = base;
   LayerWs x;
@@ -94,6 +96,8 @@ size_t layer_plan(const LayerShape& s, char* base, LayerWs* w) {
   x.lse = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   x.delta = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
   x.gpart = (float*)P.take(f4 * gain_grad_splits(R) * s.d);
+  x.seq_lo = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
+  x.seq_hi = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
   if (w) *w = x;
   return round_up((int64_t)P.off, 256);
 }
@@ -113,26 +117,10 @@ sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   return SBP_OK;
 }
 
-}  // namespace
-}  // namespace sbp
-
-using namespace sbp;
-
-extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D,
-                                                   size_t* bytes) {
-  clear_error();
-  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
-  sbp_status st = layer_check(desc, D);
-  if (st != SBP_OK) return st;
-  *bytes = layer_plan(layer_shape(desc, D), nullptr, nullptr);
-  return SBP_OK;
-}
-
-extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, const void* dy,
-                                    const sbp_layer_weights* w, int32_t D, int32_t accumulate,
-                                    void* dx, sbp_layer_grads* g, void* ws, size_t ws_bytes,
-                                    void* stream) {
-  clear_error();
+// Both entry points: checks, then pass F and pass B over the chunks.
+sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq, const void* x,
+                     const void* dy, const sbp_layer_weights* w, int32_t D, int32_t accumulate,
+                     void* dx, sbp_layer_grads* g, void* ws, size_t ws_bytes, hipStream_t str) {
   sbp_status st = layer_check(desc, D);
   if (st != SBP_OK) return st;
   if (!x || !dy || !w || !dx || !g) return set_error(SBP_ERR_INVALID_ARG, "x, dy, weights, dx, grads must be non-NULL");
@@ -145,12 +133,12 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
   if (misaligned(x) || misaligned(dy) || misaligned(dx) || misaligned(ws))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const LayerShape S = layer_shape(desc, D);
-  const size_t need = layer_plan(S, nullptr, nullptr);
+  const bool packed = cu != nullptr;
+  const size_t need = layer_plan(S, packed, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   LayerWs W;
-  layer_plan(S, (char*)ws, &W);
-  hipStream_t str = (hipStream_t)stream;
+  layer_plan(S, packed, (char*)ws, &W);
   const int64_t d = S.d, F = S.F, qd = S.qd, kd = S.kd, qkvd = S.qkvd;
   const bf16_t* X = (const bf16_t*)x;
   const bf16_t* DY = (const bf16_t*)dy;
@@ -192,6 +180,8 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
   SBP_TRY(tr(w->Wk, d, kd, d, W.WqkvT + qd, qkvd, kd));
   SBP_TRY(tr(w->Wv, d, kd, d, W.WqkvT + qd + kd, qkvd, kd));
 
+  // packed sequences: per-token sequence bounds for the attention kernels
+  if (packed) SBP_TRY(attn_seq_bounds(cu, nseq, S.T, W.seq_lo, W.seq_hi, str));
   // pass F: keys and values of every token
   for (int32_t c = 0; c < D; ++c) {
     int64_t s0, e0;
@@ -224,6 +214,7 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
     at.T = (int)S.T; at.Hq = S.Hq; at.Hkv = S.Hkv; at.G = S.Hq / S.Hkv;
     at.s = (int)s0; at.e = (int)e0; at.scale = scale;
     at.beta = (c == D - 1) ? 0 : 1;  // dK/dV accumulators start at the last chunk
+    at.seq_lo = W.seq_lo; at.seq_hi = W.seq_hi;
     SBP_TRY(attn_fwd(at, S.dh, 1, str));
     SBP_TRY(gemm(W.o, qd, w->Wo, qd, W.a, d, Tc, d, qd, EPI_OUT_RESID, 0, xc, d, "gemm_layer_fwd"));
     SBP_TRY(rmsnorm_fwd(W.a, d, w->g2, Tc, d, S.eps, W.n2, d, W.rinv2, str));
@@ -262,4 +253,51 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
   }
 #undef SBP_TRY
   return SBP_OK;
+}
+
+}  // namespace
+}  // namespace sbp
+
+using namespace sbp;
+
+extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D,
+                                                   size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = layer_check(desc, D);
+  if (st != SBP_OK) return st;
+  *bytes = layer_plan(layer_shape(desc, D), false, nullptr, nullptr);
+  return SBP_OK;
+}
+
+extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, const void* dy,
+                                    const sbp_layer_weights* w, int32_t D, int32_t accumulate,
+                                    void* dx, sbp_layer_grads* g, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  clear_error();
+  return layer_run(desc, nullptr, 0, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
+                   (hipStream_t)stream);
+}
+
+extern "C" sbp_status sbp_layer_bwd_packed_workspace_size(const sbp_layer_desc* desc, int32_t D,
+                                                          size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = layer_check(desc, D);
+  if (st != SBP_OK) return st;
+  *bytes = layer_plan(layer_shape(desc, D), true, nullptr, nullptr);
+  return SBP_OK;
+}
+
+extern "C" sbp_status sbp_layer_bwd_packed(const sbp_layer_desc* desc, const int32_t* cu_seqlens,
+                                           int32_t nseq, const void* x, const void* dy,
+                                           const sbp_layer_weights* w, int32_t D,
+                                           int32_t accumulate, void* dx, sbp_layer_grads* g,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!cu_seqlens) return set_error(SBP_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
+  if (nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (misaligned(cu_seqlens)) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  return layer_run(desc, cu_seqlens, nseq, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
+                   (hipStream_t)stream);
 }

@@ -162,8 +162,9 @@ def to_f64(t: Optional[torch.Tensor]):
 
 
 # ---------------------------------------------------------------------------
-# The five workloads (index 0..4), seed = 1000 + index, and the forward-only
-# log-probability workload (index 5).
+# The five workloads (index 0..4), seed = 1000 + index, the forward-only
+# log-probability workload (index 5) and packed-sequence variants of the
+# attention and layer workloads (6, 7).
 # ---------------------------------------------------------------------------
 WORKLOADS = {
     0: dict(kind="lmhead", name="lmhead_ce_f32_T256_d64_V512_D4",
@@ -182,7 +183,29 @@ WORKLOADS = {
     5: dict(kind="logprob", name="lmhead_logprob_bf16_T131072x8seq_d3584_V152064_D32",
             T=131072, d=3584, V=152064, D=32, dtype="bf16", w_std=0.02,
             n_seq=8, masked_frac=0.25),
+    # workloads 2 and 3 with 8 packed sequences of random lengths
+    6: dict(kind="attn", name="attn_bwd_packed_bf16_T16384x8seq_Hq32_Hkv8_dh128_D8",
+            B=1, T=16384, Hq=32, Hkv=8, dh=128, D=8, dtype="bf16", n_seq=8),
+    7: dict(kind="layer", name="layer_bwd_packed_bf16_T65536x8seq_d4096_F14336_D16",
+            T=65536, d=4096, Hq=32, Hkv=8, dh=128, F=14336, D=16, dtype="bf16", n_seq=8),
 }
+
+
+def packed_cuts(T: int, n_seq: int, seed: int):
+    """Boundaries 0 = cu[0] < ... < cu[n_seq] = T of n_seq packed sequences:
+    n_seq - 1 distinct cut points drawn uniformly from [1, T)."""
+    g = _gen(seed)
+    cuts = torch.randperm(T - 1, generator=g)[: n_seq - 1] + 1
+    return [0] + sorted(int(c) for c in cuts) + [T]
+
+
+def workload_cu(index: int, T: Optional[int] = None):
+    """Sequence boundaries of a packed workload (None if it is not packed);
+    seed 2000 + index."""
+    cfg = WORKLOADS[index]
+    if cfg["kind"] not in ("attn", "layer") or "n_seq" not in cfg:
+        return None
+    return packed_cuts(cfg["T"] if T is None else T, cfg["n_seq"], 2000 + index)
 
 
 def workload_inputs(index: int, **override):

@@ -222,3 +222,24 @@ def test_logprob_workspace_holds_no_logits():
     st, w = _ws(lib.sbp_lmhead_logprob_workspace_size, 131072, 3584, 152064, 32, 1)
     assert st == 0
     assert w < 4096 * 152064 * 4 / 25
+
+
+def test_packed_layer_argument_errors_and_workspace():
+    lib = sbp.load()
+    desc = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 1)
+    w = _lib.LayerWeights(*[FAKE] * 9)
+    g = _lib.LayerGrads(*[FAKE] * 9)
+
+    def call(cu=FAKE, nseq=2, D=2, wsb=1 << 40):
+        return lib.sbp_layer_bwd_packed(C.byref(desc), cu, nseq, FAKE, FAKE, C.byref(w), D, 0,
+                                        FAKE, C.byref(g), FAKE, wsb, None)
+
+    assert call(cu=None) == _lib.SBP_ERR_INVALID_ARG
+    assert call(cu=MIS) == _lib.SBP_ERR_INVALID_ARG
+    assert call(nseq=0) == _lib.SBP_ERR_INVALID_ARG
+    assert call(D=0) == _lib.SBP_ERR_INVALID_ARG
+    assert call(wsb=1) == _lib.SBP_ERR_WORKSPACE
+    a, b = C.c_size_t(0), C.c_size_t(0)
+    assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 2, C.byref(a)) == 0
+    assert lib.sbp_layer_bwd_packed_workspace_size(C.byref(desc), 2, C.byref(b)) == 0
+    assert a.value < b.value <= a.value + 2 * 256 + 2 * 64 * 4
