@@ -22,7 +22,8 @@ chunked algorithm:
 * ``attention.attn_bwd``    -- causal GQA attention forward and backward;
   ``attn_bwd_packed`` the same over packed independent sequences.
 * ``layer.layer_bwd``       -- one pre-norm decoder layer, forward and
-  backward by the chain rule.
+  backward by the chain rule, optionally with the rotary position embedding
+  of q and k (``layer.rope``).
 * ``chunked``               -- a separate fp64 *chunked* evaluation of the
   same three functions (sequence decomposition of the skill page's
   "Implementation"), used only to show that chunking is algebraically exact
@@ -35,9 +36,9 @@ No function here is "parity unpinned".
 """
 from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_logprob, lmhead_logprob_rows
 from .attention import attn_fwd, attn_bwd, attn_bwd_sampled, attn_bwd_packed
-from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd
+from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd, rope, rope_positions
 from . import chunked
 
 __all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
            "attn_bwd_sampled", "attn_bwd_packed", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
-           "rmsnorm_bwd", "chunked"]
+           "rmsnorm_bwd", "rope", "rope_positions", "chunked"]

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layer import rmsnorm_fwd, rmsnorm_bwd, _sigmoid
+from .layer import rmsnorm_fwd, rmsnorm_bwd, rope, rope_positions, _sigmoid
 
 
 def chunk_table(T: int, D: int):
@@ -98,8 +98,8 @@ def attn_bwd(Q, K, V, dO, scale, D):
     return dQ, dK, dV
 
 
-def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D):
-    """Streamed layer backward.
+def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D, rope_theta=0.0):
+    """Streamed layer backward (``rope_theta`` as in ``layer.layer_fwd``).
 
     Pass F: h1 and the key/value projections for every token (the causal
     prefix every later query chunk needs).  Pass B, chunks in reverse order:
@@ -116,6 +116,9 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D):
     scale = 1.0 / np.sqrt(dh)
     h1_all, _, _ = rmsnorm_fwd(x, W["g1"], eps)
     k_all = (h1_all @ W["Wk"].T).reshape(T, Hkv, dh)
+    pos = rope_positions(T)
+    if rope_theta > 0:
+        k_all = rope(k_all, pos, rope_theta)
     v_all = (h1_all @ W["Wv"].T).reshape(T, Hkv, dh)
     dk_all = np.zeros_like(k_all)
     dv_all = np.zeros_like(v_all)
@@ -125,6 +128,8 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D):
         xc = x[s:e]
         h1, _, _ = rmsnorm_fwd(xc, W["g1"], eps)
         q = (h1 @ W["Wq"].T).reshape(e - s, Hq, dh)
+        if rope_theta > 0:
+            q = rope(q, pos[s:e], rope_theta)
         ii = np.arange(s, e)[:, None]
         jj = np.arange(e)[None, :]
         o = np.zeros((e - s, Hq, dh))
@@ -166,8 +171,12 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D):
             dS = P * (dP - (do[:, h] * o[:, h]).sum(axis=1, keepdims=True))
             dq[:, h] = scale * (dS @ k_all[:e, kv])
             dk_all[:e, kv] += scale * (dS.T @ q[:, h])
+        dkc = dk_all[s:e]
+        if rope_theta > 0:
+            dq = rope(dq, pos[s:e], rope_theta, inverse=True)
+            dkc = rope(dkc, pos[s:e], rope_theta, inverse=True)
         dq2 = dq.reshape(e - s, Hq * dh)
-        dkc = dk_all[s:e].reshape(e - s, Hkv * dh)
+        dkc = dkc.reshape(e - s, Hkv * dh)
         dvc = dv_all[s:e].reshape(e - s, Hkv * dh)
         gr["Wq"] += dq2.T @ h1
         gr["Wk"] += dkc.T @ h1

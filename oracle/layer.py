@@ -6,11 +6,12 @@ Sources: StreamBP skill page, "Implementation" (the streaming layer backward:
 a layer function run forward, then backward with the upstream gradient, the
 weight gradients summed and the input gradient kept) and "Architecture
 Overview" ("Layer-Wise Application").  The pages name no layer structure; the
-plain reading of an 8B-class decoder layer is used (no bias, no rotary
-embedding, gains multiply)::
+plain reading of an 8B-class decoder layer is used (no bias, gains multiply,
+rotary position embedding optional)::
 
     h1 = RMSNorm(x; g1)
     q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T            (heads: Hq, Hkv of width dh)
+    q, k = Rope(q), Rope(k)                         (only when theta > 0)
     o  = CausalGQA(q, k, v), scale 1/sqrt(dh)
     a  = x + o Wo^T
     n2 = RMSNorm(a; g2)
@@ -27,6 +28,18 @@ upstream dy and xhat = x / r::
 (from d xhat_k / d x_j = (delta_kj - xhat_k xhat_j / n) / r).
 
 silu(u) = u sigma(u),   silu'(u) = sigma(u) (1 + u (1 - sigma(u))).
+
+Rotary position embedding (RoFormer, Su et al. 2021; not on the pages, which
+name no position encoding): each head vector of width dh is split into halves
+x = (x1, x2) of width dh/2, and for i < dh/2 the pair (x1_i, x2_i) is turned
+by the angle p * theta^(-2i/dh), p the token's position:
+
+    Rope(x)_i        = x1_i cos - x2_i sin
+    Rope(x)_{i+dh/2} = x2_i cos + x1_i sin
+
+A rotation's inverse is its transpose, so the backward turns the gradient by
+the negative angle.  Positions count from 0 at the start of the row, and
+from 0 at the start of each sequence when the row holds packed sequences.
 """
 from __future__ import annotations
 
@@ -57,14 +70,41 @@ def rmsnorm_bwd(x, g, dy, eps):
     return dx, dg
 
 
+def rope_positions(T, cu_seqlens=None):
+    """Position of every token: t, or t - cu[n] for the sequence n holding t."""
+    pos = np.arange(T, dtype=np.float64)
+    if cu_seqlens is not None:
+        cu = list(cu_seqlens)
+        for a, b in zip(cu, cu[1:]):
+            pos[a:b] -= a
+    return pos
+
+
+def rope(x, pos, theta, inverse=False):
+    """Rotary embedding of x [T, H, dh] at positions pos [T]; ``inverse``
+    turns by the negative angle (the transpose of the forward rotation)."""
+    x = _as64(x)
+    dh = x.shape[-1]
+    half = dh // 2
+    inv_freq = float(theta) ** (-2.0 * np.arange(half) / dh)
+    ang = _as64(pos)[:, None] * inv_freq[None, :]          # [T, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    if inverse:
+        s = -s
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
 def _sigmoid(u):
     return 1.0 / (1.0 + np.exp(-u))
 
 
-def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None):
+def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
     """Forward of the layer; returns ``(y, cache)``.  ``cu_seqlens``: the
     tokens are packed independent sequences (attention stays inside each;
-    every other step is token-wise)."""
+    every other step is token-wise).  ``rope_theta`` > 0 turns q and k by the
+    rotary embedding of that base; 0 leaves them as projected."""
     x = _as64(x)
     W = {k: _as64(v) for k, v in w.items()}
     T = x.shape[0]
@@ -72,6 +112,10 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None):
     q = h1 @ W["Wq"].T
     k = h1 @ W["Wk"].T
     v = h1 @ W["Wv"].T
+    if rope_theta > 0:
+        pos = rope_positions(T, cu_seqlens)
+        q = rope(q.reshape(T, Hq, dh), pos, rope_theta).reshape(T, Hq * dh)
+        k = rope(k.reshape(T, Hkv, dh), pos, rope_theta).reshape(T, Hkv * dh)
     scale = 1.0 / np.sqrt(dh)
     q4, k4, v4 = q.reshape(1, T, Hq, dh), k.reshape(1, T, Hkv, dh), v.reshape(1, T, Hkv, dh)
     if cu_seqlens is None:
@@ -90,15 +134,15 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None):
     return y, cache
 
 
-def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None):
+def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
     """Full (unchunked) backward.  Returns ``(dx, grads, y)``; ``grads`` maps
     every name of ``w`` (g1, Wq, Wk, Wv, Wo, g2, W1, W3, W2) to its gradient.
-    ``cu_seqlens`` as in ``layer_fwd``."""
+    ``cu_seqlens`` and ``rope_theta`` as in ``layer_fwd``."""
     x = _as64(x)
     dy = _as64(dy)
     W = {k: _as64(v) for k, v in w.items()}
     T = x.shape[0]
-    y, c = layer_fwd(x, W, Hq, Hkv, dh, eps, cu_seqlens)
+    y, c = layer_fwd(x, W, Hq, Hkv, dh, eps, cu_seqlens, rope_theta)
     gr = {}
     # MLP: y = a + m W2^T
     gr["W2"] = dy.T @ c["m"]
@@ -126,6 +170,10 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None):
     dq = dq4.reshape(T, Hq * dh)
     dk = dk4.reshape(T, Hkv * dh)
     dv = dv4.reshape(T, Hkv * dh)
+    if rope_theta > 0:  # q, k were turned after the projection: turn back
+        pos = rope_positions(T, cu_seqlens)
+        dq = rope(dq.reshape(T, Hq, dh), pos, rope_theta, inverse=True).reshape(T, Hq * dh)
+        dk = rope(dk.reshape(T, Hkv, dh), pos, rope_theta, inverse=True).reshape(T, Hkv * dh)
     gr["Wq"] = dq.T @ c["h1"]
     gr["Wk"] = dk.T @ c["h1"]
     gr["Wv"] = dv.T @ c["h1"]

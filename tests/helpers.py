@@ -13,7 +13,8 @@ def load_golden(name):
         return json.load(f)
 
 
-_ENV = {"__builtins__": {}, "ln": math.log, "sqrt": math.sqrt, "exp": math.exp}
+_ENV = {"__builtins__": {}, "ln": math.log, "sqrt": math.sqrt, "exp": math.exp,
+        "cos": math.cos, "sin": math.sin}
 
 
 def ev(x):
