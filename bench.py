@@ -363,6 +363,15 @@ def main():
                 prof[kname] = dict(prof[kname], flops=flops * args.steps / 3.0)
     elif cfg["kind"] == "logprob" and "gemm_logits_lp" in prof:
         prof["gemm_logits_lp"] = dict(prof["gemm_logits_lp"], flops=flops * args.steps)
+    # The attention kernels count the pairs of one causal row of T tokens; over
+    # a whole step (every chunk) that is T(T+1)/2 pairs, against the sum over
+    # packed sequences of L(L+1)/2 that is really visible.
+    cu_step = synthetic.workload_cu(idx, T)
+    if cu_step is not None and cfg["kind"] in ("attn", "layer"):
+        ratio = attn_unit(cfg["Hq"], cfg["dh"], T, 1, cu_step) / attn_unit(cfg["Hq"], cfg["dh"], T)
+        for kname in ("attn_fwd", "attn_dkdv", "attn_dq"):
+            if kname in prof:
+                prof[kname] = dict(prof[kname], flops=prof[kname]["flops"] * ratio)
     # dominant kernel and its roofline (live hipEvent timing inside the call)
     dom = max(prof.items(), key=lambda kv: kv[1]["ms"])
     name, k = dom
