@@ -217,9 +217,16 @@ sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V, cons
  * gradient) and "Architecture Overview" (layer-wise application).  Layer:
  *
  *   h1 = RMSNorm(x; g1); q,k,v = h1 Wq^T, h1 Wk^T, h1 Wv^T
+ *   q, k = Rope(q), Rope(k)        (only when desc->rope_theta > 0)
  *   o = causal GQA attention (scale 1/sqrt(dh)); a = x + o Wo^T
  *   n2 = RMSNorm(a; g2); m = silu(n2 W1^T) * (n2 W3^T); y = a + m W2^T
  *   RMSNorm(x; g) = g x / sqrt(mean(x^2) + eps)
+ *   Rope: rotary position embedding (RoFormer, Su et al.; the pages name no
+ *   position encoding): each head vector's halves (x1, x2) of width dh/2 turn
+ *   pair by pair, pair i by p * rope_theta^(-2i/dh) with p the token's
+ *   position (0 at the start of the row, or of its sequence when packed):
+ *   (x1 cos - x2 sin, x2 cos + x1 sin).  The workspace then also holds a
+ *   (cos, sin) table of T * dh/2 float pairs.
  *
  * Keys and values of all T tokens are formed once (the causal prefix); then
  * chunks run in reverse order, each recomputing its own forward, so the MLP
@@ -238,6 +245,7 @@ typedef struct {
   int64_t F;
   float eps;
   int32_t dtype;
+  float rope_theta;  /* rotary embedding base; 0 = no rotary embedding; must be >= 0 */
 } sbp_layer_desc;
 
 typedef struct {
@@ -271,6 +279,32 @@ sbp_status sbp_layer_bwd_packed(const sbp_layer_desc* desc, const int32_t* cu_se
                                 const sbp_layer_weights* weights, int32_t D, int32_t accumulate,
                                 void* dx, sbp_layer_grads* grads, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * 3c. One pre-norm decoder layer, chunked forward: y = Layer(x).
+ *
+ * Passage: skill page, "Architecture Overview" (layer-wise application) and
+ * "Implementation" (the streaming layer backward starts from each layer's
+ * input, kept from a forward pass): this call is that forward, so that a
+ * caller can run a stack of layers and keep the input of every layer for
+ * sbp_layer_bwd.  The layer is the one of (3), rotary embedding included.
+ *
+ * Chunks run in order; chunk c forms its own keys and values, then its
+ * queries attend over keys [0, e_c) (inside their own sequence when
+ * cu_seqlens is given).  Keys and values of all T tokens stay in the
+ * workspace; every other activation exists for one chunk at a time.
+ *
+ * cu_seqlens  device int32 [nseq + 1] packed-sequence boundaries as in 2b, or
+ *             NULL for one causal row of T tokens (nseq then ignored)
+ * x           [T, d] dtype (device);  y [T, d] dtype out, must not alias x
+ * weights     as in (3)
+ * Errors: as in (3); y == x -> SBP_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_layer_fwd_workspace_size(const sbp_layer_desc* desc, int32_t D, size_t* bytes);
+
+sbp_status sbp_layer_fwd(const sbp_layer_desc* desc, const int32_t* cu_seqlens, int32_t nseq,
+                         const void* x, const sbp_layer_weights* weights, int32_t D, void* y,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

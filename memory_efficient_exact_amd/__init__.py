@@ -202,21 +202,22 @@ def attn_bwd(Q, K, V, dO, D: int = 1, scale: Optional[float] = None, O=None, lse
 
 
 # ----------------------------------------------------------------------------
-def _desc(T, d, Hq, Hkv, dh, F, eps, dtype) -> LayerDesc:
-    return LayerDesc(T, d, Hq, Hkv, dh, F, eps, _DT[dtype])
+def _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta=0.0) -> LayerDesc:
+    return LayerDesc(T, d, Hq, Hkv, dh, F, eps, _DT[dtype], float(rope_theta))
 
 
-def layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6) -> int:
+def layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6,
+                             rope_theta=0.0) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
     check(load().sbp_layer_bwd_workspace_size(C.byref(desc), D, C.byref(out)))
     return out.value
 
 
 def layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16,
-                                    eps=1e-6) -> int:
+                                    eps=1e-6, rope_theta=0.0) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
     check(load().sbp_layer_bwd_packed_workspace_size(C.byref(desc), D, C.byref(out)))
     return out.value
 
@@ -224,11 +225,12 @@ def layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat1
 def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
               eps: float = 1e-6, D: int = 1, grads: Optional[Dict[str, torch.Tensor]] = None,
               accumulate: bool = False, workspace: Optional[torch.Tensor] = None,
-              cu_seqlens: Optional[torch.Tensor] = None):
+              cu_seqlens: Optional[torch.Tensor] = None, rope_theta: float = 0.0):
     """Streamed backward of one pre-norm decoder layer.  Returns ``(dx, grads)``
     with fp32 weight/gain gradients keyed like ``weights``.  ``cu_seqlens``
     (int32 [nseq + 1] on the GPU): packed independent sequences
-    (``sbp_layer_bwd_packed``)."""
+    (``sbp_layer_bwd_packed``).  ``rope_theta`` > 0: rotary embedding of q
+    and k with that base."""
     lib = load()
     _dev(x, dy, cu_seqlens, *weights.values())
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
@@ -245,13 +247,13 @@ def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: in
         if weights[n].dtype != dt or grads[n].dtype != torch.float32 or grads[n].shape != weights[n].shape:
             raise ValueError(f"bad weight/grad {n}")
     dx = torch.empty_like(x)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta)
     wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
     gst = LayerGrads(*[grads[n].data_ptr() for n in LAYER_NAMES])
     if cu_seqlens is None:
-        nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
+        nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
     else:
-        nb = layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps)
+        nb = layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
     if cu_seqlens is None:
         check(lib.sbp_layer_bwd(C.byref(desc), _ptr(x), _ptr(dy), C.byref(wst), D,
@@ -263,6 +265,45 @@ def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: in
                                        _ptr(dx), C.byref(gst), _ptr(ws), ws.numel(),
                                        _stream(dev)))
     return dx, grads
+
+
+def layer_fwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6,
+                             rope_theta=0.0) -> int:
+    out = C.c_size_t(0)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    check(load().sbp_layer_fwd_workspace_size(C.byref(desc), D, C.byref(out)))
+    return out.value
+
+
+def layer_fwd(x, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
+              eps: float = 1e-6, D: int = 1, cu_seqlens: Optional[torch.Tensor] = None,
+              rope_theta: float = 0.0, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """Chunked forward of one pre-norm decoder layer (``sbp_layer_fwd``);
+    returns ``y`` [T, d] in x's dtype."""
+    lib = load()
+    _dev(x, cu_seqlens, *weights.values())
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                                   or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be int32 [nseq + 1]")
+    T, d = x.shape
+    F = weights["W1"].shape[0]
+    dt = x.dtype
+    for n in LAYER_NAMES:
+        if weights[n].dtype != dt:
+            raise ValueError(f"bad weight {n}")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != dt:
+        raise ValueError("out must match x")
+    _dev(y)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta)
+    wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
+    nb = layer_fwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, x.device)
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    check(lib.sbp_layer_fwd(C.byref(desc), _ptr(cu_seqlens), nseq, _ptr(x), C.byref(wst), D,
+                            _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y
 
 
 # ----------------------------------------------------------------------------

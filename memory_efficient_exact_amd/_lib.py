@@ -20,7 +20,7 @@ sz = C.c_size_t
 
 class LayerDesc(C.Structure):
     _fields_ = [("T", i64), ("d", i64), ("Hq", i32), ("Hkv", i32), ("dh", i32),
-                ("F", i64), ("eps", f32), ("dtype", i32)]
+                ("F", i64), ("eps", f32), ("dtype", i32), ("rope_theta", f32)]
 
 
 LAYER_NAMES = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W3", "W2")
@@ -53,6 +53,9 @@ SIGNATURES = {
     "sbp_layer_bwd_packed_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
     "sbp_layer_bwd_packed": (i32, [C.POINTER(LayerDesc), vp, i32, vp, vp, C.POINTER(LayerWeights),
                                    i32, i32, vp, C.POINTER(LayerGrads), vp, sz, vp]),
+    "sbp_layer_fwd_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
+    "sbp_layer_fwd": (i32, [C.POINTER(LayerDesc), vp, i32, vp, C.POINTER(LayerWeights), i32, vp,
+                            vp, sz, vp]),
     "sbp_status_string": (C.c_char_p, [i32]),
     "sbp_last_error": (C.c_char_p, []),
     "sbp_version": (i32, []),

@@ -111,5 +111,14 @@ sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, v
                       hipStream_t st);
 sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t cols, void* dst,
                         int64_t ldd, hipStream_t st);
+// Rotary embedding: tab [P, dh/2] of (cos, sin) for positions 0 .. P-1;
+// rope_apply turns rows [0, rows) of src (H heads of width dh, fp32 or bf16,
+// pitch lds_) into dst (bf16, pitch ldd; dst == src allowed for bf16), row r
+// at position row0 + r - seq_lo[row0 + r] (seq_lo NULL: row0 + r);
+// inverse turns by the negative angle.
+sbp_status rope_table(float2* tab, int64_t P, int dh, double theta, hipStream_t st);
+sbp_status rope_apply(const void* src, bool src_f32, int64_t lds_, void* dst, int64_t ldd,
+                      int64_t rows, int H, int dh, int64_t row0, const int* seq_lo,
+                      const float2* tab, bool inverse, hipStream_t st);
 
 }  // namespace sbp

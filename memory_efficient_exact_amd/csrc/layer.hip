@@ -4,8 +4,9 @@
 // chunk, run the layer forward on the chunk, back-propagate the chunk's
 // upstream gradient, add the weight gradients, keep the chunk's input
 // gradient) and "Architecture Overview" (layer-wise application, causal
-// structure).  Layer (no bias, no rotary embedding):
-//   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T
+// structure).  Layer (no bias; rotary embedding of q and k when
+// rope_theta > 0, not on the pages):
+//   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T; q, k = Rope(q, k)
 //   o = causal GQA attention (packed sequences: inside each sequence only);
 //   a = x + o Wo^T
 //   n2 = RMSNorm(a; g2); [u | g] = n2 [W1; W3]^T; m = silu(u) g; y = a + m W2^T
@@ -18,7 +19,8 @@
 //   dg2 +=;  dWo += da^T o;  do = da Wo;  attention backward over the prefix
 //   (dK, dV of keys [0, e) accumulate in fp32; after chunk c, rows [s, e) are
 //   final because later chunks already added theirs and earlier chunks never
-//   reach them);  dWq, dWk, dWv += [dq | dK_c | dV_c]^T h1;
+//   reach them);  dq, dK_c turned back by the inverse rotation (if any);
+//   dWq, dWk, dWv += [dq | dK_c | dV_c]^T h1;
 //   dh1 = [dq | dK_c | dV_c] [Wq; Wk; Wv];  dx = da + RMSNorm1'(dh1), dg1 +=.
 // Every product is one bf16 ring GEMM (gemm.hip).  Weight gradients contract
 // over the chunk's tokens and read both activations K-major, in place (e.g.
@@ -41,6 +43,7 @@ struct LayerShape {
   int32_t D;
   int64_t Tcm;
   float eps;
+  float rope_theta;  // 0: no rotary embedding
 };
 
 LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
@@ -53,6 +56,7 @@ LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
   s.D = D;
   s.Tcm = max_chunk_len(L->T, D);
   s.eps = L->eps;
+  s.rope_theta = L->rope_theta;
   return s;
 }
 
@@ -63,6 +67,7 @@ struct LayerWs {
   bf16_t *h1, *q, *o, *a, *n2, *ug, *mdm, *dudg, *da, *dov, *dqkv;
   float *dn, *rinv1, *rinv2, *lse, *delta, *gpart;
   int *seq_lo, *seq_hi;  // packed sequences only
+  float2* rope_tab;      // rotary embedding only: [T, dh/2] (cos, sin)
 };
 
 size_t layer_plan(const LayerShape& s, bool packed, char* base, LayerWs* w) {
@@ -98,6 +103,7 @@ size_t layer_plan(const LayerShape& s, bool packed, char* base, LayerWs* w) {
   x.gpart = (float*)P.take(f4 * gain_grad_splits(R) * s.d);
   x.seq_lo = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
   x.seq_hi = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
+  x.rope_tab = s.rope_theta > 0.f ? (float2*)P.take(sizeof(float2) * s.T * (s.dh / 2)) : nullptr;
   if (w) *w = x;
   return round_up((int64_t)P.off, 256);
 }
@@ -110,6 +116,8 @@ sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   if (D < 1 || D > L->T) return set_error(SBP_ERR_INVALID_ARG, "need 1 <= D <= T (D=%d, T=%lld)", D, (long long)L->T);
   if (L->Hq % L->Hkv) return set_error(SBP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", L->Hq, L->Hkv);
   if (!(L->eps >= 0.f)) return set_error(SBP_ERR_INVALID_ARG, "eps must be >= 0");
+  if (!(L->rope_theta >= 0.f) || !(L->rope_theta < INFINITY))
+    return set_error(SBP_ERR_INVALID_ARG, "rope_theta must be finite and >= 0 (0 = none)");
   if (L->dh != 64 && L->dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", L->dh);
   if (L->d % 8 || L->F % 8) return set_error(SBP_ERR_UNSUPPORTED, "d and F must be multiples of 8");
   if (L->dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "the decoder-layer backward is implemented for bf16 only");
@@ -181,7 +189,10 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
   SBP_TRY(tr(w->Wv, d, kd, d, W.WqkvT + qd + kd, qkvd, kd));
 
   // packed sequences: per-token sequence bounds for the attention kernels
+  // (and the rotary positions, which restart at each sequence)
   if (packed) SBP_TRY(attn_seq_bounds(cu, nseq, S.T, W.seq_lo, W.seq_hi, str));
+  const bool rope = W.rope_tab != nullptr;
+  if (rope) SBP_TRY(rope_table(W.rope_tab, S.T, S.dh, (double)S.rope_theta, str));
   // pass F: keys and values of every token
   for (int32_t c = 0; c < D; ++c) {
     int64_t s0, e0;
@@ -190,6 +201,9 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     SBP_TRY(rmsnorm_fwd(X + s0 * d, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
     SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
     SBP_TRY(gemm(W.h1, d, w->Wv, d, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (rope)
+      SBP_TRY(rope_apply(W.Kall + s0 * kd, false, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, s0,
+                         W.seq_lo, W.rope_tab, false, str));
   }
 
   const float scale = 1.0f / sqrtf((float)S.dh);
@@ -204,6 +218,8 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     // ---- recompute the chunk's forward ----
     SBP_TRY(rmsnorm_fwd(xc, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
     SBP_TRY(gemm(W.h1, d, w->Wq, d, W.q, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (rope)
+      SBP_TRY(rope_apply(W.q, false, qd, W.q, qd, Tc, S.Hq, S.dh, s0, W.seq_lo, W.rope_tab, false, str));
     AttnArgs at;
     at.Q = W.q; at.K = W.Kall; at.V = W.Vall; at.dO = nullptr; at.O = W.o;
     at.dQ = W.dqkv; at.dK = W.dKacc; at.dV = W.dVacc;
@@ -240,7 +256,14 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     at.dO = W.dov;
     SBP_TRY(attn_delta(at, W.o, nullptr, 0, 0, S.dh, 1, str));
     SBP_TRY(attn_bwd_chunk(at, S.dh, 1, str));
-    SBP_TRY(rows_to_bf16(W.dKacc + s0 * kd, kd, Tc, kd, W.dqkv + qd, qkvd, str));
+    if (rope) {  // gradients of the rotated q, k -> of the projections
+      SBP_TRY(rope_apply(W.dqkv, false, qkvd, W.dqkv, qkvd, Tc, S.Hq, S.dh, s0, W.seq_lo,
+                         W.rope_tab, true, str));
+      SBP_TRY(rope_apply(W.dKacc + s0 * kd, true, kd, W.dqkv + qd, qkvd, Tc, S.Hkv, S.dh, s0,
+                         W.seq_lo, W.rope_tab, true, str));
+    } else {
+      SBP_TRY(rows_to_bf16(W.dKacc + s0 * kd, kd, Tc, kd, W.dqkv + qd, qkvd, str));
+    }
     SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
 
     // ---- q, k, v projections and the first norm ----
@@ -255,10 +278,143 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
   return SBP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Chunked forward y = Layer(x): chunks in order, each forming its own keys and
+// values before its queries attend over keys [0, e) (seq_lo bounds them to the
+// query's sequence when packed).  Activations exist for one chunk at a time;
+// keys and values for all tokens.
+struct LayerFwdWs {
+  bf16_t *Kall, *Vall, *h1, *q, *o, *a, *n2, *ug, *m;
+  float *rinv, *lse;
+  int *seq_lo, *seq_hi;
+  float2* rope_tab;
+};
+
+size_t layer_fwd_plan(const LayerShape& s, char* base, LayerFwdWs* w) {
+  WsPlan P;
+  P.base = base;
+  LayerFwdWs x;
+  const size_t b2 = sizeof(bf16_t), f4 = sizeof(float);
+  const int64_t R = s.Tcm;
+  x.Kall = (bf16_t*)P.take(b2 * s.T * s.kd);
+  x.Vall = (bf16_t*)P.take(b2 * s.T * s.kd);
+  x.h1 = (bf16_t*)P.take(b2 * R * s.d);
+  x.q = (bf16_t*)P.take(b2 * R * s.qd);
+  x.o = (bf16_t*)P.take(b2 * R * s.qd);
+  x.a = (bf16_t*)P.take(b2 * R * s.d);
+  x.n2 = (bf16_t*)P.take(b2 * R * s.d);
+  x.ug = (bf16_t*)P.take(b2 * R * 2 * s.F);
+  x.m = (bf16_t*)P.take(b2 * R * s.F);
+  x.rinv = (float*)P.take(f4 * R);
+  x.lse = (float*)P.take(f4 * attn_stats_pitch(R) * s.Hq);
+  x.seq_lo = (int*)P.take(sizeof(int) * s.T);
+  x.seq_hi = (int*)P.take(sizeof(int) * s.T);
+  x.rope_tab = s.rope_theta > 0.f ? (float2*)P.take(sizeof(float2) * s.T * (s.dh / 2)) : nullptr;
+  if (w) *w = x;
+  return round_up((int64_t)P.off, 256);
+}
+
+sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq,
+                         const void* x, const sbp_layer_weights* w, int32_t D, void* y, void* ws,
+                         size_t ws_bytes, hipStream_t str) {
+  sbp_status st = layer_check(desc, D);
+  if (st != SBP_OK) return st;
+  if (!x || !w || !y) return set_error(SBP_ERR_INVALID_ARG, "x, weights, y must be non-NULL");
+  const void* wp[9] = {w->g1, w->Wq, w->Wk, w->Wv, w->Wo, w->g2, w->W1, w->W3, w->W2};
+  for (int i = 0; i < 9; ++i) {
+    if (!wp[i]) return set_error(SBP_ERR_INVALID_ARG, "weight pointer %d is NULL", i);
+    if (misaligned(wp[i])) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  }
+  if (misaligned(x) || misaligned(y) || misaligned(ws) || (cu && misaligned(cu)))
+    return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (cu && nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (x == y) return set_error(SBP_ERR_INVALID_ARG, "y must not alias x");
+  const LayerShape S = layer_shape(desc, D);
+  const size_t need = layer_fwd_plan(S, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  LayerFwdWs W;
+  layer_fwd_plan(S, (char*)ws, &W);
+  const int64_t d = S.d, F = S.F, qd = S.qd, kd = S.kd;
+  const bf16_t* X = (const bf16_t*)x;
+  bf16_t* Y = (bf16_t*)y;
+  const int* seq_lo = cu ? W.seq_lo : nullptr;
+  const int* seq_hi = cu ? W.seq_hi : nullptr;
+
+  auto gemm = [&](const void* A, int64_t lda, const void* B, void* C, int64_t ldc, int64_t M,
+                  int64_t N, int64_t K, int epi, const void* R, int64_t ldr) -> sbp_status {
+    GemmParams p;
+    p.A = A; p.lda = lda; p.B = B; p.ldb = K; p.C = C; p.ldc = ldc; p.R = R; p.ldr = ldr;
+    p.M = (int)M; p.N = (int)N; p.K = (int)K;
+    return gemm_nt(SBP_BF16, epi, p, GEMM_TILE_RING, str, "gemm_layer_fwd");
+  };
+#define SBP_TRY(e_)                  \
+  do {                               \
+    sbp_status _s = (e_);            \
+    if (_s != SBP_OK) return _s;     \
+  } while (0)
+
+  if (cu) SBP_TRY(attn_seq_bounds(cu, nseq, S.T, W.seq_lo, W.seq_hi, str));
+  const bool rope = W.rope_tab != nullptr;
+  if (rope) SBP_TRY(rope_table(W.rope_tab, S.T, S.dh, (double)S.rope_theta, str));
+  const float scale = 1.0f / sqrtf((float)S.dh);
+  const int64_t Lp = attn_stats_pitch(S.Tcm);
+  for (int32_t c = 0; c < D; ++c) {
+    int64_t s0, e0;
+    chunk_bounds(S.T, D, c, &s0, &e0);
+    const int64_t Tc = e0 - s0;
+    const bf16_t* xc = X + s0 * d;
+    SBP_TRY(rmsnorm_fwd(xc, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv, str));
+    SBP_TRY(gemm(W.h1, d, w->Wk, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
+    SBP_TRY(gemm(W.h1, d, w->Wv, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
+    SBP_TRY(gemm(W.h1, d, w->Wq, W.q, qd, Tc, qd, d, EPI_OUT, nullptr, 0));
+    if (rope) {
+      SBP_TRY(rope_apply(W.Kall + s0 * kd, false, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, s0,
+                         seq_lo, W.rope_tab, false, str));
+      SBP_TRY(rope_apply(W.q, false, qd, W.q, qd, Tc, S.Hq, S.dh, s0, seq_lo, W.rope_tab, false, str));
+    }
+    AttnArgs at;
+    at.Q = W.q; at.K = W.Kall; at.V = W.Vall; at.dO = nullptr; at.O = W.o;
+    at.dQ = nullptr; at.dK = nullptr; at.dV = nullptr;
+    at.lse = W.lse; at.lse_sb = 0; at.lse_sh = Lp; at.lse_st = 1;
+    at.delta = nullptr; at.dl_sb = 0; at.dl_sh = Lp; at.dl_st = 1;
+    at.ldq = qd; at.lddq = qd; at.q_bs = 0; at.qoff = (int)s0;
+    at.T = (int)S.T; at.Hq = S.Hq; at.Hkv = S.Hkv; at.G = S.Hq / S.Hkv;
+    at.s = (int)s0; at.e = (int)e0; at.scale = scale; at.beta = 0;
+    at.seq_lo = seq_lo; at.seq_hi = seq_hi;
+    SBP_TRY(attn_fwd(at, S.dh, 1, str));
+    SBP_TRY(gemm(W.o, qd, w->Wo, W.a, d, Tc, d, qd, EPI_OUT_RESID, xc, d));          // a = x + o Wo^T
+    SBP_TRY(rmsnorm_fwd(W.a, d, w->g2, Tc, d, S.eps, W.n2, d, W.rinv, str));
+    SBP_TRY(gemm(W.n2, d, w->W1, W.ug, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
+    SBP_TRY(gemm(W.n2, d, w->W3, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
+    SBP_TRY(swiglu_fwd(W.ug, Tc, F, W.m, str));
+    SBP_TRY(gemm(W.m, F, w->W2, Y + s0 * d, d, Tc, d, F, EPI_OUT_RESID, W.a, d));   // y = a + m W2^T
+  }
+#undef SBP_TRY
+  return SBP_OK;
+}
+
 }  // namespace
 }  // namespace sbp
 
 using namespace sbp;
+
+extern "C" sbp_status sbp_layer_fwd_workspace_size(const sbp_layer_desc* desc, int32_t D,
+                                                   size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = layer_check(desc, D);
+  if (st != SBP_OK) return st;
+  *bytes = layer_fwd_plan(layer_shape(desc, D), nullptr, nullptr);
+  return SBP_OK;
+}
+
+extern "C" sbp_status sbp_layer_fwd(const sbp_layer_desc* desc, const int32_t* cu_seqlens,
+                                    int32_t nseq, const void* x, const sbp_layer_weights* w,
+                                    int32_t D, void* y, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  return layer_fwd_run(desc, cu_seqlens, nseq, x, w, D, y, ws, ws_bytes, (hipStream_t)stream);
+}
 
 extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D,
                                                    size_t* bytes) {

@@ -8,6 +8,11 @@
 // (delta_kj - xhat_k xhat_j / n) / r).
 // SwiGLU: m = silu(u) * g with silu(u) = u sigma(u); du = dm * g * silu'(u),
 // silu'(u) = sigma(u) (1 + u (1 - sigma(u))); dg = dm * silu(u).
+// Rotary position embedding (RoFormer, Su et al.): a head vector of width dh
+// is split into halves (x1, x2) and pair i turns by p * theta^(-2i/dh), p the
+// token's position: out1 = x1 cos - x2 sin, out2 = x2 cos + x1 sin.  A
+// rotation's inverse is its transpose, so gradients turn by the negative
+// angle.
 #include "common.h"
 #include "kernels.h"
 
@@ -268,6 +273,101 @@ sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t co
   const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * cols / 8, 256), 16384);
   hipLaunchKernelGGL(rows_to_bf16_kernel, dim3(grid), dim3(256), 0, st, src, lds_, rows, cols,
                      (bf16_t*)dst, ldd);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+// tab[p * half + i] = (cos, sin) of p * theta^(-2i / (2 half)).  The angle is
+// formed and reduced in double: at positions near 1e5 a float angle would
+// already be off by ~1e-2 rad from rounding alone.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int64_t P,
+                                                         int half, double theta) {
+  const int64_t n = P * half;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t p = i / half;
+    const int j = (int)(i - p * half);
+    const double f = pow(theta, -(double)j / (double)half);
+    double sn, cs;
+    sincos((double)p * f, &sn, &cs);
+    tab[i] = make_float2((float)cs, (float)sn);
+  }
+}
+
+sbp_status rope_table(float2* tab, int64_t P, int dh, double theta, hipStream_t st) {
+  if (P <= 0) return SBP_OK;
+  const int half = dh / 2;
+  ProfScope prof("rope_table", st, 0.0, 8.0 * P * half);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(P * half, 256), 8192);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, st, tab, P, half, theta);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+// One thread per (row, head, 8 consecutive pairs): reads 8 elements of each
+// half and their 8 (cos, sin), writes both halves as bf16.  In place is safe
+// (a thread reads all it writes first).
+template <bool SRC_F32>
+__global__ __launch_bounds__(256) void rope_apply_kernel(const void* __restrict__ src, int64_t lds_,
+                                                         bf16_t* dst, int64_t ldd, int64_t rows,
+                                                         int H, int dh, int64_t row0,
+                                                         const int* __restrict__ seq_lo,
+                                                         const float2* __restrict__ tab,
+                                                         float sgn) {
+  const int half = dh >> 1, G8 = half >> 3;
+  const int64_t per_row = (int64_t)H * G8, n = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row;
+    const int rem = (int)(i - r * per_row);
+    const int h = rem / G8, g = rem - h * G8;
+    const int64_t t = row0 + r;
+    const int64_t p = seq_lo ? t - seq_lo[t] : t;
+    const int64_t off = (int64_t)h * dh + g * 8;
+    float x1[8], x2[8];
+    if constexpr (SRC_F32) {
+      const float* sp = reinterpret_cast<const float*>(src) + r * lds_ + off;
+      load8f(sp, x1);
+      load8f(sp + half, x2);
+    } else {
+      const bf16_t* sp = reinterpret_cast<const bf16_t*>(src) + r * lds_ + off;
+      unpack8(*reinterpret_cast<const uint4*>(sp), x1);
+      unpack8(*reinterpret_cast<const uint4*>(sp + half), x2);
+    }
+    const float4* tp = reinterpret_cast<const float4*>(tab + p * half + g * 8);
+    float cs[8], sn[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = tp[k];
+      cs[2 * k] = v.x; sn[2 * k] = sgn * v.y;
+      cs[2 * k + 1] = v.z; sn[2 * k + 1] = sgn * v.w;
+    }
+    float o1[8], o2[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o1[k] = x1[k] * cs[k] - x2[k] * sn[k];
+      o2[k] = x2[k] * cs[k] + x1[k] * sn[k];
+    }
+    bf16_t* dp = dst + r * ldd + off;
+    *reinterpret_cast<uint4*>(dp) = pack8(o1);
+    *reinterpret_cast<uint4*>(dp + half) = pack8(o2);
+  }
+}
+
+sbp_status rope_apply(const void* src, bool src_f32, int64_t lds_, void* dst, int64_t ldd,
+                      int64_t rows, int H, int dh, int64_t row0, const int* seq_lo,
+                      const float2* tab, bool inverse, hipStream_t st) {
+  if (rows <= 0) return SBP_OK;
+  if (dh % 16 || lds_ % 8 || ldd % 8 || lds_ < (int64_t)H * dh || ldd < (int64_t)H * dh)
+    return set_error(SBP_ERR_INVALID_ARG, "rope_apply: bad head width or pitch");
+  const int64_t n = rows * H * (dh / 16);
+  const double eb = src_f32 ? 4.0 : 2.0;
+  ProfScope prof("rope_apply", st, 0.0, (eb + 2.0 + 4.0) * rows * H * dh);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(n, 256), 16384);
+  if (src_f32)
+    hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid), dim3(256), 0, st, src, lds_,
+                       (bf16_t*)dst, ldd, rows, H, dh, row0, seq_lo, tab, inverse ? -1.f : 1.f);
+  else
+    hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid), dim3(256), 0, st, src, lds_,
+                       (bf16_t*)dst, ldd, rows, H, dh, row0, seq_lo, tab, inverse ? -1.f : 1.f);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

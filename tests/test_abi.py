@@ -123,9 +123,10 @@ def test_attn_argument_errors(kw, code):
 
 
 def _layer_call(desc_kw=None, D=2, **kw):
-    d = dict(T=64, d=64, Hq=4, Hkv=2, dh=64, F=128, eps=1e-6, dtype=1)
+    d = dict(T=64, d=64, Hq=4, Hkv=2, dh=64, F=128, eps=1e-6, dtype=1, rope_theta=0.0)
     d.update(desc_kw or {})
-    desc = _lib.LayerDesc(d["T"], d["d"], d["Hq"], d["Hkv"], d["dh"], d["F"], d["eps"], d["dtype"])
+    desc = _lib.LayerDesc(d["T"], d["d"], d["Hq"], d["Hkv"], d["dh"], d["F"], d["eps"], d["dtype"],
+                          d["rope_theta"])
     w = _lib.LayerWeights(*[FAKE] * 9)
     g = _lib.LayerGrads(*[FAKE] * 9)
     for k, v in kw.get("wset", {}).items():
@@ -144,6 +145,9 @@ def _layer_call(desc_kw=None, D=2, **kw):
     ({}, 2, dict(wset={"W2": None}), _lib.SBP_ERR_INVALID_ARG),
     ({}, 2, dict(wset={"Wq": MIS}), _lib.SBP_ERR_INVALID_ARG),
     ({}, 2, dict(wsb=1), _lib.SBP_ERR_WORKSPACE),
+    (dict(rope_theta=-1.0), 2, {}, _lib.SBP_ERR_INVALID_ARG),
+    (dict(rope_theta=float("inf")), 2, {}, _lib.SBP_ERR_INVALID_ARG),
+    (dict(rope_theta=float("nan")), 2, {}, _lib.SBP_ERR_INVALID_ARG),
 ])
 def test_layer_argument_errors(desc_kw, D, kw, code):
     assert _layer_call(desc_kw, D, **kw) == code
@@ -159,6 +163,18 @@ def test_layer_workspace_is_chunk_sized():
         sizes.append(out.value)
     # MLP activations are per chunk: D = 16 needs far less than D = 1
     assert sizes[1] < sizes[0] / 3
+
+
+def test_layer_rope_workspace_adds_the_rotation_table():
+    lib = sbp.load()
+    sizes = []
+    for theta in (0.0, 1e4):
+        desc = _lib.LayerDesc(4096, 512, 8, 2, 128, 1024, 1e-6, 1, theta)
+        out = C.c_size_t(0)
+        assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 4, C.byref(out)) == 0
+        sizes.append(out.value)
+    # one (cos, sin) float pair per position and pair of a head: T * dh/2 * 8 bytes
+    assert 0 <= sizes[1] - sizes[0] - 4096 * 64 * 8 < 512
 
 
 def _packed_call(**kw):
@@ -243,3 +259,18 @@ def test_packed_layer_argument_errors_and_workspace():
     assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 2, C.byref(a)) == 0
     assert lib.sbp_layer_bwd_packed_workspace_size(C.byref(desc), 2, C.byref(b)) == 0
     assert a.value < b.value <= a.value + 2 * 256 + 2 * 64 * 4
+
+
+def test_layer_fwd_argument_errors():
+    lib = sbp.load()
+    desc = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 1, 0.0)
+    w = _lib.LayerWeights(*[FAKE] * 9)
+    call = lambda x, y, wsb, D=2: lib.sbp_layer_fwd(C.byref(desc), None, 0, x, C.byref(w), D, y,
+                                                    FAKE, wsb, None)
+    assert call(FAKE, FAKE, 1 << 40) == _lib.SBP_ERR_INVALID_ARG            # y aliases x
+    assert call(FAKE, None, 1 << 40) == _lib.SBP_ERR_INVALID_ARG
+    assert call(FAKE, MIS, 1 << 40) == _lib.SBP_ERR_INVALID_ARG
+    assert call(FAKE, FAKE + 4096, 1) == _lib.SBP_ERR_WORKSPACE
+    assert call(FAKE, FAKE + 4096, 1 << 40, D=0) == _lib.SBP_ERR_INVALID_ARG
+    out = C.c_size_t(0)
+    assert lib.sbp_layer_fwd_workspace_size(C.byref(desc), 2, C.byref(out)) == 0 and out.value > 0

@@ -146,3 +146,61 @@ def test_packed_one_sequence_equals_layer_call():
     assert torch.equal(dx, dxp)
     for k in NAMES:
         assert torch.equal(gr[k], grp[k]), k
+
+
+# ---- rotary embedding of q and k (rope_theta > 0) -------------------------
+def _gpu_rope(L, D, theta, cu=None, dy=None):
+    dev = torch.device("cuda:0")
+    w = {k: v.to(dev) for k, v in L.w.items()}
+    c = None if cu is None else torch.tensor(cu, dtype=torch.int32, device=dev)
+    dyd = (L.dy if dy is None else dy).to(dev)
+    dx, gr = sbp.layer_bwd(L.x.to(dev), dyd, w, L.Hq, L.Hkv, L.dh, L.eps, D=D, cu_seqlens=c,
+                           rope_theta=theta)
+    torch.cuda.synchronize()
+    return dx, gr
+
+
+def _oracle_rope(L, theta, cu=None, T=None, dy=None):
+    T = L.x.shape[0] if T is None else T
+    dyv = L.dy if dy is None else dy
+    w = {k: synthetic.to_f64(v) for k, v in L.w.items()}
+    return oracle.layer_bwd(synthetic.to_f64(L.x[:T]), synthetic.to_f64(dyv[:T]), w, L.Hq, L.Hkv,
+                            L.dh, L.eps, cu_seqlens=cu, rope_theta=theta)
+
+
+@pytest.mark.parametrize("T,d,Hq,Hkv,dh,F,D,theta,cu", [
+    (300, 256, 4, 2, 64, 512, 3, 10000.0, None),                      # ragged chunks, dh 64
+    (512, 512, 8, 2, 128, 1024, 4, 1e6, None),                        # dh 128, large base
+    (1000, 256, 4, 1, 128, 512, 7, 500.0, None),                      # MQA, fast rotation
+    (640, 256, 4, 2, 128, 512, 5, 10000.0, [0, 1, 1, 333, 639, 640]),  # packed: positions restart
+])
+def test_rope_parity(T, d, Hq, Hkv, dh, F, D, theta, cu):
+    L = synthetic.layer_inputs(T, d, Hq, Hkv, dh, F, "bf16", seed=3 * T + d + D, w_std=0.05,
+                               gain_std=0.1)
+    dx, gr = _gpu_rope(L, D, theta, cu)
+    rdx, rgr, _ = _oracle_rope(L, theta, cu)
+    _check(dx, gr, rdx, rgr)
+
+
+def test_rope_long_row():
+    """T = 4096 with a base of 1e4: the fastest pair turns by ~4095 rad at the
+    last position, where the table's angle reduction matters."""
+    L = synthetic.layer_inputs(4096, 256, 4, 2, 128, 512, "bf16", seed=77, w_std=0.05,
+                               gain_std=0.1)
+    dx, gr = _gpu_rope(L, 4, 1e4)
+    rdx, rgr, _ = _oracle_rope(L, 1e4)
+    _check(dx, gr, rdx, rgr)
+
+
+def test_rope_full_size_T65536_prefix():
+    """Workload-3 shapes with rotary embedding (base 1e6), upstream gradient
+    zero beyond the first P tokens: the P-token prefix backward is exact."""
+    cfg = synthetic.WORKLOADS[3]
+    L = synthetic.workload_inputs(3)
+    P = 128
+    dy = L.dy.clone()
+    dy[P:] = 0
+    dx, gr = _gpu_rope(L, cfg["D"], 1e6, dy=dy)
+    assert (dx[P:] == 0).all()
+    rdx, rgr, _ = _oracle_rope(L, 1e6, T=P, dy=dy)
+    _check(dx[:P], gr, rdx, rgr)
