@@ -24,6 +24,9 @@ chunked algorithm:
 * ``layer.layer_bwd``       -- one pre-norm decoder layer, forward and
   backward by the chain rule, optionally with the rotary position embedding
   of q and k (``layer.rope``).
+* ``model.model_bwd``       -- a stack of layers under a final RMSNorm and the
+  LM head with cross-entropy: loss and every gradient (skill page,
+  "Architecture Overview", "Layer-Wise Application").
 * ``chunked``               -- a separate fp64 *chunked* evaluation of the
   same three functions (sequence decomposition of the skill page's
   "Implementation"), used only to show that chunking is algebraically exact
@@ -37,8 +40,9 @@ No function here is "parity unpinned".
 from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_logprob, lmhead_logprob_rows
 from .attention import attn_fwd, attn_bwd, attn_bwd_sampled, attn_bwd_packed
 from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd, rope, rope_positions
+from .model import model_fwd, model_bwd
 from . import chunked
 
 __all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
            "attn_bwd_sampled", "attn_bwd_packed", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
-           "rmsnorm_bwd", "rope", "rope_positions", "chunked"]
+           "rmsnorm_bwd", "rope", "rope_positions", "model_fwd", "model_bwd", "chunked"]
