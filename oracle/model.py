@@ -40,6 +40,22 @@ def model_bwd(x0, layers, g_f, W, targets, weights=None, reduction="mean_valid",
     """Returns ``(loss, dx0, layer_grads, dg_f, dW)``; ``layer_grads[l]`` maps
     the names of ``layers[l]`` to their gradients."""
     xs = model_fwd(x0, layers, Hq, Hkv, dh, eps, cu_seqlens, rope_theta)
+    return model_bwd_at(xs, layers, g_f, W, targets, weights, reduction, Hq=Hq, Hkv=Hkv, dh=dh,
+                        eps=eps, cu_seqlens=cu_seqlens, rope_theta=rope_theta)
+
+
+def model_bwd_at(xs, layers, g_f, W, targets, weights=None, reduction="mean_valid", *, Hq, Hkv,
+                 dh, eps, cu_seqlens=None, rope_theta=0.0):
+    """The same chain rule evaluated at given layer inputs ``xs = [x_0, ...,
+    x_L]`` (kept from a forward pass): the loss and dx_L at x_L, then each
+    layer's backward at its own input x_l with upstream dx_{l+1}.  This is
+    what a streamed backward from stored layer inputs computes; it equals
+    ``model_bwd`` when ``xs[l+1] = Layer_l(xs[l])`` exactly, and otherwise
+    (inputs from a lower-precision forward) it is the exact backward at the
+    inputs actually given."""
+    xs = [np.asarray(x, dtype=np.float64) for x in xs]
+    if len(xs) != len(layers) + 1:
+        raise ValueError("xs must hold L + 1 arrays")
     h, _, _ = rmsnorm_fwd(xs[-1], g_f, eps)
     loss, dh_, dW, _, _ = lmhead_ce(h, W, targets, weights, reduction)
     dx, dg_f = rmsnorm_bwd(xs[-1], g_f, dh_, eps)

@@ -166,3 +166,29 @@ def test_packed_sequences_are_independent():
     for l in range(2):
         for k in NAMES:
             np.testing.assert_allclose(grads[l][k], g1[l][k], rtol=1e-11, atol=1e-15)
+
+
+def test_backward_at_given_inputs():
+    # at the inputs of its own forward, the backward at given layer inputs is
+    # the model backward; at perturbed inputs each layer's gradients are the
+    # single-layer backward at that layer's given input
+    Hq, Hkv, dh, eps = 2, 1, 4, 1e-6
+    x0, layers, g_f, W, y, _ = _rand(L=3, T=6, d=8, Hq=Hq, Hkv=Hkv, dh=dh, Fw=12, V=9, seed=12)
+    kw = dict(Hq=Hq, Hkv=Hkv, dh=dh, eps=eps, rope_theta=30.0)
+    ref = oracle.model_bwd(x0, layers, g_f, W, y, **kw)
+    xs = oracle.model_fwd(x0, layers, Hq, Hkv, dh, eps, None, 30.0)
+    got = oracle.model_bwd_at(xs, layers, g_f, W, y, **kw)
+    assert got[0] == ref[0]
+    np.testing.assert_array_equal(got[1], ref[1])
+    rng = np.random.default_rng(3)
+    xs2 = [x + 1e-2 * rng.normal(size=x.shape) for x in xs]
+    loss, dx0, grads, _, _ = oracle.model_bwd_at(xs2, layers, g_f, W, y, **kw)
+    hn, _, _ = oracle.rmsnorm_fwd(xs2[3], g_f, eps)
+    L3, dH, _, _, _ = oracle.lmhead_ce(hn, W, y)
+    up, _ = oracle.rmsnorm_bwd(xs2[3], g_f, dH, eps)
+    assert loss == L3
+    for l in (2, 1, 0):
+        up, g, _ = oracle.layer_bwd(xs2[l], up, layers[l], Hq, Hkv, dh, eps, rope_theta=30.0)
+        for k in NAMES:
+            np.testing.assert_array_equal(grads[l][k], g[k])
+    np.testing.assert_array_equal(dx0, up)
