@@ -18,7 +18,9 @@ library's kernel timer), and the CPU oracle timed on a bounded sample.
 Workloads (--workload): 0..4 the LM-head, attention and layer configurations
 (1 is the default), 5 the forward-only per-token log-probability on the
 weighted LM-head shapes, 6 and 7 the attention and layer workloads over 8
-packed sequences of random lengths.
+packed sequences of random lengths, 8 the whole-model backward (4 layers
+with rotary embedding under the LM head; the layer inputs come from an
+untimed chunked forward).
 """
 from __future__ import annotations
 
@@ -199,6 +201,54 @@ def layer_setup(cfg, dev):
     return step, 6.0 * P * T + 7.0 * attn_unit(Hq, dh, T, 1, cu), L
 
 
+def model_setup(cfg, dev):
+    """Whole-model backward: the layer inputs come from the chunked forward
+    (untimed); the step is one sbp_model_bwd call."""
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    M = synthetic.workload_inputs(cfg["index"], T=cfg["T"])
+    T, d, Hq, Hkv, dh, F, V = (cfg[k] for k in ("T", "d", "Hq", "Hkv", "dh", "F", "V"))
+    layers = [{k: v.to(dev) for k, v in w.items()} for w in M.layers]
+    xs = sbp.model_fwd(M.x0.to(dev), layers, Hq, Hkv, dh, M.eps, cfg["D"], None, M.rope_theta)
+    g_f, W, y = M.g_final.to(dev), M.W.to(dev), M.targets.to(dev)
+    grads = [{k: torch.empty(v.shape, dtype=torch.float32, device=dev) for k, v in w.items()}
+             for w in layers]
+    dg_f = torch.empty(d, dtype=torch.float32, device=dev)
+    dW = torch.empty(V, d, dtype=torch.float32, device=dev)
+    nb = sbp.model_bwd_workspace_size(T, d, Hq, Hkv, dh, F, len(layers), V, cfg["D_lm"], cfg["D"],
+                                      False, xs[0].dtype, M.eps, M.rope_theta)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def step():
+        return sbp.model_bwd(xs, layers, g_f, W, y, None, Hq=Hq, Hkv=Hkv, dh=dh, eps=M.eps,
+                             D_lm=cfg["D_lm"], D_layer=cfg["D"], rope_theta=M.rope_theta,
+                             grads=grads, dg_final=dg_f, dW_lm=dW, workspace=ws)
+
+    # algorithmic work: the LM head's 6 T V d plus, per layer, 6 P T for the
+    # linear maps and 7 attention units
+    P = (Hq * dh) * d + 2 * (Hkv * dh) * d + d * (Hq * dh) + 3 * F * d
+    flops = 6.0 * T * V * d + len(layers) * (6.0 * P * T + 7.0 * attn_unit(Hq, dh, T))
+    return step, flops, M
+
+
+def cpu_baseline_model(M, cfg, sample):
+    """The oracle, untouched, on the first `sample` tokens of the same input."""
+    import oracle
+    import synthetic
+    f = synthetic.to_f64
+    layers = [{k: f(v) for k, v in w.items()} for w in M.layers]
+    x0, g_f, W = f(M.x0[:sample]), f(M.g_final), f(M.W)
+    y = M.targets[:sample].numpy()
+    t0 = time.perf_counter()
+    oracle.model_bwd(x0, layers, g_f, W, y, Hq=M.Hq, Hkv=M.Hkv, dh=M.dh, eps=M.eps,
+                     rope_theta=M.rope_theta)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {sample} of {cfg['T']} tokens through all {len(layers)} layers and "
+                      f"the full LM head (fp64 NumPy, unchunked, forward included); {dt:.1f} s"}
+
+
 def cpu_baseline_layer(L, cfg, sample):
     """The oracle, untouched, on the first `sample` tokens of the same input."""
     import oracle
@@ -323,6 +373,8 @@ def main():
         step, flops, inp, n_valid = logprob_setup(cfg, dev)
     elif cfg["kind"] == "attn":
         step, flops, inp = attn_setup(cfg, dev)
+    elif cfg["kind"] == "model":
+        step, flops, inp = model_setup(cfg, dev)
     else:
         step, flops, inp = layer_setup(cfg, dev)
     dtype = cfg["dtype"]
@@ -425,6 +477,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_lmhead(inp, cfg, sample)
         elif cfg["kind"] == "attn":
             out["cpu_baseline"] = cpu_baseline_attn(inp, cfg)
+        elif cfg["kind"] == "model":
+            out["cpu_baseline"] = cpu_baseline_model(inp, cfg, args.cpu_sample or 1024)
         else:
             out["cpu_baseline"] = cpu_baseline_layer(inp, cfg, args.cpu_sample or 1024)
     print(json.dumps(out), flush=True)

@@ -307,6 +307,52 @@ sbp_status sbp_layer_fwd(const sbp_layer_desc* desc, const int32_t* cu_seqlens, 
                          void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 4. Whole decoder-only model, streamed backward layer by layer.
+ *
+ * Passage: skill page, "Architecture Overview" -- the "Layer-Wise
+ * Application" item (the chunked backward applied through the model one
+ * layer at a time) -- and "Implementation" (the LM-head logits gradient; the
+ * streaming layer backward that starts from each layer's stored input).
+ *
+ *   x_{l+1} = Layer_l(x_l), l = 0 .. L-1     (the layer of (3), desc shared)
+ *   h = RMSNorm(x_L; g_final)                (eps = desc->eps)
+ *   loss = CE(h W_lm^T; targets, weights)    (as in (1), reduction likewise)
+ *
+ * The caller keeps x_0 .. x_L from a forward pass (sbp_layer_fwd per layer)
+ * and the embedding lookup: dx0 is the gradient of x_0, its rows are what a
+ * scatter-add into the embedding table takes.  The call runs the final norm,
+ * the LM head over D_lm chunks (never the [T, V] logits), the final norm's
+ * backward, then every layer's streamed backward over D_layer chunks, last
+ * layer first.  Transient memory: the larger of the LM-head and layer
+ * workspaces plus three [T, d] bf16 buffers.
+ *
+ * desc        layer shape (bf16 only), rope_theta included
+ * n_layers    L >= 0 (0: final norm under the LM head)
+ * cu_seqlens  packed-sequence boundaries as in 2b, or NULL (one causal row)
+ * x_layers    host array of L + 1 device pointers [T, d] bf16: the input of
+ *             every layer, then the last layer's output
+ * layers      host array of L weight structs (as in 3); grads host array of
+ *             L grad structs (fp32, accumulate semantics)
+ * g_final     [d] bf16; dg_final [d] fp32 out (accumulate semantics)
+ * W_lm        [V, d] bf16; dW_lm [V, d] fp32 out (accumulate semantics)
+ * targets, weights, reduction, loss, token_loss   as in (1)
+ * dx0         [T, d] bf16 out; must not alias any x_layers entry
+ * Errors: as in (1) and (3); argument errors are returned before any launch.
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_model_bwd_workspace_size(const sbp_layer_desc* desc, int32_t n_layers,
+                                        int32_t packed, int64_t V, int32_t D_lm,
+                                        int32_t D_layer, size_t* bytes);
+
+sbp_status sbp_model_bwd(const sbp_layer_desc* desc, int32_t n_layers,
+                         const int32_t* cu_seqlens, int32_t nseq, const void* const* x_layers,
+                         const sbp_layer_weights* layers, const void* g_final, const void* W_lm,
+                         int64_t V, const int32_t* targets, const float* weights,
+                         int32_t reduction, int32_t D_lm, int32_t D_layer, int32_t accumulate,
+                         float* loss, float* token_loss, void* dx0, sbp_layer_grads* grads,
+                         float* dg_final, float* dW_lm, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ---------------------------------------------------------------------- */
 const char* sbp_status_string(int32_t status);

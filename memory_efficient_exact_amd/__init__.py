@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes as C
 import math
 from contextlib import contextmanager
-from typing import Dict, Optional
+from typing import Dict, List, Optional
 
 import torch
 
@@ -304,6 +304,101 @@ def layer_fwd(x, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
     check(lib.sbp_layer_fwd(C.byref(desc), _ptr(cu_seqlens), nseq, _ptr(x), C.byref(wst), D,
                             _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)))
     return y
+
+
+# ----------------------------------------------------------------------------
+def model_fwd(x0: torch.Tensor, layers: List[Dict[str, torch.Tensor]], Hq: int, Hkv: int,
+              dh: int, eps: float = 1e-6, D: int = 1, cu_seqlens: Optional[torch.Tensor] = None,
+              rope_theta: float = 0.0) -> List[torch.Tensor]:
+    """Forward through a stack of layers (one ``sbp_layer_fwd`` per layer);
+    returns ``[x_0, ..., x_L]``, the inputs ``sbp_model_bwd`` starts from."""
+    xs = [x0]
+    ws = None
+    for w in layers:
+        if ws is None:
+            T, d = x0.shape
+            nb = layer_fwd_workspace_size(T, d, Hq, Hkv, dh, w["W1"].shape[0], D, x0.dtype, eps,
+                                          rope_theta)
+            ws = _ws(nb, x0.device)
+        xs.append(layer_fwd(xs[-1], w, Hq, Hkv, dh, eps, D, cu_seqlens, rope_theta, workspace=ws))
+    return xs
+
+
+def model_bwd_workspace_size(T, d, Hq, Hkv, dh, F, n_layers, V, D_lm, D_layer, packed=False,
+                             dtype=torch.bfloat16, eps=1e-6, rope_theta=0.0) -> int:
+    out = C.c_size_t(0)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    check(load().sbp_model_bwd_workspace_size(C.byref(desc), n_layers, int(packed), V, D_lm,
+                                              D_layer, C.byref(out)))
+    return out.value
+
+
+def model_bwd(xs: List[torch.Tensor], layers: List[Dict[str, torch.Tensor]],
+              g_final: torch.Tensor, W_lm: torch.Tensor, targets: torch.Tensor,
+              weights: Optional[torch.Tensor] = None, *, Hq: int, Hkv: int, dh: int,
+              eps: float = 1e-6, D_lm: int = 1, D_layer: int = 1,
+              reduction: str = "mean_valid", cu_seqlens: Optional[torch.Tensor] = None,
+              rope_theta: float = 0.0, grads: Optional[List[Dict[str, torch.Tensor]]] = None,
+              dg_final: Optional[torch.Tensor] = None, dW_lm: Optional[torch.Tensor] = None,
+              accumulate: bool = False, token_loss: bool = False,
+              workspace: Optional[torch.Tensor] = None):
+    """Streamed backward of a whole model (``sbp_model_bwd``) from the layer
+    inputs ``xs = [x_0, ..., x_L]`` (``model_fwd``).  Returns ``(loss, dx0,
+    grads, dg_final, dW_lm, token_loss)`` with fp32 gradients."""
+    lib = load()
+    L = len(layers)
+    if len(xs) != L + 1:
+        raise ValueError("xs must hold the L inputs and the last output")
+    _dev(*xs, g_final, W_lm, targets, weights, cu_seqlens, dg_final, dW_lm)
+    T, d = xs[0].shape
+    V = W_lm.shape[0]
+    dev, dt = xs[0].device, xs[0].dtype
+    for x in xs:
+        if x.shape != (T, d) or x.dtype != dt:
+            raise ValueError("every x must be [T, d] of one dtype")
+    if W_lm.shape != (V, d) or W_lm.dtype != dt or g_final.shape != (d,) or g_final.dtype != dt:
+        raise ValueError("bad W_lm / g_final")
+    if targets.shape != (T,) or targets.dtype != torch.int32:
+        raise ValueError("targets must be int32 [T]")
+    if weights is not None and (weights.shape != (T,) or weights.dtype != torch.float32):
+        raise ValueError("weights must be fp32 [T]")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+                                   or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be int32 [nseq + 1]")
+    F = layers[0]["W1"].shape[0] if L else 8
+    Hd = (Hq, Hkv, dh)
+    if grads is None:
+        grads = [{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in LAYER_NAMES}
+                 for w in layers]
+    for w, g in zip(layers, grads):
+        _dev(*w.values(), *g.values())
+        for n in LAYER_NAMES:
+            if w[n].dtype != dt or g[n].dtype != torch.float32 or g[n].shape != w[n].shape:
+                raise ValueError(f"bad weight/grad {n}")
+    if dg_final is None:
+        dg_final = torch.empty(d, dtype=torch.float32, device=dev)
+    if dW_lm is None:
+        dW_lm = torch.empty(V, d, dtype=torch.float32, device=dev)
+    if dg_final.shape != (d,) or dW_lm.shape != (V, d):
+        raise ValueError("bad dg_final / dW_lm")
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    tl = torch.empty(T, dtype=torch.float32, device=dev) if token_loss else None
+    dx0 = torch.empty_like(xs[0])
+    desc = _desc(T, d, *Hd, F, eps, dt, rope_theta)
+    nb = model_bwd_workspace_size(T, d, *Hd, F, L, V, D_lm, D_layer, cu_seqlens is not None, dt,
+                                  eps, rope_theta)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
+    xp = (C.c_void_p * (L + 1))(*[x.data_ptr() for x in xs])
+    wa = (LayerWeights * max(L, 1))(*[LayerWeights(*[w[n].data_ptr() for n in LAYER_NAMES])
+                                       for w in layers])
+    ga = (LayerGrads * max(L, 1))(*[LayerGrads(*[g[n].data_ptr() for n in LAYER_NAMES])
+                                     for g in grads])
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    check(lib.sbp_model_bwd(C.byref(desc), L, _ptr(cu_seqlens), nseq, xp, wa, _ptr(g_final),
+                            _ptr(W_lm), V, _ptr(targets), _ptr(weights), _RED[reduction], D_lm,
+                            D_layer, int(accumulate), _ptr(loss), _ptr(tl), _ptr(dx0), ga,
+                            _ptr(dg_final), _ptr(dW_lm), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, dx0, grads, dg_final, dW_lm, tl
 
 
 # ----------------------------------------------------------------------------

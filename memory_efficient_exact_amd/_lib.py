@@ -56,6 +56,11 @@ SIGNATURES = {
     "sbp_layer_fwd_workspace_size": (i32, [C.POINTER(LayerDesc), i32, C.POINTER(sz)]),
     "sbp_layer_fwd": (i32, [C.POINTER(LayerDesc), vp, i32, vp, C.POINTER(LayerWeights), i32, vp,
                             vp, sz, vp]),
+    "sbp_model_bwd_workspace_size": (i32, [C.POINTER(LayerDesc), i32, i32, i64, i32, i32,
+                                           C.POINTER(sz)]),
+    "sbp_model_bwd": (i32, [C.POINTER(LayerDesc), i32, vp, i32, C.POINTER(vp),
+                            C.POINTER(LayerWeights), vp, vp, i64, vp, vp, i32, i32, i32, i32, vp,
+                            vp, vp, C.POINTER(LayerGrads), vp, vp, vp, sz, vp]),
     "sbp_status_string": (C.c_char_p, [i32]),
     "sbp_last_error": (C.c_char_p, []),
     "sbp_version": (i32, []),

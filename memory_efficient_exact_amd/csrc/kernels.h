@@ -99,6 +99,7 @@ sbp_status fill_zero_bytes(void* p, int64_t nbytes, hipStream_t st);
 // ------------------------------------------------------- decoder layer ----
 sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, int64_t d,
                        float eps, void* out, int64_t ldo, float* rinv, hipStream_t st);
+// out = resid + RMSNorm'(dn) (resid may be NULL)
 sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* dn, int64_t ldn,
                        const float* rinv, const void* resid, int64_t ldr, int64_t rows, int64_t d,
                        void* out, int64_t ldo, hipStream_t st);
@@ -111,6 +112,8 @@ sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, v
                       hipStream_t st);
 sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t cols, void* dst,
                         int64_t ldd, hipStream_t st);
+sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols, float* dst,
+                       int64_t ldd, hipStream_t st);
 // Rotary embedding: tab [P, dh/2] of (cos, sin) for positions 0 .. P-1;
 // rope_apply turns rows [0, rows) of src (H heads of width dh, fp32 or bf16,
 // pitch lds_) into dst (bf16, pitch ldd; dst == src allowed for bf16), row r

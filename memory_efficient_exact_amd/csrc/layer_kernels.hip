@@ -84,6 +84,7 @@ sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, 
 }
 
 // out = resid + (g * dn - xhat * mean(xhat * g * dn)) * rinv, one block per row
+// (resid NULL: no residual term)
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     const bf16_t* __restrict__ x, int64_t ldx, const bf16_t* __restrict__ g,
     const float* __restrict__ dn, int64_t ldn, const float* __restrict__ rinv,
@@ -106,7 +107,12 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     unpack8(*reinterpret_cast<const uint4*>(x + r * ldx + j), xv);
     unpack8(*reinterpret_cast<const uint4*>(g + j), gv);
     load8f(dn + r * ldn + j, dv);
-    unpack8(*reinterpret_cast<const uint4*>(resid + r * ldr + j), rv);
+    if (resid) {
+      unpack8(*reinterpret_cast<const uint4*>(resid + r * ldr + j), rv);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rv[k] = 0.f;
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) rv[k] += (gv[k] * dv[k] - xv[k] * ri * mean) * ri;
     *reinterpret_cast<uint4*>(out + r * ldo + j) = pack8(rv);
@@ -273,6 +279,32 @@ sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t co
   const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * cols / 8, 256), 16384);
   hipLaunchKernelGGL(rows_to_bf16_kernel, dim3(grid), dim3(256), 0, st, src, lds_, rows, cols,
                      (bf16_t*)dst, ldd);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+__global__ __launch_bounds__(256) void rows_to_f32_kernel(const bf16_t* __restrict__ src, int64_t lds_,
+                                                          int64_t rows, int64_t cols,
+                                                          float* __restrict__ dst, int64_t ldd) {
+  const int64_t C8 = cols / 8, n = rows * C8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / C8, j = (i - r * C8) * 8;
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(src + r * lds_ + j), v);
+    float4* o = reinterpret_cast<float4*>(dst + r * ldd + j);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols, float* dst,
+                       int64_t ldd, hipStream_t st) {
+  if (rows <= 0) return SBP_OK;
+  if (cols % 8 || lds_ % 8 || ldd % 8) return set_error(SBP_ERR_INVALID_ARG, "rows_to_f32: sizes must be multiples of 8");
+  ProfScope prof("rows_to_f32", st, 0.0, 6.0 * rows * cols);
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(rows * cols / 8, 256), 16384);
+  hipLaunchKernelGGL(rows_to_f32_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)src, lds_,
+                     rows, cols, dst, ldd);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

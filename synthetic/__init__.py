@@ -154,6 +154,56 @@ def layer_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int,
     return LayerInputs(x, dy, w, Hq, Hkv, dh, F, eps)
 
 
+@dataclass
+class ModelInputs:
+    x0: torch.Tensor            # [T, d]  output of the embedding lookup
+    layers: list                # per layer: name -> tensor, as LayerInputs.w
+    g_final: torch.Tensor       # [d]     final RMSNorm gain
+    W: torch.Tensor             # [V, d]  LM-head weight
+    targets: torch.Tensor       # [T]     int32, < 0 = ignored
+    weights: Optional[torch.Tensor]  # [T] fp32 or None
+    Hq: int
+    Hkv: int
+    dh: int
+    F: int
+    eps: float
+    rope_theta: float
+
+
+def model_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int, V: int, n_layers: int,
+                 dtype: str = "bf16", seed: int = 0, w_std: float = 0.02,
+                 gain_std: float = 0.0, eps: float = 1e-6, rope_theta: float = 0.0,
+                 ignore_frac: float = 0.0, weighted: bool = False,
+                 lm_w_std: Optional[float] = None) -> ModelInputs:
+    """Draw order: x0; per layer Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2; g_final;
+    W; targets; per-token weights; random ignore mask."""
+    g = _gen(seed)
+    tdt = DTYPES[dtype]
+    x0 = _normal(g, (T, d), 1.0, tdt)
+    shapes = {"Wq": (Hq * dh, d), "Wk": (Hkv * dh, d), "Wv": (Hkv * dh, d),
+              "Wo": (d, Hq * dh), "W1": (F, d), "W3": (F, d), "W2": (d, F)}
+
+    def gain():
+        gg = torch.ones(d, dtype=torch.float32)
+        if gain_std > 0.0:
+            gg = gg + gain_std * torch.randn(d, generator=g, dtype=torch.float32)
+        return gg.to(tdt)
+
+    layers = []
+    for _ in range(n_layers):
+        w = {n: _normal(g, shapes[n], w_std, tdt) for n in ("Wq", "Wk", "Wv", "Wo", "W1", "W3", "W2")}
+        w["g1"] = gain()
+        w["g2"] = gain()
+        layers.append(w)
+    g_final = gain()
+    W = _normal(g, (V, d), w_std if lm_w_std is None else lm_w_std, tdt)
+    targets = torch.randint(0, V, (T,), generator=g, dtype=torch.int64).to(torch.int32)
+    weights = torch.randn(T, generator=g, dtype=torch.float32) if weighted else None
+    if ignore_frac > 0.0:
+        targets[torch.rand(T, generator=g) < ignore_frac] = -1
+    return ModelInputs(x0, layers, g_final, W, targets, weights, Hq, Hkv, dh, F, eps, rope_theta)
+
+
 def to_f64(t: Optional[torch.Tensor]):
     """Exact upcast of a CPU tensor to a float64 numpy array (None passes)."""
     if t is None:
@@ -163,8 +213,8 @@ def to_f64(t: Optional[torch.Tensor]):
 
 # ---------------------------------------------------------------------------
 # The five workloads (index 0..4), seed = 1000 + index, the forward-only
-# log-probability workload (index 5) and packed-sequence variants of the
-# attention and layer workloads (6, 7).
+# log-probability workload (index 5), packed-sequence variants of the
+# attention and layer workloads (6, 7) and a whole-model backward (8).
 # ---------------------------------------------------------------------------
 WORKLOADS = {
     0: dict(kind="lmhead", name="lmhead_ce_f32_T256_d64_V512_D4",
@@ -188,6 +238,11 @@ WORKLOADS = {
             B=1, T=16384, Hq=32, Hkv=8, dh=128, D=8, dtype="bf16", n_seq=8),
     7: dict(kind="layer", name="layer_bwd_packed_bf16_T65536x8seq_d4096_F14336_D16",
             T=65536, d=4096, Hq=32, Hkv=8, dh=128, F=14336, D=16, dtype="bf16", n_seq=8),
+    # whole-model backward: 4 layers of workload 3's shape with rotary
+    # embedding under workload 1's LM head, chunk lengths of those workloads
+    8: dict(kind="model", name="model_bwd_bf16_L4_T16384_d4096_F14336_V128256_rope",
+            T=16384, d=4096, Hq=32, Hkv=8, dh=128, F=14336, V=128256, n_layers=4,
+            D_lm=8, D=4, rope_theta=500000.0, dtype="bf16"),
 }
 
 
@@ -225,4 +280,8 @@ def workload_inputs(index: int, **override):
     if kind == "layer":
         return layer_inputs(cfg["T"], cfg["d"], cfg["Hq"], cfg["Hkv"], cfg["dh"],
                             cfg["F"], cfg["dtype"], seed)
+    if kind == "model":
+        return model_inputs(cfg["T"], cfg["d"], cfg["Hq"], cfg["Hkv"], cfg["dh"], cfg["F"],
+                            cfg["V"], cfg["n_layers"], cfg["dtype"], seed,
+                            rope_theta=cfg["rope_theta"])
     raise ValueError(kind)

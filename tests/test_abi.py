@@ -274,3 +274,33 @@ def test_layer_fwd_argument_errors():
     assert call(FAKE, FAKE + 4096, 1 << 40, D=0) == _lib.SBP_ERR_INVALID_ARG
     out = C.c_size_t(0)
     assert lib.sbp_layer_fwd_workspace_size(C.byref(desc), 2, C.byref(out)) == 0 and out.value > 0
+
+
+def test_model_bwd_argument_errors():
+    lib = sbp.load()
+    desc = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 1, 1e4)
+    L = 2
+    w = (_lib.LayerWeights * L)(*[_lib.LayerWeights(*[FAKE] * 9) for _ in range(L)])
+    g = (_lib.LayerGrads * L)(*[_lib.LayerGrads(*[FAKE] * 9) for _ in range(L)])
+
+    def call(xs, dx0=FAKE + 8192, n=L, V=100, D_lm=2, D_layer=2, wsb=1 << 40, gf=FAKE):
+        xp = (C.c_void_p * len(xs))(*xs)
+        return lib.sbp_model_bwd(C.byref(desc), n, None, 0, xp, w, gf, FAKE, V, FAKE, None, 0,
+                                 D_lm, D_layer, 0, FAKE, None, dx0, g, FAKE, FAKE, FAKE, wsb, None)
+
+    good = [FAKE, FAKE + 256, FAKE + 512]
+    assert call(good, wsb=1) == _lib.SBP_ERR_WORKSPACE
+    assert call([FAKE, None, FAKE + 512]) == _lib.SBP_ERR_INVALID_ARG          # missing x_1
+    assert call([FAKE, MIS, FAKE + 512]) == _lib.SBP_ERR_INVALID_ARG           # misaligned
+    assert call(good, dx0=FAKE + 256) == _lib.SBP_ERR_INVALID_ARG              # dx0 aliases x_1
+    assert call(good, gf=None) == _lib.SBP_ERR_INVALID_ARG
+    assert call(good, V=0) == _lib.SBP_ERR_INVALID_ARG
+    assert call(good, D_lm=65) == _lib.SBP_ERR_INVALID_ARG
+    assert call(good, D_layer=0) == _lib.SBP_ERR_INVALID_ARG
+    assert call(good, n=-1) == _lib.SBP_ERR_INVALID_ARG
+    out = C.c_size_t(0)
+    assert lib.sbp_model_bwd_workspace_size(C.byref(desc), L, 0, 100, 2, 2, C.byref(out)) == 0
+    lay = C.c_size_t(0)
+    assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 2, C.byref(lay)) == 0
+    # three [T, d] bf16 buffers plus the inner calls' workspace (at least a layer's)
+    assert out.value >= lay.value + 3 * 64 * 64 * 2
