@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", type=int, default=1)
     p.add_argument("--D", type=int, default=None, help="override the chunk count")
+    p.add_argument("--D-lm", type=int, default=None,
+                   help="override the LM head's chunk count (whole-model workload)")
     p.add_argument("--T", type=int, default=None, help="override the sequence length")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None)
@@ -364,6 +366,8 @@ def main():
     cfg["index"] = idx
     if args.D:
         cfg["D"] = args.D
+    if args.D_lm:
+        cfg["D_lm"] = args.D_lm
     if args.T:
         cfg["T"] = args.T
     n_valid = None
