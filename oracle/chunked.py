@@ -116,6 +116,10 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D, rope_theta=0.0):
     scale = 1.0 / np.sqrt(dh)
     h1_all, _, _ = rmsnorm_fwd(x, W["g1"], eps)
     k_all = (h1_all @ W["Wk"].T).reshape(T, Hkv, dh)
+    qk_norm = "qn" in W
+    kraw_all = k_all
+    if qk_norm:
+        k_all = rmsnorm_fwd(k_all.reshape(T * Hkv, dh), W["kn"], eps)[0].reshape(T, Hkv, dh)
     pos = rope_positions(T)
     if rope_theta > 0:
         k_all = rope(k_all, pos, rope_theta)
@@ -128,6 +132,9 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D, rope_theta=0.0):
         xc = x[s:e]
         h1, _, _ = rmsnorm_fwd(xc, W["g1"], eps)
         q = (h1 @ W["Wq"].T).reshape(e - s, Hq, dh)
+        q_raw = q
+        if qk_norm:
+            q = rmsnorm_fwd(q.reshape(-1, dh), W["qn"], eps)[0].reshape(e - s, Hq, dh)
         if rope_theta > 0:
             q = rope(q, pos[s:e], rope_theta)
         ii = np.arange(s, e)[:, None]
@@ -175,6 +182,11 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D, rope_theta=0.0):
         if rope_theta > 0:
             dq = rope(dq, pos[s:e], rope_theta, inverse=True)
             dkc = rope(dkc, pos[s:e], rope_theta, inverse=True)
+        if qk_norm:
+            dq, dqn = rmsnorm_bwd(q_raw.reshape(-1, dh), W["qn"], dq.reshape(-1, dh), eps)
+            dkc, dkn = rmsnorm_bwd(kraw_all[s:e].reshape(-1, dh), W["kn"], dkc.reshape(-1, dh), eps)
+            gr["qn"] += dqn
+            gr["kn"] += dkn
         dq2 = dq.reshape(e - s, Hq * dh)
         dkc = dkc.reshape(e - s, Hkv * dh)
         dvc = dv_all[s:e].reshape(e - s, Hkv * dh)

@@ -11,6 +11,7 @@ rotary position embedding optional)::
 
     h1 = RMSNorm(x; g1)
     q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T            (heads: Hq, Hkv of width dh)
+    q, k = HeadNorm(q; qn), HeadNorm(k; kn)         (only when w has "qn", "kn")
     q, k = Rope(q), Rope(k)                         (only when theta > 0)
     o  = CausalGQA(q, k, v), scale 1/sqrt(dh)
     a  = x + o Wo^T
@@ -40,6 +41,11 @@ by the angle p * theta^(-2i/dh), p the token's position:
 A rotation's inverse is its transpose, so the backward turns the gradient by
 the negative angle.  Positions count from 0 at the start of the row, and
 from 0 at the start of each sequence when the row holds packed sequences.
+
+QK-norm (optional, as in Qwen 3; not on the pages): HeadNorm is the RMSNorm
+above applied to every head vector of width dh on its own, with one gain of
+width dh shared by all heads of q (qn) and one shared by all heads of k (kn),
+and the layer's eps.  Its backward is RMSNorm's, over (token, head) rows.
 """
 from __future__ import annotations
 
@@ -112,6 +118,11 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
     q = h1 @ W["Wq"].T
     k = h1 @ W["Wk"].T
     v = h1 @ W["Wv"].T
+    qk_norm = "qn" in W
+    q_raw, k_raw = q, k
+    if qk_norm:
+        q = rmsnorm_fwd(q.reshape(T * Hq, dh), W["qn"], eps)[0].reshape(T, Hq * dh)
+        k = rmsnorm_fwd(k.reshape(T * Hkv, dh), W["kn"], eps)[0].reshape(T, Hkv * dh)
     if rope_theta > 0:
         pos = rope_positions(T, cu_seqlens)
         q = rope(q.reshape(T, Hq, dh), pos, rope_theta).reshape(T, Hq * dh)
@@ -130,13 +141,15 @@ def layer_fwd(x, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
     su = u * _sigmoid(u)
     m = su * g
     y = a + m @ W["W2"].T
-    cache = dict(h1=h1, q=q, k=k, v=v, o=o, a=a, n2=n2, u=u, g=g, m=m, lse=lse)
+    cache = dict(h1=h1, q=q, k=k, v=v, o=o, a=a, n2=n2, u=u, g=g, m=m, lse=lse, q_raw=q_raw,
+                 k_raw=k_raw)
     return y, cache
 
 
 def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
     """Full (unchunked) backward.  Returns ``(dx, grads, y)``; ``grads`` maps
-    every name of ``w`` (g1, Wq, Wk, Wv, Wo, g2, W1, W3, W2) to its gradient.
+    every name of ``w`` (g1, Wq, Wk, Wv, Wo, g2, W1, W3, W2, and qn, kn with
+    QK-norm) to its gradient.
     ``cu_seqlens`` and ``rope_theta`` as in ``layer_fwd``."""
     x = _as64(x)
     dy = _as64(dy)
@@ -174,6 +187,11 @@ def layer_bwd(x, dy, w, Hq, Hkv, dh, eps, cu_seqlens=None, rope_theta=0.0):
         pos = rope_positions(T, cu_seqlens)
         dq = rope(dq.reshape(T, Hq, dh), pos, rope_theta, inverse=True).reshape(T, Hq * dh)
         dk = rope(dk.reshape(T, Hkv, dh), pos, rope_theta, inverse=True).reshape(T, Hkv * dh)
+    if "qn" in W:  # back through the per-head norms
+        dq, gr["qn"] = rmsnorm_bwd(c["q_raw"].reshape(T * Hq, dh), W["qn"], dq.reshape(T * Hq, dh), eps)
+        dk, gr["kn"] = rmsnorm_bwd(c["k_raw"].reshape(T * Hkv, dh), W["kn"], dk.reshape(T * Hkv, dh), eps)
+        dq = dq.reshape(T, Hq * dh)
+        dk = dk.reshape(T, Hkv * dh)
     gr["Wq"] = dq.T @ c["h1"]
     gr["Wk"] = dk.T @ c["h1"]
     gr["Wv"] = dv.T @ c["h1"]

@@ -232,8 +232,15 @@ def _torch_rope(x, theta):
 def _torch_layer_rope(x, w, Hq, Hkv, dh, eps, theta):
     T, d = x.shape
     h1 = F.rms_norm(x, (d,), weight=w["g1"], eps=eps)
-    q = _torch_rope((h1 @ w["Wq"].T).reshape(T, Hq, dh), theta).transpose(0, 1)[None]
-    k = _torch_rope((h1 @ w["Wk"].T).reshape(T, Hkv, dh), theta).transpose(0, 1)[None]
+    q = (h1 @ w["Wq"].T).reshape(T, Hq, dh)
+    k = (h1 @ w["Wk"].T).reshape(T, Hkv, dh)
+    if "qn" in w:  # QK-norm: RMSNorm over each head vector
+        q = F.rms_norm(q, (dh,), weight=w["qn"], eps=eps)
+        k = F.rms_norm(k, (dh,), weight=w["kn"], eps=eps)
+    if theta > 0:
+        q, k = _torch_rope(q, theta), _torch_rope(k, theta)
+    q = q.transpose(0, 1)[None]
+    k = k.transpose(0, 1)[None]
     v = (h1 @ w["Wv"].T).reshape(T, Hkv, dh).transpose(0, 1)[None]
     o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=dh ** -0.5,
                                        enable_gqa=(Hq != Hkv))
@@ -314,3 +321,79 @@ def test_rope_packed_sequence_starts_at_position_zero():
     assert (dx[:4] == 0).all()
     for k in NAMES:
         np.testing.assert_allclose(gr[k], gr2[k], rtol=1e-12, atol=1e-14, err_msg=k)
+
+
+# ---------------------------------------------------------------------------
+# QK-norm: RMSNorm of every q and k head vector (gains qn, kn of width dh)
+
+def _with_qk_norm(w, dh, seed):
+    rng = np.random.default_rng(seed)
+    w = dict(w)
+    w["qn"] = 1 + 0.2 * rng.normal(size=dh)
+    w["kn"] = 1 + 0.2 * rng.normal(size=dh)
+    return w
+
+
+@pytest.mark.parametrize("theta", [1e4, 0.0])
+def test_qk_norm_against_torch_autograd(theta):
+    T, d, Hq, Hkv, dh, Fw, eps = 12, 16, 4, 2, 8, 24, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=51)
+    w = _with_qk_norm(w, dh, 52)
+    xt = torch.tensor(x, requires_grad=True)
+    wt = {k: torch.tensor(v, requires_grad=True) for k, v in w.items()}
+    yt = _torch_layer_rope(xt, wt, Hq, Hkv, dh, eps, theta)
+    yt.backward(torch.tensor(dy))
+    dx, gr, y = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, rope_theta=theta)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for k in NAMES + ("qn", "kn"):
+        np.testing.assert_allclose(gr[k], wt[k].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+
+
+def test_qk_norm_finite_differences():
+    T, d, Hq, Hkv, dh, Fw, eps, theta = 6, 8, 2, 1, 4, 12, 1e-6, 5.0
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=53)
+    w = _with_qk_norm(w, dh, 54)
+    dx, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, rope_theta=theta)
+    h = 1e-6
+
+    def f(ww):
+        return float((oracle.layer_fwd(x, ww, Hq, Hkv, dh, eps, rope_theta=theta)[0] * dy).sum())
+
+    for k in ("qn", "kn", "Wq", "Wk"):
+        A = w[k]
+        fd = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            wp, wm = dict(w), dict(w)
+            wp[k], wm[k] = A.copy(), A.copy()
+            wp[k][idx] += h
+            wm[k][idx] -= h
+            fd[idx] = (f(wp) - f(wm)) / (2 * h)
+        assert np.abs(fd - gr[k]).max() <= 1e-7 * max(1.0, np.abs(gr[k]).max()), k
+
+
+def test_qk_norm_scale_invariance():
+    # scaling Wq (or Wk) leaves every head vector's direction, hence the layer,
+    # unchanged at eps = 0; so the gradient of Wq is orthogonal to Wq
+    T, d, Hq, Hkv, dh, Fw = 7, 8, 2, 1, 4, 12
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=55)
+    w = _with_qk_norm(w, dh, 56)
+    y0, _ = oracle.layer_fwd(x, w, Hq, Hkv, dh, 0.0, rope_theta=3.0)
+    w2 = dict(w, Wq=3.0 * w["Wq"], Wk=0.5 * w["Wk"])
+    y1, _ = oracle.layer_fwd(x, w2, Hq, Hkv, dh, 0.0, rope_theta=3.0)
+    np.testing.assert_allclose(y0, y1, rtol=1e-12, atol=1e-13)
+    _, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, 0.0, rope_theta=3.0)
+    assert abs((gr["Wq"] * w["Wq"]).sum()) < 1e-12 * np.abs(gr["Wq"]).sum()
+    assert abs((gr["Wk"] * w["Wk"]).sum()) < 1e-12 * np.abs(gr["Wk"]).sum()
+
+
+@pytest.mark.parametrize("D", [1, 3, 7])
+def test_qk_norm_chunked_equals_unchunked(D):
+    T, d, Hq, Hkv, dh, Fw, eps = 7, 8, 4, 2, 4, 12, 1e-6
+    x, dy, w = _rand(T, d, Hq, Hkv, dh, Fw, seed=60 + D)
+    w = _with_qk_norm(w, dh, 61)
+    dx, gr, _ = oracle.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, rope_theta=50.0)
+    dx2, gr2 = chunked.layer_bwd(x, dy, w, Hq, Hkv, dh, eps, D, rope_theta=50.0)
+    assert np.abs(dx - dx2).max() < 1e-12
+    for k in NAMES + ("qn", "kn"):
+        assert np.abs(gr[k] - gr2[k]).max() < 1e-12, k
