@@ -217,6 +217,7 @@ sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V, cons
  * gradient) and "Architecture Overview" (layer-wise application).  Layer:
  *
  *   h1 = RMSNorm(x; g1); q,k,v = h1 Wq^T, h1 Wk^T, h1 Wv^T
+ *   q, k = HeadNorm(q; qn), HeadNorm(k; kn)   (only when desc->qk_norm)
  *   q, k = Rope(q), Rope(k)        (only when desc->rope_theta > 0)
  *   o = causal GQA attention (scale 1/sqrt(dh)); a = x + o Wo^T
  *   n2 = RMSNorm(a; g2); m = silu(n2 W1^T) * (n2 W3^T); y = a + m W2^T
@@ -227,6 +228,9 @@ sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V, cons
  *   position (0 at the start of the row, or of its sequence when packed):
  *   (x1 cos - x2 sin, x2 cos + x1 sin).  The workspace then also holds a
  *   (cos, sin) table of T * dh/2 float pairs.
+ *   HeadNorm (QK-norm, as in Qwen 3; not on the pages): the RMSNorm above
+ *   over every head vector of width dh, one gain [dh] shared by all q heads
+ *   (qn) and one by all k heads (kn), eps = desc->eps.
  *
  * Keys and values of all T tokens are formed once (the causal prefix); then
  * chunks run in reverse order, each recomputing its own forward, so the MLP
@@ -246,14 +250,17 @@ typedef struct {
   float eps;
   int32_t dtype;
   float rope_theta;  /* rotary embedding base; 0 = no rotary embedding; must be >= 0 */
+  int32_t qk_norm;   /* 1: per-head RMSNorm of q and k with gains qn, kn; 0: none */
 } sbp_layer_desc;
 
 typedef struct {
   const void *g1, *Wq, *Wk, *Wv, *Wo, *g2, *W1, *W3, *W2;
+  const void *qn, *kn;  /* [dh] each; read only when desc->qk_norm */
 } sbp_layer_weights;
 
 typedef struct {
   float *g1, *Wq, *Wk, *Wv, *Wo, *g2, *W1, *W3, *W2;
+  float *qn, *kn;       /* [dh] each; written only when desc->qk_norm */
 } sbp_layer_grads;
 
 sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D, size_t* bytes);

@@ -23,7 +23,7 @@ from typing import Dict, List, Optional
 import torch
 
 from . import _lib
-from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, LayerDesc,
+from ._lib import (SBP_BF16, SBP_F32, SBP_MEAN_VALID, SBP_SUM, LAYER_NAMES, QK_NORM_NAMES, LayerDesc,
                    LayerGrads, LayerWeights, StreamBPError, check, load)
 
 __all__ = ["lmhead_ce", "lmhead_logprob", "attn_bwd", "layer_bwd", "lmhead_ce_workspace_size",
@@ -202,22 +202,37 @@ def attn_bwd(Q, K, V, dO, D: int = 1, scale: Optional[float] = None, O=None, lse
 
 
 # ----------------------------------------------------------------------------
-def _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta=0.0) -> LayerDesc:
-    return LayerDesc(T, d, Hq, Hkv, dh, F, eps, _DT[dtype], float(rope_theta))
+def _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta=0.0, qk_norm=False) -> LayerDesc:
+    return LayerDesc(T, d, Hq, Hkv, dh, F, eps, _DT[dtype], float(rope_theta), int(bool(qk_norm)))
+
+
+def _names(weights) -> tuple:
+    """The weight names a layer uses: the nine always, qn / kn with QK-norm."""
+    return LAYER_NAMES + QK_NORM_NAMES if "qn" in weights else LAYER_NAMES
+
+
+def _wstruct(weights) -> LayerWeights:
+    return LayerWeights(*[weights[n].data_ptr() if n in weights else None
+                          for n in LAYER_NAMES + QK_NORM_NAMES])
+
+
+def _gstruct(grads) -> LayerGrads:
+    return LayerGrads(*[grads[n].data_ptr() if n in grads else None
+                        for n in LAYER_NAMES + QK_NORM_NAMES])
 
 
 def layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6,
-                             rope_theta=0.0) -> int:
+                             rope_theta=0.0, qk_norm=False) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta, qk_norm)
     check(load().sbp_layer_bwd_workspace_size(C.byref(desc), D, C.byref(out)))
     return out.value
 
 
 def layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16,
-                                    eps=1e-6, rope_theta=0.0) -> int:
+                                    eps=1e-6, rope_theta=0.0, qk_norm=False) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta, qk_norm)
     check(load().sbp_layer_bwd_packed_workspace_size(C.byref(desc), D, C.byref(out)))
     return out.value
 
@@ -240,20 +255,22 @@ def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: in
     F = weights["W1"].shape[0]
     dev = x.device
     dt = x.dtype
+    names = _names(weights)
+    qk = "qn" in weights
     if grads is None:
-        grads = {n: torch.empty(weights[n].shape, dtype=torch.float32, device=dev) for n in LAYER_NAMES}
+        grads = {n: torch.empty(weights[n].shape, dtype=torch.float32, device=dev) for n in names}
     _dev(*grads.values())
-    for n in LAYER_NAMES:
+    for n in names:
         if weights[n].dtype != dt or grads[n].dtype != torch.float32 or grads[n].shape != weights[n].shape:
             raise ValueError(f"bad weight/grad {n}")
     dx = torch.empty_like(x)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta)
-    wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
-    gst = LayerGrads(*[grads[n].data_ptr() for n in LAYER_NAMES])
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta, qk)
+    wst = _wstruct(weights)
+    gst = _gstruct(grads)
     if cu_seqlens is None:
-        nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
+        nb = layer_bwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta, qk)
     else:
-        nb = layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
+        nb = layer_bwd_packed_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta, qk)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
     if cu_seqlens is None:
         check(lib.sbp_layer_bwd(C.byref(desc), _ptr(x), _ptr(dy), C.byref(wst), D,
@@ -268,9 +285,9 @@ def layer_bwd(x, dy, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: in
 
 
 def layer_fwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dtype=torch.bfloat16, eps=1e-6,
-                             rope_theta=0.0) -> int:
+                             rope_theta=0.0, qk_norm=False) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta, qk_norm)
     check(load().sbp_layer_fwd_workspace_size(C.byref(desc), D, C.byref(out)))
     return out.value
 
@@ -289,16 +306,16 @@ def layer_fwd(x, weights: Dict[str, torch.Tensor], Hq: int, Hkv: int, dh: int,
     T, d = x.shape
     F = weights["W1"].shape[0]
     dt = x.dtype
-    for n in LAYER_NAMES:
+    for n in _names(weights):
         if weights[n].dtype != dt:
             raise ValueError(f"bad weight {n}")
     y = torch.empty_like(x) if out is None else out
     if y.shape != x.shape or y.dtype != dt:
         raise ValueError("out must match x")
     _dev(y)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta)
-    wst = LayerWeights(*[weights[n].data_ptr() for n in LAYER_NAMES])
-    nb = layer_fwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dt, rope_theta, "qn" in weights)
+    wst = _wstruct(weights)
+    nb = layer_fwd_workspace_size(T, d, Hq, Hkv, dh, F, D, dt, eps, rope_theta, "qn" in weights)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, x.device)
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     check(lib.sbp_layer_fwd(C.byref(desc), _ptr(cu_seqlens), nseq, _ptr(x), C.byref(wst), D,
@@ -318,16 +335,16 @@ def model_fwd(x0: torch.Tensor, layers: List[Dict[str, torch.Tensor]], Hq: int, 
         if ws is None:
             T, d = x0.shape
             nb = layer_fwd_workspace_size(T, d, Hq, Hkv, dh, w["W1"].shape[0], D, x0.dtype, eps,
-                                          rope_theta)
+                                          rope_theta, "qn" in w)
             ws = _ws(nb, x0.device)
         xs.append(layer_fwd(xs[-1], w, Hq, Hkv, dh, eps, D, cu_seqlens, rope_theta, workspace=ws))
     return xs
 
 
 def model_bwd_workspace_size(T, d, Hq, Hkv, dh, F, n_layers, V, D_lm, D_layer, packed=False,
-                             dtype=torch.bfloat16, eps=1e-6, rope_theta=0.0) -> int:
+                             dtype=torch.bfloat16, eps=1e-6, rope_theta=0.0, qk_norm=False) -> int:
     out = C.c_size_t(0)
-    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta)
+    desc = _desc(T, d, Hq, Hkv, dh, F, eps, dtype, rope_theta, qk_norm)
     check(load().sbp_model_bwd_workspace_size(C.byref(desc), n_layers, int(packed), V, D_lm,
                                               D_layer, C.byref(out)))
     return out.value
@@ -367,12 +384,15 @@ def model_bwd(xs: List[torch.Tensor], layers: List[Dict[str, torch.Tensor]],
         raise ValueError("cu_seqlens must be int32 [nseq + 1]")
     F = layers[0]["W1"].shape[0] if L else 8
     Hd = (Hq, Hkv, dh)
+    qk = L > 0 and "qn" in layers[0]
     if grads is None:
-        grads = [{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in LAYER_NAMES}
+        grads = [{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in _names(w)}
                  for w in layers]
     for w, g in zip(layers, grads):
         _dev(*w.values(), *g.values())
-        for n in LAYER_NAMES:
+        if ("qn" in w) != qk:
+            raise ValueError("every layer must have QK-norm gains, or none")
+        for n in _names(w):
             if w[n].dtype != dt or g[n].dtype != torch.float32 or g[n].shape != w[n].shape:
                 raise ValueError(f"bad weight/grad {n}")
     if dg_final is None:
@@ -384,15 +404,13 @@ def model_bwd(xs: List[torch.Tensor], layers: List[Dict[str, torch.Tensor]],
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     tl = torch.empty(T, dtype=torch.float32, device=dev) if token_loss else None
     dx0 = torch.empty_like(xs[0])
-    desc = _desc(T, d, *Hd, F, eps, dt, rope_theta)
+    desc = _desc(T, d, *Hd, F, eps, dt, rope_theta, qk)
     nb = model_bwd_workspace_size(T, d, *Hd, F, L, V, D_lm, D_layer, cu_seqlens is not None, dt,
-                                  eps, rope_theta)
+                                  eps, rope_theta, qk)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
     xp = (C.c_void_p * (L + 1))(*[x.data_ptr() for x in xs])
-    wa = (LayerWeights * max(L, 1))(*[LayerWeights(*[w[n].data_ptr() for n in LAYER_NAMES])
-                                       for w in layers])
-    ga = (LayerGrads * max(L, 1))(*[LayerGrads(*[g[n].data_ptr() for n in LAYER_NAMES])
-                                     for g in grads])
+    wa = (LayerWeights * max(L, 1))(*[_wstruct(w) for w in layers])
+    ga = (LayerGrads * max(L, 1))(*[_gstruct(g) for g in grads])
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     check(lib.sbp_model_bwd(C.byref(desc), L, _ptr(cu_seqlens), nseq, xp, wa, _ptr(g_final),
                             _ptr(W_lm), V, _ptr(targets), _ptr(weights), _RED[reduction], D_lm,

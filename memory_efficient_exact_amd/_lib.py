@@ -20,18 +20,20 @@ sz = C.c_size_t
 
 class LayerDesc(C.Structure):
     _fields_ = [("T", i64), ("d", i64), ("Hq", i32), ("Hkv", i32), ("dh", i32),
-                ("F", i64), ("eps", f32), ("dtype", i32), ("rope_theta", f32)]
+                ("F", i64), ("eps", f32), ("dtype", i32), ("rope_theta", f32),
+                ("qk_norm", i32)]
 
 
 LAYER_NAMES = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W3", "W2")
+QK_NORM_NAMES = ("qn", "kn")  # per-head norm gains, present only with QK-norm
 
 
 class LayerWeights(C.Structure):
-    _fields_ = [(n, vp) for n in LAYER_NAMES]
+    _fields_ = [(n, vp) for n in LAYER_NAMES + QK_NORM_NAMES]
 
 
 class LayerGrads(C.Structure):
-    _fields_ = [(n, vp) for n in LAYER_NAMES]
+    _fields_ = [(n, vp) for n in LAYER_NAMES + QK_NORM_NAMES]
 
 
 # name -> (restype, argtypes); every symbol include/streambp.h declares

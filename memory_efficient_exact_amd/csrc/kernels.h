@@ -114,6 +114,16 @@ sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t co
                         int64_t ldd, hipStream_t st);
 sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols, float* dst,
                        int64_t ldd, hipStream_t st);
+// QK-norm: RMSNorm of each head vector (width dh in {64, 128}) of rows x H
+// heads, one gain g [dh] for all heads.  headnorm_fwd: out may equal x.
+// headnorm_bwd: dx (may equal dy) from x, dy; dg (+)= sum dy * xhat (beta 1
+// adds) through part [HEADNORM_PARTS, dh] floats of scratch.
+constexpr int HEADNORM_PARTS = 1024;
+sbp_status headnorm_fwd(const void* x, int64_t ldx, void* out, int64_t ldo, int64_t rows, int H,
+                        int dh, const void* g, float eps, hipStream_t st);
+sbp_status headnorm_bwd(const void* x, int64_t ldx, const void* dy, int64_t ldy, void* dx,
+                        int64_t ldd, int64_t rows, int H, int dh, const void* g, float eps,
+                        float* dg, int beta, float* part, hipStream_t st);
 // Rotary embedding: tab [P, dh/2] of (cos, sin) for positions 0 .. P-1;
 // rope_apply turns rows [0, rows) of src (H heads of width dh, fp32 or bf16,
 // pitch lds_) into dst (bf16, pitch ldd; dst == src allowed for bf16), row r

@@ -4,9 +4,10 @@
 // chunk, run the layer forward on the chunk, back-propagate the chunk's
 // upstream gradient, add the weight gradients, keep the chunk's input
 // gradient) and "Architecture Overview" (layer-wise application, causal
-// structure).  Layer (no bias; rotary embedding of q and k when
-// rope_theta > 0, not on the pages):
-//   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T; q, k = Rope(q, k)
+// structure).  Layer (no bias; optional per-head RMSNorm of q and k and
+// rotary embedding, neither on the pages):
+//   h1 = RMSNorm(x; g1); q, k, v = h1 Wq^T, h1 Wk^T, h1 Wv^T;
+//   q, k = HeadNorm(q, k) (qk_norm); q, k = Rope(q, k) (rope_theta > 0)
 //   o = causal GQA attention (packed sequences: inside each sequence only);
 //   a = x + o Wo^T
 //   n2 = RMSNorm(a; g2); [u | g] = n2 [W1; W3]^T; m = silu(u) g; y = a + m W2^T
@@ -19,7 +20,8 @@
 //   dg2 +=;  dWo += da^T o;  do = da Wo;  attention backward over the prefix
 //   (dK, dV of keys [0, e) accumulate in fp32; after chunk c, rows [s, e) are
 //   final because later chunks already added theirs and earlier chunks never
-//   reach them);  dq, dK_c turned back by the inverse rotation (if any);
+//   reach them);  dq, dK_c turned back by the inverse rotation and through
+//   the per-head norms (if any);
 //   dWq, dWk, dWv += [dq | dK_c | dV_c]^T h1;
 //   dh1 = [dq | dK_c | dV_c] [Wq; Wk; Wv];  dx = da + RMSNorm1'(dh1), dg1 +=.
 // Every product is one bf16 ring GEMM (gemm.hip).  Weight gradients contract
@@ -44,6 +46,7 @@ struct LayerShape {
   int64_t Tcm;
   float eps;
   float rope_theta;  // 0: no rotary embedding
+  bool qk_norm;      // per-head RMSNorm of q and k
 };
 
 LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
@@ -57,6 +60,7 @@ LayerShape layer_shape(const sbp_layer_desc* L, int32_t D) {
   s.Tcm = max_chunk_len(L->T, D);
   s.eps = L->eps;
   s.rope_theta = L->rope_theta;
+  s.qk_norm = L->qk_norm != 0;
   return s;
 }
 
@@ -68,6 +72,8 @@ struct LayerWs {
   float *dn, *rinv1, *rinv2, *lse, *delta, *gpart;
   int *seq_lo, *seq_hi;  // packed sequences only
   float2* rope_tab;      // rotary embedding only: [T, dh/2] (cos, sin)
+  bf16_t *Kraw, *qraw;   // QK-norm only: k before its norm [T, kd], q [Tcm, qd]
+  float* hnpart;         // QK-norm only: [HEADNORM_PARTS, dh]
 };
 
 size_t layer_plan(const LayerShape& s, bool packed, char* base, LayerWs* w) {
@@ -104,6 +110,9 @@ size_t layer_plan(const LayerShape& s, bool packed, char* base, LayerWs* w) {
   x.seq_lo = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
   x.seq_hi = packed ? (int*)P.take(sizeof(int) * s.T) : nullptr;
   x.rope_tab = s.rope_theta > 0.f ? (float2*)P.take(sizeof(float2) * s.T * (s.dh / 2)) : nullptr;
+  x.Kraw = s.qk_norm ? (bf16_t*)P.take(b2 * s.T * s.kd) : nullptr;
+  x.qraw = s.qk_norm ? (bf16_t*)P.take(b2 * R * s.qd) : nullptr;
+  x.hnpart = s.qk_norm ? (float*)P.take(f4 * HEADNORM_PARTS * s.dh) : nullptr;
   if (w) *w = x;
   return round_up((int64_t)P.off, 256);
 }
@@ -118,6 +127,7 @@ sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   if (!(L->eps >= 0.f)) return set_error(SBP_ERR_INVALID_ARG, "eps must be >= 0");
   if (!(L->rope_theta >= 0.f) || !(L->rope_theta < INFINITY))
     return set_error(SBP_ERR_INVALID_ARG, "rope_theta must be finite and >= 0 (0 = none)");
+  if (L->qk_norm != 0 && L->qk_norm != 1) return set_error(SBP_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
   if (L->dh != 64 && L->dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", L->dh);
   if (L->d % 8 || L->F % 8) return set_error(SBP_ERR_UNSUPPORTED, "d and F must be multiples of 8");
   if (L->dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "the decoder-layer backward is implemented for bf16 only");
@@ -138,6 +148,9 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     if (!wp[i] || !gp[i]) return set_error(SBP_ERR_INVALID_ARG, "weight/grad pointer %d is NULL", i);
     if (misaligned(wp[i]) || misaligned(gp[i])) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   }
+  if (desc->qk_norm && (!w->qn || !w->kn || !g->qn || !g->kn || misaligned(w->qn) ||
+                        misaligned(w->kn) || misaligned(g->qn) || misaligned(g->kn)))
+    return set_error(SBP_ERR_INVALID_ARG, "qk_norm: qn, kn weights and grads must be non-NULL and 16-byte aligned");
   if (misaligned(x) || misaligned(dy) || misaligned(dx) || misaligned(ws))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const LayerShape S = layer_shape(desc, D);
@@ -199,7 +212,12 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     chunk_bounds(S.T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
     SBP_TRY(rmsnorm_fwd(X + s0 * d, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
-    SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (S.qk_norm) {  // keys before their norm are kept for the norm's backward
+      SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kraw + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+      SBP_TRY(headnorm_fwd(W.Kraw + s0 * kd, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, w->kn, S.eps, str));
+    } else {
+      SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    }
     SBP_TRY(gemm(W.h1, d, w->Wv, d, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
     if (rope)
       SBP_TRY(rope_apply(W.Kall + s0 * kd, false, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, s0,
@@ -217,7 +235,12 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
 
     // ---- recompute the chunk's forward ----
     SBP_TRY(rmsnorm_fwd(xc, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
-    SBP_TRY(gemm(W.h1, d, w->Wq, d, W.q, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (S.qk_norm) {
+      SBP_TRY(gemm(W.h1, d, w->Wq, d, W.qraw, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+      SBP_TRY(headnorm_fwd(W.qraw, qd, W.q, qd, Tc, S.Hq, S.dh, w->qn, S.eps, str));
+    } else {
+      SBP_TRY(gemm(W.h1, d, w->Wq, d, W.q, qd, Tc, qd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    }
     if (rope)
       SBP_TRY(rope_apply(W.q, false, qd, W.q, qd, Tc, S.Hq, S.dh, s0, W.seq_lo, W.rope_tab, false, str));
     AttnArgs at;
@@ -263,6 +286,12 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
                          W.seq_lo, W.rope_tab, true, str));
     } else {
       SBP_TRY(rows_to_bf16(W.dKacc + s0 * kd, kd, Tc, kd, W.dqkv + qd, qkvd, str));
+    }
+    if (S.qk_norm) {  // through the per-head norms, in place; gain gradients
+      SBP_TRY(headnorm_bwd(W.qraw, qd, W.dqkv, qkvd, W.dqkv, qkvd, Tc, S.Hq, S.dh, w->qn, S.eps,
+                           g->qn, wb, W.hnpart, str));
+      SBP_TRY(headnorm_bwd(W.Kraw + s0 * kd, kd, W.dqkv + qd, qkvd, W.dqkv + qd, qkvd, Tc, S.Hkv,
+                           S.dh, w->kn, S.eps, g->kn, wb, W.hnpart, str));
     }
     SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
 
@@ -325,6 +354,8 @@ sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t 
     if (!wp[i]) return set_error(SBP_ERR_INVALID_ARG, "weight pointer %d is NULL", i);
     if (misaligned(wp[i])) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   }
+  if (desc->qk_norm && (!w->qn || !w->kn || misaligned(w->qn) || misaligned(w->kn)))
+    return set_error(SBP_ERR_INVALID_ARG, "qk_norm: qn, kn must be non-NULL and 16-byte aligned");
   if (misaligned(x) || misaligned(y) || misaligned(ws) || (cu && misaligned(cu)))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (cu && nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
@@ -368,6 +399,10 @@ sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t 
     SBP_TRY(gemm(W.h1, d, w->Wk, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
     SBP_TRY(gemm(W.h1, d, w->Wv, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
     SBP_TRY(gemm(W.h1, d, w->Wq, W.q, qd, Tc, qd, d, EPI_OUT, nullptr, 0));
+    if (S.qk_norm) {  // in place
+      SBP_TRY(headnorm_fwd(W.Kall + s0 * kd, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, w->kn, S.eps, str));
+      SBP_TRY(headnorm_fwd(W.q, qd, W.q, qd, Tc, S.Hq, S.dh, w->qn, S.eps, str));
+    }
     if (rope) {
       SBP_TRY(rope_apply(W.Kall + s0 * kd, false, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, s0,
                          seq_lo, W.rope_tab, false, str));

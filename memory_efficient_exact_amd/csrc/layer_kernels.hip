@@ -309,6 +309,126 @@ sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols
   return SBP_OK;
 }
 
+// QK-norm: RMSNorm of every head vector (width dh = 64 or 128) of a [rows, H
+// heads] tile with pitch ld, one gain of width dh for all heads.  One wave
+// per (row, head); lane l holds elements l and l + 64.
+template <int DH>
+__global__ __launch_bounds__(256) void headnorm_fwd_kernel(const bf16_t* x, int64_t ldx,
+                                                           bf16_t* out, int64_t ldo, int64_t rows,
+                                                           int H, const bf16_t* __restrict__ g,
+                                                           float eps) {
+  constexpr int NE = DH / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= rows * H) return;
+  const int64_t r = i / H;
+  const int h = (int)(i - r * H);
+  const bf16_t* xr = x + r * ldx + (int64_t)h * DH;
+  float v[NE], ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    v[j] = bf2f(xr[lane + 64 * j]);
+    ss += v[j] * v[j];
+  }
+  const float ri = rsqrtf(wave_sum(ss) / (float)DH + eps);
+  bf16_t* orow = out + r * ldo + (int64_t)h * DH;
+#pragma unroll
+  for (int j = 0; j < NE; ++j) orow[lane + 64 * j] = f2bf(v[j] * ri * bf2f(g[lane + 64 * j]));
+}
+
+// dx = (g dy - xhat mean(xhat g dy)) / r per head vector (r recomputed from
+// x), in place over dy allowed; per-block partial sums of dy * xhat into
+// part[blockIdx.x][DH] (summed afterwards, so the result is deterministic).
+template <int DH>
+__global__ __launch_bounds__(256) void headnorm_bwd_kernel(const bf16_t* __restrict__ x, int64_t ldx,
+                                                           const bf16_t* dy, int64_t ldy,
+                                                           bf16_t* dx, int64_t ldd, int64_t rows,
+                                                           int H, const bf16_t* __restrict__ g,
+                                                           float eps, float* __restrict__ part) {
+  constexpr int NE = DH / 64;
+  __shared__ float sh[4][DH];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float gv[NE], acc[NE];
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    gv[j] = bf2f(g[lane + 64 * j]);
+    acc[j] = 0.f;
+  }
+  const int64_t n = rows * H;
+  for (int64_t i = (int64_t)blockIdx.x * 4 + w; i < n; i += (int64_t)gridDim.x * 4) {
+    const int64_t r = i / H;
+    const int h = (int)(i - r * H);
+    const bf16_t* xr = x + r * ldx + (int64_t)h * DH;
+    const bf16_t* dr = dy + r * ldy + (int64_t)h * DH;
+    float xv[NE], dv[NE], ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      xv[j] = bf2f(xr[lane + 64 * j]);
+      dv[j] = bf2f(dr[lane + 64 * j]);
+      ss += xv[j] * xv[j];
+    }
+    const float ri = rsqrtf(wave_sum(ss) / (float)DH + eps);
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      xv[j] *= ri;  // xhat
+      dot += xv[j] * gv[j] * dv[j];
+      acc[j] += dv[j] * xv[j];
+    }
+    const float mean = wave_sum(dot) / (float)DH;
+    bf16_t* orow = dx + r * ldd + (int64_t)h * DH;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) orow[lane + 64 * j] = f2bf((gv[j] * dv[j] - xv[j] * mean) * ri);
+  }
+#pragma unroll
+  for (int j = 0; j < NE; ++j) sh[w][lane + 64 * j] = acc[j];
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int c = lane + 64 * j;
+      part[(int64_t)blockIdx.x * DH + c] = (sh[0][c] + sh[1][c]) + (sh[2][c] + sh[3][c]);
+    }
+  }
+}
+
+sbp_status headnorm_fwd(const void* x, int64_t ldx, void* out, int64_t ldo, int64_t rows, int H,
+                        int dh, const void* g, float eps, hipStream_t st) {
+  if (rows <= 0) return SBP_OK;
+  if ((dh != 64 && dh != 128) || ldx < (int64_t)H * dh || ldo < (int64_t)H * dh)
+    return set_error(SBP_ERR_INVALID_ARG, "headnorm_fwd: bad head width or pitch");
+  ProfScope prof("headnorm_fwd", st, 0.0, 4.0 * rows * H * dh);
+  const unsigned grid = (unsigned)cdiv(rows * H, 4);
+  if (dh == 128)
+    hipLaunchKernelGGL(headnorm_fwd_kernel<128>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, ldx,
+                       (bf16_t*)out, ldo, rows, H, (const bf16_t*)g, eps);
+  else
+    hipLaunchKernelGGL(headnorm_fwd_kernel<64>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, ldx,
+                       (bf16_t*)out, ldo, rows, H, (const bf16_t*)g, eps);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
+sbp_status headnorm_bwd(const void* x, int64_t ldx, const void* dy, int64_t ldy, void* dx,
+                        int64_t ldd, int64_t rows, int H, int dh, const void* g, float eps,
+                        float* dg, int beta, float* part, hipStream_t st) {
+  if (rows <= 0) return SBP_OK;
+  if ((dh != 64 && dh != 128) || ldx < (int64_t)H * dh || ldy < (int64_t)H * dh || ldd < (int64_t)H * dh)
+    return set_error(SBP_ERR_INVALID_ARG, "headnorm_bwd: bad head width or pitch");
+  ProfScope prof("headnorm_bwd", st, 0.0, 6.0 * rows * H * dh);
+  const int nb = (int)std::min<int64_t>(cdiv(rows * H, 4), HEADNORM_PARTS);
+  if (dh == 128)
+    hipLaunchKernelGGL(headnorm_bwd_kernel<128>, dim3(nb), dim3(256), 0, st, (const bf16_t*)x, ldx,
+                       (const bf16_t*)dy, ldy, (bf16_t*)dx, ldd, rows, H, (const bf16_t*)g, eps, part);
+  else
+    hipLaunchKernelGGL(headnorm_bwd_kernel<64>, dim3(nb), dim3(256), 0, st, (const bf16_t*)x, ldx,
+                       (const bf16_t*)dy, ldy, (bf16_t*)dx, ldd, rows, H, (const bf16_t*)g, eps, part);
+  SBP_LAUNCH_CHECK();
+  hipLaunchKernelGGL(gain_sum_kernel, dim3((unsigned)cdiv(dh, 256)), dim3(256), 0, st, part, nb, dh,
+                     dg, beta);
+  SBP_LAUNCH_CHECK();
+  return SBP_OK;
+}
+
 // tab[p * half + i] = (cos, sin) of p * theta^(-2i / (2 half)).  The angle is
 // formed and reduced in double: at positions near 1e5 a float angle would
 // already be off by ~1e-2 rad from rounding alone.

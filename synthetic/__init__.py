@@ -131,8 +131,9 @@ class LayerInputs:
 def layer_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int,
                  dtype: str = "bf16", seed: int = 0, w_std: float = 0.02,
                  gain_std: float = 0.0, eps: float = 1e-6,
-                 x_std: float = 1.0, dy_std: float = 1.0) -> LayerInputs:
-    """Draw order: x, Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2, dy.
+                 x_std: float = 1.0, dy_std: float = 1.0, qk_norm: bool = False) -> LayerInputs:
+    """Draw order: x, Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2, dy, then (QK-norm)
+    qn, kn.
 
     Gains are exactly one when ``gain_std`` is 0 (the benchmark setting) and
     1 + N(0, gain_std^2) otherwise (to exercise the gain gradients).
@@ -151,6 +152,12 @@ def layer_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int,
             gg = gg + gain_std * torch.randn(d, generator=g, dtype=torch.float32)
         w[name] = gg.to(tdt)
     dy = _normal(g, (T, d), dy_std, tdt)
+    if qk_norm:
+        for name in ("qn", "kn"):
+            gg = torch.ones(dh, dtype=torch.float32)
+            if gain_std > 0.0:
+                gg = gg + gain_std * torch.randn(dh, generator=g, dtype=torch.float32)
+            w[name] = gg.to(tdt)
     return LayerInputs(x, dy, w, Hq, Hkv, dh, F, eps)
 
 
@@ -174,19 +181,20 @@ def model_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int, V: int, n_l
                  dtype: str = "bf16", seed: int = 0, w_std: float = 0.02,
                  gain_std: float = 0.0, eps: float = 1e-6, rope_theta: float = 0.0,
                  ignore_frac: float = 0.0, weighted: bool = False,
-                 lm_w_std: Optional[float] = None) -> ModelInputs:
-    """Draw order: x0; per layer Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2; g_final;
-    W; targets; per-token weights; random ignore mask."""
+                 lm_w_std: Optional[float] = None, qk_norm: bool = False) -> ModelInputs:
+    """Draw order: x0; per layer Wq, Wk, Wv, Wo, W1, W3, W2, g1, g2 (then qn,
+    kn with QK-norm); g_final; W; targets; per-token weights; random ignore
+    mask."""
     g = _gen(seed)
     tdt = DTYPES[dtype]
     x0 = _normal(g, (T, d), 1.0, tdt)
     shapes = {"Wq": (Hq * dh, d), "Wk": (Hkv * dh, d), "Wv": (Hkv * dh, d),
               "Wo": (d, Hq * dh), "W1": (F, d), "W3": (F, d), "W2": (d, F)}
 
-    def gain():
-        gg = torch.ones(d, dtype=torch.float32)
+    def gain(n=d):
+        gg = torch.ones(n, dtype=torch.float32)
         if gain_std > 0.0:
-            gg = gg + gain_std * torch.randn(d, generator=g, dtype=torch.float32)
+            gg = gg + gain_std * torch.randn(n, generator=g, dtype=torch.float32)
         return gg.to(tdt)
 
     layers = []
@@ -194,6 +202,9 @@ def model_inputs(T: int, d: int, Hq: int, Hkv: int, dh: int, F: int, V: int, n_l
         w = {n: _normal(g, shapes[n], w_std, tdt) for n in ("Wq", "Wk", "Wv", "Wo", "W1", "W3", "W2")}
         w["g1"] = gain()
         w["g2"] = gain()
+        if qk_norm:
+            w["qn"] = gain(dh)
+            w["kn"] = gain(dh)
         layers.append(w)
     g_final = gain()
     W = _normal(g, (V, d), w_std if lm_w_std is None else lm_w_std, tdt)

@@ -304,3 +304,25 @@ def test_model_bwd_argument_errors():
     assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 2, C.byref(lay)) == 0
     # three [T, d] bf16 buffers plus the inner calls' workspace (at least a layer's)
     assert out.value >= lay.value + 3 * 64 * 64 * 2
+
+
+def test_layer_qk_norm_arguments():
+    lib = sbp.load()
+    desc = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 1, 0.0, 1)
+    w = _lib.LayerWeights(*[FAKE] * 9)          # qn, kn NULL
+    g = _lib.LayerGrads(*[FAKE] * 11)
+    assert lib.sbp_layer_bwd(C.byref(desc), FAKE, FAKE, C.byref(w), 2, 0, FAKE, C.byref(g), FAKE,
+                             1 << 40, None) == _lib.SBP_ERR_INVALID_ARG
+    assert lib.sbp_layer_fwd(C.byref(desc), None, 0, FAKE, C.byref(w), 2, FAKE + 4096, FAKE,
+                             1 << 40, None) == _lib.SBP_ERR_INVALID_ARG
+    bad = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 1, 0.0, 2)
+    out = C.c_size_t(0)
+    assert lib.sbp_layer_bwd_workspace_size(C.byref(bad), 2, C.byref(out)) == _lib.SBP_ERR_INVALID_ARG
+    sizes = []
+    for qk in (0, 1):
+        dsc = _lib.LayerDesc(4096, 512, 8, 2, 128, 1024, 1e-6, 1, 0.0, qk)
+        assert lib.sbp_layer_bwd_workspace_size(C.byref(dsc), 4, C.byref(out)) == 0
+        sizes.append(out.value)
+    # keys before their norm [T, kd], one chunk's q [T_c, qd] (bf16), gain partials
+    extra = 2 * 4096 * 256 + 2 * 1024 * 1024 + 4 * 1024 * 128
+    assert 0 <= sizes[1] - sizes[0] - extra < 1024

@@ -204,3 +204,36 @@ def test_rope_full_size_T65536_prefix():
     assert (dx[P:] == 0).all()
     rdx, rgr, _ = _oracle_rope(L, 1e6, T=P, dy=dy)
     _check(dx[:P], gr, rdx, rgr)
+
+
+# ---- QK-norm: per-head RMSNorm of q and k (gains qn, kn) -----------------
+@pytest.mark.parametrize("T,d,Hq,Hkv,dh,F,D,theta,cu", [
+    (300, 256, 4, 2, 64, 512, 3, 1e4, None),                          # dh 64, rotary
+    (512, 512, 8, 2, 128, 1024, 4, 0.0, None),                        # no rotation
+    (640, 256, 4, 2, 128, 512, 5, 1e6, [0, 1, 1, 333, 639, 640]),      # packed
+])
+def test_qk_norm_parity(T, d, Hq, Hkv, dh, F, D, theta, cu):
+    L = synthetic.layer_inputs(T, d, Hq, Hkv, dh, F, "bf16", seed=11 * T + d + D, w_std=0.05,
+                               gain_std=0.1, qk_norm=True)
+    dx, gr = _gpu_rope(L, D, theta, cu)
+    rdx, rgr, _ = _oracle_rope(L, theta, cu)
+    _check(dx, gr, rdx, rgr)
+    for k in ("qn", "kn"):
+        assert normwise(gr[k].cpu().numpy(), rgr[k]) <= TOL, k
+
+
+def test_qk_norm_full_size_T65536_prefix():
+    """Workload-3 shapes with QK-norm and rotary embedding (base 1e6), upstream
+    gradient zero beyond the first P tokens: the P-token prefix is exact."""
+    cfg = synthetic.WORKLOADS[3]
+    L = synthetic.layer_inputs(cfg["T"], cfg["d"], cfg["Hq"], cfg["Hkv"], cfg["dh"], cfg["F"],
+                               "bf16", seed=1003, gain_std=0.1, qk_norm=True)
+    P = 128
+    dy = L.dy.clone()
+    dy[P:] = 0
+    dx, gr = _gpu_rope(L, cfg["D"], 1e6, dy=dy)
+    assert (dx[P:] == 0).all()
+    rdx, rgr, _ = _oracle_rope(L, 1e6, T=P, dy=dy)
+    _check(dx[:P], gr, rdx, rgr)
+    for k in ("qn", "kn"):
+        assert normwise(gr[k].cpu().numpy(), rgr[k]) <= TOL, k

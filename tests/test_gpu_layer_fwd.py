@@ -82,3 +82,11 @@ def test_full_size_T65536_first_and_last_sequence():
                                    rope_theta=1e6)
     assert normwise(yp[T - P:], ref_tail) <= TOL
     assert normwise(yp[:P], ref_head) <= TOL
+
+
+@pytest.mark.parametrize("theta,cu", [(1e4, None), (0.0, [0, 100, 257])])
+def test_qk_norm_parity(theta, cu):
+    L = synthetic.layer_inputs(257, 256, 4, 2, 128, 512, "bf16", seed=23, w_std=0.05,
+                               gain_std=0.1, qk_norm=True)
+    y = _gpu(L, 3, theta, cu)
+    assert normwise(y, _oracle(L, theta, cu)) <= TOL

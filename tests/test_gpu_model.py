@@ -90,6 +90,18 @@ def test_parity(L, T, D_lm, D_layer, theta, cu, weighted):
     _check(out, ref, _loss_scale(M) if cu is None else abs(ref[0]))
 
 
+def test_qk_norm_parity():
+    M = synthetic.model_inputs(300, 256, 4, 2, 64, 512, 1000, 2, "bf16", seed=31, w_std=0.05,
+                               gain_std=0.1, rope_theta=1e6, ignore_frac=0.1, lm_w_std=0.1,
+                               qk_norm=True)
+    out = _gpu(M, 3, 2)
+    ref = _oracle(M)
+    _check(out, ref, _loss_scale(M))
+    for l, g in enumerate(out[2]):
+        for k in ("qn", "kn"):
+            assert normwise(g[k].cpu().numpy(), ref[2][l][k]) <= TOL, (l, k)
+
+
 def test_accumulate_adds_into_every_gradient():
     M = synthetic.model_inputs(256, 128, 2, 1, 64, 256, 500, 2, "bf16", seed=5, w_std=0.05,
                                gain_std=0.1, rope_theta=1e4, lm_w_std=0.1)
