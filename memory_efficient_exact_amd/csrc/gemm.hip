@@ -373,6 +373,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   const int ke = min(Kpad, kb + p.k_per_split);
   const bf16_t* zero = reinterpret_cast<const bf16_t*>(&g_ring_zero);
 
+  // B rows past b_split come from the second buffer (tile-aligned split)
+  const void* Bsel = p.B;
+  if (p.B2 && n0 >= p.b_split)
+    Bsel = reinterpret_cast<const bf16_t*>(p.B2) - (int64_t)p.b_split * p.ldb;
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   // row-major: instruction j fills LDS rows 256 opnd + rbase + 8j + lane / 8,
   // slot lane % 8, with logical chunk slot ^ ((row >> 1) & 7)
   const int chunk_even = (lane & 7) ^ (lane >> 4), chunk_odd = (lane & 7) ^ (4 + (lane >> 4));
-  const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? p.B : p.A);
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(opnd ? Bsel : p.A);
   const int64_t ld = opnd ? p.ldb : p.lda;
   const int lim = opnd ? p.N : p.M;
   const int r0 = (opnd ? n0 : m0) + rbase + (lane >> 3);
@@ -606,6 +611,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   // (after the trailing refill and prefetch DMAs have landed).
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   __syncthreads();
+  // output tiles past a split go to that split's buffer (whole tiles: the
+  // splits are multiples of 256)
+  if constexpr (EPI == EPI_OUT || EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+    constexpr int64_t es = EPI == EPI_OUT ? 2 : 4;
+    const int at = p.c_split_cols ? n0 : m0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (p.Cx[i] && at >= p.c_split[i])
+        p.C = reinterpret_cast<char*>(p.Cx[i]) -
+              (int64_t)p.c_split[i] * (p.c_split_cols ? 1 : p.ldc) * es;
+  }
   float* W = reinterpret_cast<float*>((wave < 2 ? L0 : L1)) + (wave & 1) * (32 * 128);
   float beta = (float)p.beta;
   if (EPI == EPI_F32_ACC && p.beta_zero && *p.beta_zero) beta = 0.f;
@@ -866,6 +882,14 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
     return set_error(SBP_ERR_UNSUPPORTED, "target-value epilogue needs row-major operands and its row arrays");
   if ((p.a_kmajor || p.b_kmajor) && !(tile == GEMM_TILE_RING && ring_ok && p.a_kmajor == p.b_kmajor))
     return set_error(SBP_ERR_UNSUPPORTED, "K-major GEMM operands need the bf16 ring GEMM, both K-major");
+  if (p.B2 || p.Cx[0] || p.Cx[1]) {
+    const bool ok = tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 &&
+                    (epi == EPI_OUT || epi == EPI_F32 || epi == EPI_F32_ACC) &&
+                    (!p.B2 || (!p.b_kmajor && p.b_split > 0 && p.b_split % 256 == 0)) &&
+                    (!p.Cx[0] || (p.c_split[0] > 0 && p.c_split[0] % 256 == 0)) &&
+                    (!p.Cx[1] || (p.Cx[0] && p.c_split[1] > p.c_split[0] && p.c_split[1] % 256 == 0));
+    if (!ok) return set_error(SBP_ERR_UNSUPPORTED, "GEMM operand/output splits need the bf16 ring GEMM and tile-aligned splits");
+  }
   if (dtype == SBP_BF16) {
     if (tile == GEMM_TILE_RING && ring_ok)
       launch_bf16_ring(epi, p, st);

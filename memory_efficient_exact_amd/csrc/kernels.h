@@ -41,6 +41,18 @@ struct GemmParams {
   int64_t ld_stats = 0;
   const int32_t* row_target = nullptr;  // EPI_LSE_TGT: [M] column of each row (< 0: none)
   float* target_out = nullptr;          // EPI_LSE_TGT: [M]
+  // bf16 ring GEMM only (k_split 1): tile-aligned splits (multiples of 256)
+  // that let one launch cover products whose operands or results live in
+  // separate buffers.  Rows n >= b_split of a row-major B come from B2 (row n
+  // at B2 + (n - b_split) ldb).  Output tiles at or past c_split[i] (rows, or
+  // columns if c_split_cols) go to Cx[i]: element (r, c) at Cx[i] +
+  // (r - c_split[i]) ldc + c, or r ldc + (c - c_split[i]); c_split[0] <
+  // c_split[1], the last one reached wins.  EPI_OUT, EPI_F32, EPI_F32_ACC.
+  const void* B2 = nullptr;
+  int b_split = 0;
+  void* Cx[2] = {nullptr, nullptr};
+  int c_split[2] = {0, 0};
+  int c_split_cols = 0;
   int tiles_m = 0, tiles_n = 0;    // filled by the launcher
 };
 

@@ -187,6 +187,39 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
                      int64_t N, int64_t Tc, int beta) -> sbp_status {
     return gemm(A, lda, B, ldb, G, N, M, N, Tc, EPI_F32_ACC, beta, nullptr, 0, "gemm_layer_dW", 1);
   };
+  // Merged launches where the shapes allow tile-aligned splits (K and V
+  // projections: columns at kd; W1 and W3: B rows at F; their gradients: C
+  // rows at F, at qd and qd + kd): one launch instead of two or three that
+  // would each leave most of the chip idle.
+  const bool merge_kv = kd % 256 == 0, merge_13 = F % 256 == 0;
+  const bool merge_qkv = qd % 256 == 0 && kd % 256 == 0;
+  // [K | V] (Tc x 2kd) = h1 [Wk; Wv]^T into two row arrays of pitch kd
+  auto gemm_kv = [&](const void* h1, void* Kdst, void* Vdst, int64_t Tc) -> sbp_status {
+    GemmParams p;
+    p.A = h1; p.lda = d; p.B = w->Wk; p.B2 = w->Wv; p.b_split = (int)kd; p.ldb = d;
+    p.C = Kdst; p.ldc = kd; p.Cx[0] = Vdst; p.c_split[0] = (int)kd; p.c_split_cols = 1;
+    p.M = (int)Tc; p.N = (int)(2 * kd); p.K = (int)d;
+    return gemm_nt(SBP_BF16, EPI_OUT, p, GEMM_TILE_RING, str, "gemm_layer_fwd");
+  };
+  // [u | g] = n2 [W1; W3]^T
+  auto gemm_13 = [&](const void* n2, void* ug, int64_t Tc) -> sbp_status {
+    GemmParams p;
+    p.A = n2; p.lda = d; p.B = w->W1; p.B2 = w->W3; p.b_split = (int)F; p.ldb = d;
+    p.C = ug; p.ldc = 2 * F; p.M = (int)Tc; p.N = (int)(2 * F); p.K = (int)d;
+    return gemm_nt(SBP_BF16, EPI_OUT, p, GEMM_TILE_RING, str, "gemm_layer_fwd");
+  };
+  // G (+)= A^T n over the chunk's tokens, with A [Tc, M] K-major and the
+  // result rows split over up to three gradient arrays of pitch N
+  auto gemm_wg_split = [&](const void* A, int64_t lda, const void* Bm, int64_t ldb, int64_t M,
+                           int64_t N, int64_t Tc, int beta, float* G0, float* G1, int s1,
+                           float* G2, int s2) -> sbp_status {
+    GemmParams p;
+    p.A = A; p.lda = lda; p.B = Bm; p.ldb = ldb; p.C = G0; p.ldc = N;
+    p.Cx[0] = G1; p.c_split[0] = s1; p.Cx[1] = G2; p.c_split[1] = s2;
+    p.M = (int)M; p.N = (int)N; p.K = (int)Tc; p.beta = beta;
+    p.a_kmajor = p.b_kmajor = 1;
+    return gemm_nt(SBP_BF16, EPI_F32_ACC, p, GEMM_TILE_RING, str, "gemm_layer_dW");
+  };
   auto tr = [&](const void* src, int64_t ld_src, int64_t rows, int64_t cols, void* dst,
                 int64_t ld_dst, int64_t rows_pad) -> sbp_status {
     return transpose_pad(SBP_BF16, src, ld_src, rows, cols, dst, ld_dst, rows_pad, nullptr, str);
@@ -212,13 +245,16 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     chunk_bounds(S.T, D, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
     SBP_TRY(rmsnorm_fwd(X + s0 * d, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv1, str));
-    if (S.qk_norm) {  // keys before their norm are kept for the norm's backward
-      SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kraw + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
-      SBP_TRY(headnorm_fwd(W.Kraw + s0 * kd, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, w->kn, S.eps, str));
+    // keys before their norm are kept (QK-norm) for the norm's backward
+    bf16_t* kdst = (S.qk_norm ? W.Kraw : W.Kall) + s0 * kd;
+    if (merge_kv) {
+      SBP_TRY(gemm_kv(W.h1, kdst, W.Vall + s0 * kd, Tc));
     } else {
-      SBP_TRY(gemm(W.h1, d, w->Wk, d, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+      SBP_TRY(gemm(W.h1, d, w->Wk, d, kdst, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+      SBP_TRY(gemm(W.h1, d, w->Wv, d, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
     }
-    SBP_TRY(gemm(W.h1, d, w->Wv, d, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (S.qk_norm)
+      SBP_TRY(headnorm_fwd(W.Kraw + s0 * kd, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, w->kn, S.eps, str));
     if (rope)
       SBP_TRY(rope_apply(W.Kall + s0 * kd, false, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, s0,
                          W.seq_lo, W.rope_tab, false, str));
@@ -257,16 +293,24 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     SBP_TRY(attn_fwd(at, S.dh, 1, str));
     SBP_TRY(gemm(W.o, qd, w->Wo, qd, W.a, d, Tc, d, qd, EPI_OUT_RESID, 0, xc, d, "gemm_layer_fwd"));
     SBP_TRY(rmsnorm_fwd(W.a, d, w->g2, Tc, d, S.eps, W.n2, d, W.rinv2, str));
-    SBP_TRY(gemm(W.n2, d, w->W1, d, W.ug, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
-    SBP_TRY(gemm(W.n2, d, w->W3, d, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    if (merge_13) {
+      SBP_TRY(gemm_13(W.n2, W.ug, Tc));
+    } else {
+      SBP_TRY(gemm(W.n2, d, w->W1, d, W.ug, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+      SBP_TRY(gemm(W.n2, d, w->W3, d, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_fwd"));
+    }
     SBP_TRY(swiglu_fwd(W.ug, Tc, F, W.mdm, str));
 
     // ---- MLP backward ----
     SBP_TRY(gemm_wg(dyc, d, W.mdm, F, g->W2, d, F, Tc, wb));                    // dW2 += dy^T m
     SBP_TRY(gemm(dyc, d, W.W2T, d, W.mdm, F, Tc, F, d, EPI_OUT, 0, nullptr, 0, "gemm_layer_dX"));  // dm
     SBP_TRY(swiglu_bwd(W.mdm, W.ug, Tc, F, W.dudg, str));
-    SBP_TRY(gemm_wg(W.dudg, 2 * F, W.n2, d, g->W1, F, d, Tc, wb));             // dW1 += du^T n2
-    SBP_TRY(gemm_wg(W.dudg + F, 2 * F, W.n2, d, g->W3, F, d, Tc, wb));         // dW3 += dg^T n2
+    if (merge_13) {  // [dW1; dW3] += [du | dg]^T n2
+      SBP_TRY(gemm_wg_split(W.dudg, 2 * F, W.n2, d, 2 * F, d, Tc, wb, g->W1, g->W3, (int)F, nullptr, 0));
+    } else {
+      SBP_TRY(gemm_wg(W.dudg, 2 * F, W.n2, d, g->W1, F, d, Tc, wb));             // dW1 += du^T n2
+      SBP_TRY(gemm_wg(W.dudg + F, 2 * F, W.n2, d, g->W3, F, d, Tc, wb));         // dW3 += dg^T n2
+    }
     SBP_TRY(gemm(W.dudg, 2 * F, W.W13T, 2 * F, W.dn, d, Tc, d, 2 * F, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(W.a, d, w->g2, W.dn, d, W.rinv2, dyc, d, Tc, d, W.da, d, str));
     SBP_TRY(gain_grad(W.dn, d, W.a, d, W.rinv2, Tc, d, g->g2, wb, W.gpart, str));
@@ -296,9 +340,14 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     SBP_TRY(rows_to_bf16(W.dVacc + s0 * kd, kd, Tc, kd, W.dqkv + qd + kd, qkvd, str));
 
     // ---- q, k, v projections and the first norm ----
-    SBP_TRY(gemm_wg(W.dqkv, qkvd, W.h1, d, g->Wq, qd, d, Tc, wb));             // dWq += dq^T h1
-    SBP_TRY(gemm_wg(W.dqkv + qd, qkvd, W.h1, d, g->Wk, kd, d, Tc, wb));        // dWk += dK^T h1
-    SBP_TRY(gemm_wg(W.dqkv + qd + kd, qkvd, W.h1, d, g->Wv, kd, d, Tc, wb));   // dWv += dV^T h1
+    if (merge_qkv) {  // [dWq; dWk; dWv] += [dq | dK | dV]^T h1
+      SBP_TRY(gemm_wg_split(W.dqkv, qkvd, W.h1, d, qkvd, d, Tc, wb, g->Wq, g->Wk, (int)qd, g->Wv,
+                            (int)(qd + kd)));
+    } else {
+      SBP_TRY(gemm_wg(W.dqkv, qkvd, W.h1, d, g->Wq, qd, d, Tc, wb));             // dWq += dq^T h1
+      SBP_TRY(gemm_wg(W.dqkv + qd, qkvd, W.h1, d, g->Wk, kd, d, Tc, wb));        // dWk += dK^T h1
+      SBP_TRY(gemm_wg(W.dqkv + qd + kd, qkvd, W.h1, d, g->Wv, kd, d, Tc, wb));   // dWv += dV^T h1
+    }
     SBP_TRY(gemm(W.dqkv, qkvd, W.WqkvT, qkvd, W.dn, d, Tc, d, qkvd, EPI_F32, 0, nullptr, 0, "gemm_layer_dX"));
     SBP_TRY(rmsnorm_bwd(xc, d, w->g1, W.dn, d, W.rinv1, W.da, d, Tc, d, DX + s0 * d, d, str));
     SBP_TRY(gain_grad(W.dn, d, xc, d, W.rinv1, Tc, d, g->g1, wb, W.gpart, str));
@@ -396,8 +445,16 @@ sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t 
     const int64_t Tc = e0 - s0;
     const bf16_t* xc = X + s0 * d;
     SBP_TRY(rmsnorm_fwd(xc, d, w->g1, Tc, d, S.eps, W.h1, d, W.rinv, str));
-    SBP_TRY(gemm(W.h1, d, w->Wk, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
-    SBP_TRY(gemm(W.h1, d, w->Wv, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
+    if (kd % 256 == 0) {  // [K | V] = h1 [Wk; Wv]^T in one launch
+      GemmParams p;
+      p.A = W.h1; p.lda = d; p.B = w->Wk; p.B2 = w->Wv; p.b_split = (int)kd; p.ldb = d;
+      p.C = W.Kall + s0 * kd; p.ldc = kd; p.Cx[0] = W.Vall + s0 * kd; p.c_split[0] = (int)kd;
+      p.c_split_cols = 1; p.M = (int)Tc; p.N = (int)(2 * kd); p.K = (int)d;
+      SBP_TRY(gemm_nt(SBP_BF16, EPI_OUT, p, GEMM_TILE_RING, str, "gemm_layer_fwd"));
+    } else {
+      SBP_TRY(gemm(W.h1, d, w->Wk, W.Kall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
+      SBP_TRY(gemm(W.h1, d, w->Wv, W.Vall + s0 * kd, kd, Tc, kd, d, EPI_OUT, nullptr, 0));
+    }
     SBP_TRY(gemm(W.h1, d, w->Wq, W.q, qd, Tc, qd, d, EPI_OUT, nullptr, 0));
     if (S.qk_norm) {  // in place
       SBP_TRY(headnorm_fwd(W.Kall + s0 * kd, kd, W.Kall + s0 * kd, kd, Tc, S.Hkv, S.dh, w->kn, S.eps, str));
@@ -420,8 +477,15 @@ sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t 
     SBP_TRY(attn_fwd(at, S.dh, 1, str));
     SBP_TRY(gemm(W.o, qd, w->Wo, W.a, d, Tc, d, qd, EPI_OUT_RESID, xc, d));          // a = x + o Wo^T
     SBP_TRY(rmsnorm_fwd(W.a, d, w->g2, Tc, d, S.eps, W.n2, d, W.rinv, str));
-    SBP_TRY(gemm(W.n2, d, w->W1, W.ug, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
-    SBP_TRY(gemm(W.n2, d, w->W3, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
+    if (F % 256 == 0) {  // [u | g] = n2 [W1; W3]^T in one launch
+      GemmParams p;
+      p.A = W.n2; p.lda = d; p.B = w->W1; p.B2 = w->W3; p.b_split = (int)F; p.ldb = d;
+      p.C = W.ug; p.ldc = 2 * F; p.M = (int)Tc; p.N = (int)(2 * F); p.K = (int)d;
+      SBP_TRY(gemm_nt(SBP_BF16, EPI_OUT, p, GEMM_TILE_RING, str, "gemm_layer_fwd"));
+    } else {
+      SBP_TRY(gemm(W.n2, d, w->W1, W.ug, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
+      SBP_TRY(gemm(W.n2, d, w->W3, W.ug + F, 2 * F, Tc, F, d, EPI_OUT, nullptr, 0));
+    }
     SBP_TRY(swiglu_fwd(W.ug, Tc, F, W.m, str));
     SBP_TRY(gemm(W.m, F, w->W2, Y + s0 * d, d, Tc, d, F, EPI_OUT_RESID, W.a, d));   // y = a + m W2^T
   }
