@@ -61,6 +61,91 @@ def measured_traffic(workload, kernel):
     return None
 
 
+# rocprofv3 kernel symbol of each library timer name (traffic records)
+KERNEL_SYMBOLS = {
+    "gemm_logits": "gemm_nt_bf16_ring_kernel<5, false, false>",
+    "gemm_dH": "gemm_nt_bf16_ring_kernel<4, false, false>",
+    "gemm_dW": "gemm_nt_bf16_ring_kernel<1, true, true>",
+    "gemm_layer_dW": "gemm_nt_bf16_ring_kernel<1, true, true>",
+    "gemm_logits_lp": "gemm_nt_bf16_ring_kernel<6, false, false>",
+    "ce_grad": "ce_grad_kernel<unsigned short, false>",
+    "attn_dkdv": "attn_dkdv_kernel<128>",
+    "attn_dq": "attn_dq_kernel<128>",
+    "attn_fwd": "attn_fwd_kernel<128>",
+}
+# sources whose kernels a record covers (their hash invalidates it)
+TRAFFIC_SOURCES = {
+    "gemm": ["memory_efficient_exact_amd/csrc/gemm.hip", "memory_efficient_exact_amd/csrc/ce.hip",
+             "memory_efficient_exact_amd/csrc/common.h", "memory_efficient_exact_amd/csrc/kernels.h"],
+    "attn": ["memory_efficient_exact_amd/csrc/attn.hip", "memory_efficient_exact_amd/csrc/attn.h",
+             "memory_efficient_exact_amd/csrc/common.h"],
+}
+
+
+def _pmc_per_dispatch(csv_path, counter):
+    """Mean of `counter` per dispatch, by kernel symbol, from a rocprofv3
+    --pmc counter_collection CSV (the counter summed over its instances)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        rows = list(csv.DictReader(f))
+    key = {k.lower(): k for k in rows[0]} if rows else {}
+    kn, cn, cv = key.get("kernel_name"), key.get("counter_name"), key.get("counter_value")
+    did = key.get("dispatch_id") or key.get("correlation_id")
+    tot = {}
+    for r in rows:
+        if r[cn] != counter:
+            continue
+        name = r[kn].replace("void ", "").replace("sbp::", "").split("(")[0].strip()
+        d = tot.setdefault(name, {})
+        d[r[did]] = d.get(r[did], 0.0) + float(r[cv])
+    for name, d in tot.items():
+        per[name] = (sum(d.values()) / len(d), len(d))
+    return per
+
+
+def traffic_record(args):
+    """Write profiles/<workload>_traffic.json from four rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE of the workload and of the 1 GiB copy)."""
+    import hashlib
+    import synthetic
+    fetch = _pmc_per_dispatch(args.fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(args.write_csv, "WRITE_SIZE")
+    cfetch = _pmc_per_dispatch(args.copy_fetch_csv, "FETCH_SIZE")
+    cwrite = _pmc_per_dispatch(args.copy_write_csv, "WRITE_SIZE")
+    copy = [k for k in cfetch if "copyBuffer" in k][0]
+    gib_kib = float(1 << 20)
+    fscale = gib_kib / cfetch[copy][0]
+    wscale = gib_kib / cwrite[copy][0]
+    cfg = synthetic.WORKLOADS[args.workload]
+    srcs = TRAFFIC_SOURCES[args.traffic_sources]
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    kernels = {}
+    for lib_name in args.traffic_kernels.split(","):
+        sym = KERNEL_SYMBOLS[lib_name]
+        if sym in fetch and sym in write:
+            kernels[lib_name] = {"read_bytes": fetch[sym][0] * 1024 * fscale,
+                                 "write_bytes": write[sym][0] * 1024 * wscale}
+    rec = {"workload": cfg["name"], "source_sha": h.hexdigest()[:16], "sources": srcs,
+           "fetch_scale": fscale, "write_scale": wscale, "kernels": kernels}
+    out = os.path.join(ROOT, "profiles", f"{cfg['name']}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"wrote {out}")
+    print(f"copy: FETCH_SIZE {cfetch[copy][0]:.0f} KiB, WRITE_SIZE {cwrite[copy][0]:.0f} KiB per 1 GiB copy")
+    print("| kernel | dispatches | FETCH_SIZE KiB/disp | WRITE_SIZE KiB/disp | scaled read GiB | scaled write GiB |")
+    print("|---|---|---|---|---|---|")
+    for name in fetch:
+        if name not in write:
+            continue
+        fk, n = fetch[name]
+        wk, _ = write[name]
+        print(f"| `{name}` | {n} | {fk:.0f} | {wk:.0f} | {fk * fscale / gib_kib:.3f} | {wk * wscale / gib_kib:.3f} |")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -75,6 +160,14 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--traffic-record", action="store_true",
+                   help="(no GPU) write the workload's HBM traffic record from four --pmc CSVs")
+    p.add_argument("--fetch-csv")
+    p.add_argument("--write-csv")
+    p.add_argument("--copy-fetch-csv")
+    p.add_argument("--copy-write-csv")
+    p.add_argument("--traffic-kernels", default="gemm_logits,ce_grad,gemm_dH,gemm_dW")
+    p.add_argument("--traffic-sources", default="gemm")
     return p.parse_args()
 
 
@@ -344,6 +437,9 @@ def cpu_baseline_logprob(inp, cfg, sample):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        traffic_record(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; multi-GPU data parallelism is not built)",
