@@ -93,7 +93,7 @@ typedef enum {
  * H        [T, d]   dtype       hidden states
  * W        [V, d]   dtype       LM-head weight
  * targets  [T]      int32       target ids in [0, V); < 0 = ignored token
- *                               (ids >= V are a caller error, not checked)
+ *                               (ids >= V are a caller error, checked only in debug mode)
  * weights  [T]      fp32 or NULL  per-token weights w_t (GRPO advantage, DPO
  *                               sequence weight); NULL = all ones
  * loss     [1]      fp32 out    the loss above
@@ -358,6 +358,16 @@ sbp_status sbp_model_bwd(const sbp_layer_desc* desc, int32_t n_layers,
                          float* loss, float* token_loss, void* dx0, sbp_layer_grads* grads,
                          float* dg_final, float* dW_lm, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Debug mode.  With the environment variable SBP_DEBUG set (to anything but
+ * "0"), every call checks on the device, before any of its own kernels run,
+ * the inputs it otherwise trusts -- target ids >= V (calls 1, 1b, 4) and
+ * cu_seqlens that do not rise from 0 to T without decreasing (2b, 3b, 3c, 4)
+ * -> SBP_ERR_INVALID_ARG -- and synchronises its stream after its last
+ * launch, so that a failing kernel is reported (SBP_ERR_HIP) by the call that
+ * launched it.  Debug mode blocks the host and is not for graph capture.
+ * ---------------------------------------------------------------------- */
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

@@ -967,8 +967,9 @@ extern "C" sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const v
                                            int32_t accumulate, void* dQ, float* dK, float* dV,
                                            void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  return attn_run(Q, K, V, dO, O, lse, nullptr, 0, B, T, Hq, Hkv, dh, scale, D, dtype, accumulate,
-                  dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
+  const sbp_status st = attn_run(Q, K, V, dO, O, lse, nullptr, 0, B, T, Hq, Hkv, dh, scale, D,
+                                 dtype, accumulate, dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_attn_bwd_chunked") : st;
 }
 
 extern "C" sbp_status sbp_attn_bwd_packed_workspace_size(int64_t T, int32_t Hq, int32_t Hkv,
@@ -993,6 +994,9 @@ extern "C" sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const vo
   if (!cu_seqlens) return set_error(SBP_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
   if (nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
   if (misaligned(cu_seqlens)) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  return attn_run(Q, K, V, dO, O, lse, cu_seqlens, nseq, 1, T, Hq, Hkv, dh, scale, D, dtype,
-                  accumulate, dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
+  sbp_status st = debug_check_cu(cu_seqlens, nseq, T, (hipStream_t)stream);
+  if (st != SBP_OK) return st;
+  st = attn_run(Q, K, V, dO, O, lse, cu_seqlens, nseq, 1, T, Hq, Hkv, dh, scale, D, dtype,
+                accumulate, dQ, dK, dV, ws, ws_bytes, (hipStream_t)stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_attn_bwd_packed") : st;
 }

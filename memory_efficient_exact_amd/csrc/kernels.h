@@ -146,4 +146,12 @@ sbp_status rope_apply(const void* src, bool src_f32, int64_t lds_, void* dst, in
                       int64_t rows, int H, int dh, int64_t row0, const int* seq_lo,
                       const float2* tab, bool inverse, hipStream_t st);
 
+// ------------------------------------------------------------ debug mode ----
+// SBP_DEBUG set (and not "0"): device-side input checks before a call's
+// launches, and a stream synchronisation after them (debug.hip).
+bool debug_on();
+sbp_status debug_check_targets(const int32_t* targets, int64_t T, int64_t V, hipStream_t st);
+sbp_status debug_check_cu(const int32_t* cu, int nseq, int64_t T, hipStream_t st);
+sbp_status debug_sync(hipStream_t st, const char* call);
+
 }  // namespace sbp

@@ -512,7 +512,12 @@ extern "C" sbp_status sbp_layer_fwd(const sbp_layer_desc* desc, const int32_t* c
                                     int32_t nseq, const void* x, const sbp_layer_weights* w,
                                     int32_t D, void* y, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  return layer_fwd_run(desc, cu_seqlens, nseq, x, w, D, y, ws, ws_bytes, (hipStream_t)stream);
+  sbp_status st = desc && cu_seqlens && nseq >= 1 && !misaligned(cu_seqlens)
+                      ? debug_check_cu(cu_seqlens, nseq, desc->T, (hipStream_t)stream)
+                      : SBP_OK;
+  if (st != SBP_OK) return st;
+  st = layer_fwd_run(desc, cu_seqlens, nseq, x, w, D, y, ws, ws_bytes, (hipStream_t)stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_layer_fwd") : st;
 }
 
 extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, int32_t D,
@@ -530,8 +535,9 @@ extern "C" sbp_status sbp_layer_bwd(const sbp_layer_desc* desc, const void* x, c
                                     void* dx, sbp_layer_grads* g, void* ws, size_t ws_bytes,
                                     void* stream) {
   clear_error();
-  return layer_run(desc, nullptr, 0, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
-                   (hipStream_t)stream);
+  const sbp_status st = layer_run(desc, nullptr, 0, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
+                                  (hipStream_t)stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_layer_bwd") : st;
 }
 
 extern "C" sbp_status sbp_layer_bwd_packed_workspace_size(const sbp_layer_desc* desc, int32_t D,
@@ -553,6 +559,9 @@ extern "C" sbp_status sbp_layer_bwd_packed(const sbp_layer_desc* desc, const int
   if (!cu_seqlens) return set_error(SBP_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
   if (nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
   if (misaligned(cu_seqlens)) return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  return layer_run(desc, cu_seqlens, nseq, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
-                   (hipStream_t)stream);
+  sbp_status st = desc ? debug_check_cu(cu_seqlens, nseq, desc->T, (hipStream_t)stream) : SBP_OK;
+  if (st != SBP_OK) return st;
+  st = layer_run(desc, cu_seqlens, nseq, x, dy, w, D, accumulate, dx, g, ws, ws_bytes,
+                 (hipStream_t)stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_layer_bwd_packed") : st;
 }

@@ -159,13 +159,12 @@ extern "C" sbp_status sbp_lmhead_ce_workspace_size(int64_t T, int64_t d, int64_t
   return SBP_OK;
 }
 
-extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* targets,
-                                            const float* weights, int64_t T, int64_t d, int64_t V,
-                                            int32_t D, int32_t dtype, int32_t reduction,
-                                            int32_t accumulate, float* loss, float* token_loss,
-                                            void* dH, float* dW, void* ws, size_t ws_bytes,
-                                            void* stream) {
-  clear_error();
+static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* targets,
+                                 const float* weights, int64_t T, int64_t d, int64_t V,
+                                 int32_t D, int32_t dtype, int32_t reduction,
+                                 int32_t accumulate, float* loss, float* token_loss,
+                                 void* dH, float* dW, void* ws, size_t ws_bytes,
+                                 void* stream) {
   sbp_status st = lm_check_sizes(T, d, V, D, dtype);
   if (st != SBP_OK) return st;
   if (reduction != SBP_MEAN_VALID && reduction != SBP_SUM)
@@ -294,11 +293,10 @@ extern "C" sbp_status sbp_lmhead_logprob_workspace_size(int64_t T, int64_t d, in
 // the per-64-column (max, sum-exp) partials and each row's target logit, and
 // lp_rows merges them; otherwise Z_c is written in fp32 and lp_rows passes
 // over it.  Chunks without a valid token are skipped (their rows are zeros).
-extern "C" sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const int32_t* targets,
-                                             int64_t T, int64_t d, int64_t V, int32_t D,
-                                             int32_t dtype, float* logprob, float* lse, void* ws,
-                                             size_t ws_bytes, void* stream) {
-  clear_error();
+static sbp_status lmhead_logprob_impl(const void* H, const void* W, const int32_t* targets,
+                                      int64_t T, int64_t d, int64_t V, int32_t D,
+                                      int32_t dtype, float* logprob, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
   sbp_status st = lm_check_sizes(T, d, V, D, dtype);
   if (st != SBP_OK) return st;
   if (!H || !W || !targets || !logprob)
@@ -341,4 +339,29 @@ extern "C" sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const
     }
   }
   return r;
+}
+
+extern "C" sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* targets,
+                                            const float* weights, int64_t T, int64_t d, int64_t V,
+                                            int32_t D, int32_t dtype, int32_t reduction,
+                                            int32_t accumulate, float* loss, float* token_loss,
+                                            void* dH, float* dW, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  clear_error();
+  sbp_status st = debug_check_targets(targets, T, V, (hipStream_t)stream);
+  if (st != SBP_OK) return st;
+  st = lmhead_ce_impl(H, W, targets, weights, T, d, V, D, dtype, reduction, accumulate, loss,
+                      token_loss, dH, dW, ws, ws_bytes, stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_lmhead_ce_fwd_bwd") : st;
+}
+
+extern "C" sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const int32_t* targets,
+                                             int64_t T, int64_t d, int64_t V, int32_t D,
+                                             int32_t dtype, float* logprob, float* lse, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  clear_error();
+  sbp_status st = debug_check_targets(targets, T, V, (hipStream_t)stream);
+  if (st != SBP_OK) return st;
+  st = lmhead_logprob_impl(H, W, targets, T, d, V, D, dtype, logprob, lse, ws, ws_bytes, stream);
+  return st == SBP_OK ? debug_sync((hipStream_t)stream, "sbp_lmhead_logprob_fwd") : st;
 }

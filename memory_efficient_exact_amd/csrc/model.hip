@@ -163,5 +163,5 @@ extern "C" sbp_status sbp_model_bwd(const sbp_layer_desc* desc, int32_t n_layers
     up = out;
   }
 #undef SBP_TRY
-  return SBP_OK;
+  return debug_sync(str, "sbp_model_bwd");
 }
