@@ -189,10 +189,13 @@ sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const f
 }
 
 // Same outputs as ce_stats, from the logits GEMM's per-64-column (max,
-// sum-exp) partials instead of a pass over the fp32 logits row.
+// sum-exp) partials instead of a pass over the logits row, and the target
+// logit the GEMM wrote in fp32.
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict__ parts, int64_t ldp,
-                                                       int nparts, const float* __restrict__ Z,
-                                                       int64_t ldz, const int32_t* __restrict__ targets,
+                                                       int nparts, const float* __restrict__ ztgt,
+                                                       const int32_t* __restrict__ targets,
                                                        const float* __restrict__ weights, int64_t s0,
                                                        float* __restrict__ lse_out,
                                                        float* __restrict__ loss_part,
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
   block_lse(m, sx);
   if (tid == 0) {
     const float lse = m + __logf(sx);
-    const float ell = lse - Z[(int64_t)r * ldz + y];
+    const float ell = lse - ztgt[r];
     const float w = weights ? weights[t] : 1.f;
     lse_out[r] = lse;
     loss_part[t] = w * ell;
@@ -225,11 +228,11 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
   }
 }
 
-sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z, int64_t ldz,
+sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* zt,
                     const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
                     float* loss_part, float* token_loss, hipStream_t st) {
   ProfScope prof("ce_merge", st, 0.0, 8.0 * (double)Tc * nparts);
-  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts, Z, ldz,
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts, zt,
                      targets, weights, s, lse, loss_part, token_loss);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
@@ -310,9 +313,12 @@ __device__ __forceinline__ void store8<float>(float* p, const float* v) {
 
 // Tile: 64 rows (tokens of the chunk) x 128 columns (vocab).  With TR the
 // tile is also written transposed (dZt, vocab-major).
-template <typename OutT, bool TR>
+// REL16: Z holds fp16 values relative to the max of their 64-column group
+// (parts[r][v / 64].x), the logits GEMM's EPI_REL16_LSE output.
+template <typename OutT, bool TR, bool REL16>
 __global__ __launch_bounds__(256) void ce_grad_kernel(
-    const float* __restrict__ Z, int64_t ldz, const int32_t* __restrict__ targets,
+    const void* __restrict__ Zv, const float2* __restrict__ parts, int64_t ldp, int64_t ldz,
+    const int32_t* __restrict__ targets,
     const float* __restrict__ weights, const float* __restrict__ inv_norm,
     const float* __restrict__ lse, int64_t s0, int64_t Tc, int64_t V, int64_t Vp,
     OutT* __restrict__ dZ, int64_t ldg, OutT* __restrict__ dZt, int64_t ldgt, int64_t Tcp,
@@ -352,8 +358,28 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(
       float g[8];
       const int y = s_y[lrow];
       const float sc = s_sc[lrow], l = s_lse[lrow];
-      if (r < Tc && sc != 0.f) {
-        const float* zr = Z + r * ldz;
+      if (REL16 && r < Tc && sc != 0.f) {
+        // fp16 values relative to the group max: z = y + max (v is 8-aligned,
+        // so the 8 columns share one 64-column group)
+        const uint16_t* yr = reinterpret_cast<const uint16_t*>(Zv) + r * ldz;
+        const float lm = (v < V ? parts[r * ldp + v / 64].x : 0.f) - l;
+        if (v + 8 <= V) {
+          const uint4 u = *reinterpret_cast<const uint4*>(yr + v);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            g[2 * k] = f16_to_f32((uint16_t)(w4[k] & 0xffff));
+            g[2 * k + 1] = f16_to_f32((uint16_t)(w4[k] >> 16));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) g[j] = sc * (__expf(g[j] + lm) - ((v + j) == y ? 1.f : 0.f));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            g[j] = (v + j < V) ? sc * (__expf(f16_to_f32(yr[v + j]) + lm) - ((v + j) == y ? 1.f : 0.f)) : 0.f;
+        }
+      } else if (!REL16 && r < Tc && sc != 0.f) {
+        const float* zr = reinterpret_cast<const float*>(Zv) + r * ldz;
         if (v + 8 <= V) {
           const float4 a = *reinterpret_cast<const float4*>(zr + v);
           const float4 b = *reinterpret_cast<const float4*>(zr + v + 4);
@@ -398,26 +424,37 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(
   }
 }
 
-sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* targets,
-                   const float* weights, const float* inv_norm, const float* lse, int64_t s,
-                   int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,
-                   int64_t ldgt, int64_t Tcp, const int* active, hipStream_t st) {
+sbp_status ce_grad(int dtype, const void* Z, const float2* parts, int64_t ldp, int64_t ldz,
+                   const int32_t* targets, const float* weights, const float* inv_norm,
+                   const float* lse, int64_t s, int64_t Tc, int64_t V, int64_t Vp, void* dZ,
+                   int64_t ldg, void* dZt, int64_t ldgt, int64_t Tcp, const int* active,
+                   hipStream_t st) {
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
-  ProfScope prof("ce_grad", st, 0.0, (double)Tc * V * (4.0 + (dZt ? 2.0 : 1.0) * esz));
+  if (parts && (dtype != SBP_BF16 || dZt || ldz % 8))
+    return set_error(SBP_ERR_INVALID_ARG, "ce_grad: fp16 relative logits need bf16 output without dZ^T");
+  ProfScope prof("ce_grad", st, 0.0, (double)Tc * V * ((parts ? 2.0 : 4.0) + (dZt ? 2.0 : 1.0) * esz));
   if (!dZt) Tcp = Tc;
   dim3 grid((unsigned)cdiv(Vp, 128), (unsigned)cdiv(Tcp, 64));
-  if (dtype == SBP_BF16 && dZt)
-    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, true>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)dZt, ldgt, Tcp, active);
+  if (parts)
+    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, false, true>), grid, dim3(256), 0, st, Z, parts, ldp, ldz,
+                       targets, weights, inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)nullptr,
+                       ldgt, Tcp, active);
+  else if (dtype == SBP_BF16 && dZt)
+    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, true, false>), grid, dim3(256), 0, st, Z, parts, ldp, ldz,
+                       targets, weights, inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)dZt,
+                       ldgt, Tcp, active);
   else if (dtype == SBP_BF16)
-    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, false>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)nullptr, ldgt, Tcp, active);
+    hipLaunchKernelGGL((ce_grad_kernel<bf16_t, false, false>), grid, dim3(256), 0, st, Z, parts, ldp, ldz,
+                       targets, weights, inv_norm, lse, s, Tc, V, Vp, (bf16_t*)dZ, ldg, (bf16_t*)nullptr,
+                       ldgt, Tcp, active);
   else if (dZt)
-    hipLaunchKernelGGL((ce_grad_kernel<float, true>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)dZt, ldgt, Tcp, active);
+    hipLaunchKernelGGL((ce_grad_kernel<float, true, false>), grid, dim3(256), 0, st, Z, parts, ldp, ldz,
+                       targets, weights, inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)dZt, ldgt,
+                       Tcp, active);
   else
-    hipLaunchKernelGGL((ce_grad_kernel<float, false>), grid, dim3(256), 0, st, Z, ldz, targets, weights,
-                       inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)nullptr, ldgt, Tcp, active);
+    hipLaunchKernelGGL((ce_grad_kernel<float, false, false>), grid, dim3(256), 0, st, Z, parts, ldp, ldz,
+                       targets, weights, inv_norm, lse, s, Tc, V, Vp, (float*)dZ, ldg, (float*)nullptr,
+                       ldgt, Tcp, active);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }

@@ -220,6 +220,13 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
+  const f16x2_t h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // ---------------------------------------------------------------------------
 // Pipelined variant (the default for bf16): the same 256 x 256 tile and
@@ -362,6 +369,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
   __shared__ uint4 L0[(BM + BN) * 8];
   __shared__ uint4 L1[(BM + BN) * 8];
   __shared__ uint32_t PF[4][64];  // sink of the L2 prefetches (never read)
+  __shared__ float MQ[EPI == EPI_REL16_LSE ? 4 * 64 : 1];  // quarter maxima of a 32-row block
   if (p.active && *p.active == 0) return;
   int tm, tn, split;
   tile_coords(p, tm, tn, split);
@@ -644,8 +652,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         W[lr * 128 + fn * 32 + (lane & 31)] = acc[fm][fn][e];
       }
     __builtin_amdgcn_wave_barrier();
-    if constexpr (EPI == EPI_LSE_TGT) {
-      // statistics and target values only: C is not written
+    if constexpr (EPI == EPI_LSE_TGT || EPI == EPI_REL16_LSE) {
+      // statistics (and target values) first; REL16 stores after them
     } else if (full) {
       // rows m0 + wm 128 + fm 32 + 2 bq + l / 32, columns n0 + wn 128 + 4 (l % 32)
       const int64_t rc0 = (int64_t)(m0 + wm * WT + fm * 32 + (lane >> 5));
@@ -674,7 +682,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + (lane & 31) * 4]);
         float v[4] = {p.alpha * v4.x, p.alpha * v4.y, p.alpha * v4.z, p.alpha * v4.w};
         const int64_t off = (rc0 + 2 * bq) * p.ldc + c0;
-        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
+        if constexpr (EPI == EPI_F32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_PARTIAL) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
@@ -728,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         if (row >= p.M || col >= p.N) continue;
         const int64_t off = (int64_t)row * p.ldc + col;
         if (vec_ok && col + 4 <= p.N) {
-          if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
+          if constexpr (EPI == EPI_F32) {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
           } else if constexpr (EPI == EPI_PARTIAL) {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (int64_t)split * p.split_stride + off) =
@@ -750,7 +758,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (col + j >= p.N) break;
-            if constexpr (EPI == EPI_F32 || EPI == EPI_F32_LSE) {
+            if constexpr (EPI == EPI_F32) {
               reinterpret_cast<float*>(p.C)[off + j] = v[j];
             } else if constexpr (EPI == EPI_PARTIAL) {
               reinterpret_cast<float*>(p.C)[(int64_t)split * p.split_stride + off + j] = v[j];
@@ -767,7 +775,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         }
       }
     }
-    if constexpr (EPI == EPI_F32_LSE || EPI == EPI_LSE_TGT) {
+    if constexpr (EPI == EPI_REL16_LSE || EPI == EPI_LSE_TGT) {
       // (max, sum-exp) of each row's 64-column quarters of the wave's block,
       // one lane per (row l % 32, quarter l / 32), read from the staged block
       // in a lane-rotated order (conflict-free); no cross-lane traffic.
@@ -807,11 +815,36 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         if (m != -INFINITY) sx += __expf(x0 - m) + __expf(x1 - m) + __expf(x2 - m) + __expf(x3 - m);
       }
       if (row < p.M) p.row_stats[(int64_t)row * p.ld_stats + 4 * tn + 2 * wn + hq] = make_float2(m, sx);
-      if constexpr (EPI == EPI_LSE_TGT) {
+      if constexpr (EPI == EPI_REL16_LSE) MQ[wave * 64 + lane] = m;
+      if constexpr (EPI == EPI_LSE_TGT || EPI == EPI_REL16_LSE) {
         // the one lane whose quarter holds the row's target column
-        if (row < p.M) {
+        if (row < p.M && p.target_out) {
           const int y = p.row_target[row];
           if (y >= cbase && y < cbase + 64 && y < p.N) p.target_out[row] = Wr[y - cbase];
+        }
+      }
+    }
+    if constexpr (EPI == EPI_REL16_LSE) {
+      // every value minus the max of its 64-column quarter, as fp16, in
+      // row-contiguous 8-byte stores (quarter maxima from the pass above)
+      __builtin_amdgcn_wave_barrier();
+      const int q = (lane & 31) >> 4;  // the lane's quarter of the wave's 128 columns
+      const int c0 = n0 + wn * WT + (lane & 31) * 4;
+      uint16_t* C16 = reinterpret_cast<uint16_t*>(p.C);
+#pragma unroll
+      for (int bq = 0; bq < 16; ++bq) {
+        const int lr = bq * 2 + (lane >> 5);
+        const int row = m0 + wm * WT + fm * 32 + lr;
+        const float mq = MQ[wave * 64 + q * 32 + lr];
+        const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + (lane & 31) * 4]);
+        const float v[4] = {v4.x - mq, v4.y - mq, v4.z - mq, v4.w - mq};
+        if (full || (row < p.M && vec_ok && c0 + 4 <= p.N)) {
+          *reinterpret_cast<uint2*>(C16 + (int64_t)row * p.ldc + c0) =
+              make_uint2(pk_f16(v[0], v[1]), pk_f16(v[2], v[3]));
+        } else if (row < p.M) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (c0 + j < p.N) C16[(int64_t)row * p.ldc + c0 + j] = __builtin_bit_cast(uint16_t, (_Float16)v[j]);
         }
       }
     }
@@ -823,7 +856,7 @@ template <bool AKM, bool BKM>
 static void launch_bf16_ring_layout(int epi, const GemmParams& p, int grid, hipStream_t st) {
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
-    case EPI_F32_LSE: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_F32_LSE, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
+    case EPI_REL16_LSE: hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_REL16_LSE, AKM, BKM>), dim3(grid), dim3(256), 0, st, p); break;
     case EPI_LSE_TGT:
       if constexpr (!AKM) hipLaunchKernelGGL((gemm_nt_bf16_ring_kernel<EPI_LSE_TGT, false, false>), dim3(grid), dim3(256), 0, st, p);
       break;
@@ -868,16 +901,18 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
   const double flops = 2.0 * p.M * p.N * (double)p.K;
   const size_t esz = dtype == SBP_BF16 ? 2 : 4;
   const double bytes = ((double)p.M * p.K + (double)p.N * p.K) * esz +
-                       (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : epi == EPI_LSE_TGT ? 0.0 : 4.0 * p.k_split);
-  // (the row statistics of EPI_F32_LSE / EPI_LSE_TGT add 8 bytes per 64 output columns)
+                       (double)p.M * p.N * (epi == EPI_F32_ACC ? 8.0 : epi == EPI_OUT || epi == EPI_OUT_RESID ? (double)esz : epi == EPI_LSE_TGT ? 0.0 : epi == EPI_REL16_LSE ? 2.0 : 4.0 * p.k_split);
+  // (the row statistics of EPI_REL16_LSE / EPI_LSE_TGT add 8 bytes per 64 output columns)
   ProfScope prof(name, st, flops, bytes);
   const bool ring_ok = dtype == SBP_BF16 && (p.K % 8 == 0 || p.a_kmajor) &&
                        p.k_per_split % 128 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
                        (!p.a_kmajor || p.lda >= round_up(p.M, 8)) &&
                        (!p.b_kmajor || p.ldb >= round_up(p.N, 8));
-  if ((epi == EPI_F32_LSE || epi == EPI_LSE_TGT) &&
+  if ((epi == EPI_REL16_LSE || epi == EPI_LSE_TGT) &&
       !(tile == GEMM_TILE_RING && ring_ok && p.k_split == 1 && p.row_stats))
     return set_error(SBP_ERR_UNSUPPORTED, "row-statistics epilogue needs the bf16 ring GEMM without split-K");
+  if (epi == EPI_REL16_LSE && p.target_out && !p.row_target)
+    return set_error(SBP_ERR_INVALID_ARG, "target-value output needs the row target array");
   if (epi == EPI_LSE_TGT && (p.a_kmajor || !p.row_target || !p.target_out))
     return set_error(SBP_ERR_UNSUPPORTED, "target-value epilogue needs row-major operands and its row arrays");
   if ((p.a_kmajor || p.b_kmajor) && !(tile == GEMM_TILE_RING && ring_ok && p.a_kmajor == p.b_kmajor))

@@ -6,12 +6,16 @@
 namespace sbp {
 
 // ---------------------------------------------------------------- GEMM ----
-// EPI_F32_LSE: as EPI_F32, plus the (max, sum-exp) of every 64-column quarter
-// of a tile row (columns < N) into row_stats (ring kernel only, k_split 1).
-// EPI_LSE_TGT: the row statistics of EPI_F32_LSE and, for each row m with
+// EPI_REL16_LSE: the (max, sum-exp) of every 64-column quarter of a tile row
+// (columns < N) into row_stats, and into C (fp16, pitch ldc) each value minus
+// the max of its quarter (so <= 0: the values near 0 that dominate a softmax
+// keep ~11 bits; the quarter's max, kept in fp32 in row_stats, restores the
+// value), and, when target_out is set, the fp32 value at each row's target
+// column as for EPI_LSE_TGT (ring kernel only, k_split 1).
+// EPI_LSE_TGT: the row statistics of EPI_REL16_LSE and, for each row m with
 // 0 <= row_target[m] < N, its value at that column into target_out[m]; C is
 // not written (ring kernel only, k_split 1).
-enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_F32_LSE = 5,
+enum { EPI_F32 = 0, EPI_F32_ACC = 1, EPI_OUT = 2, EPI_OUT_RESID = 3, EPI_PARTIAL = 4, EPI_REL16_LSE = 5,
        EPI_LSE_TGT = 6 };
 enum { GEMM_TILE_128 = 0, GEMM_TILE_RING = 3 };
 
@@ -37,7 +41,7 @@ struct GemmParams {
   // between k-rows (rows are read in 8-element chunks up to that bound);
   // the two flags must be equal
   int a_kmajor = 0, b_kmajor = 0;
-  float2* row_stats = nullptr;     // EPI_F32_LSE, EPI_LSE_TGT: [M, ld_stats], entry 4 tn + quarter
+  float2* row_stats = nullptr;     // EPI_REL16_LSE, EPI_LSE_TGT: [M, ld_stats], entry 4 tn + quarter
   int64_t ld_stats = 0;
   const int32_t* row_target = nullptr;  // EPI_LSE_TGT: [M] column of each row (< 0: none)
   float* target_out = nullptr;          // EPI_LSE_TGT: [M]
@@ -72,8 +76,9 @@ sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int 
                    int accumulate, const LmPrep& pr, hipStream_t st);
 // Per-row log-sum-exp and per-token loss for rows [s, s+Tc) of one chunk.
 // Row statistics from the logits GEMM's per-64-column partials (nparts per
-// row, pitch ldp): lse, l_t = lse - z_t[y_t] (z read from Z), c_t l_t.
-sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* Z, int64_t ldz,
+// row, pitch ldp): lse, l_t = lse - z_t[y_t], c_t l_t, with z_t[y_t] the fp32
+// target logit the GEMM wrote into zt [Tc].
+sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* zt,
                     const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
                     float* loss_part, float* token_loss, hipStream_t st);
 sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
@@ -81,10 +86,14 @@ sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const f
                     float* token_loss, hipStream_t st);
 // dZ (dtype) [Tc, ldg] and, if dZt is not NULL, dZ^T (dtype) [Vp, ldgt] for
 // one chunk; zero pads (columns V .. Vp of dZ, columns Tc .. Tcp of dZ^T).
-sbp_status ce_grad(int dtype, const float* Z, int64_t ldz, const int32_t* targets,
-                   const float* weights, const float* inv_norm, const float* lse, int64_t s,
-                   int64_t Tc, int64_t V, int64_t Vp, void* dZ, int64_t ldg, void* dZt,
-                   int64_t ldgt, int64_t Tcp, const int* active, hipStream_t st);
+// Z: fp32 logits [Tc, ldz], or, when parts is not NULL, the fp16 relative
+// logits of EPI_REL16_LSE with their group maxima in parts [Tc, ldp] (bf16
+// output without dZ^T only).
+sbp_status ce_grad(int dtype, const void* Z, const float2* parts, int64_t ldp, int64_t ldz,
+                   const int32_t* targets, const float* weights, const float* inv_norm,
+                   const float* lse, int64_t s, int64_t Tc, int64_t V, int64_t Vp, void* dZ,
+                   int64_t ldg, void* dZt, int64_t ldgt, int64_t Tcp, const int* active,
+                   hipStream_t st);
 // Per-token target log-probability of rows [s, s+Tc) of one chunk:
 // logprob[s+r] = z_r[y] - lse_r and (if lse_out is not NULL) lse_out[s+r] =
 // lse_r, both 0 where y = targets[s+r] < 0.  From the logits GEMM's

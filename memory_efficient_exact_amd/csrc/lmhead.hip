@@ -3,10 +3,12 @@
 // Per chunk c = [s, e) (skill page "Implementation": the sequence
 // decomposition, the logits-gradient routine and the linear-layer chunk
 // gradient):
-//   Z_c   = H_c W^T                fp32 [T_c, V]          (gemm, EPI_F32_LSE: with
-//                                  per-64-column row (max, sum-exp) partials)
+//   Z_c   = H_c W^T                [T_c, V]                (gemm, EPI_REL16_LSE: per-64-
+//                                  column row (max, sum-exp) partials in fp32 and every
+//                                  logit minus its group's max in fp16; fp32 logits
+//                                  where that epilogue does not apply: fp32, d % 128)
 //   lse, l_t, c_t l_t              per row                 (ce_merge of the partials;
-//                                  ce_stats over Z where the GEMM cannot: fp32, d % 128)
+//                                  ce_stats over the fp32 logits otherwise)
 //   dZ_c                           dtype, zero-padded      (ce_grad)
 //   dH_c  = dZ_c W                 split-K partials, sum   (gemm EPI_PARTIAL, splitk_reduce)
 //   dW   += dZ_g^T H_g             fp32 read-modify-write  (gemm EPI_F32_ACC)
@@ -26,7 +28,8 @@ namespace sbp {
 namespace {
 
 struct LmWs {
-  float* Z;
+  void* Z;    // fp16 relative logits [T_c, Vp] (fused statistics) or fp32 logits
+  float* ztgt;  // fused statistics: each row's target logit, fp32 [T_c]
   void* dZ;   // bf16: the group buffer [G T_c, Vp]; fp32: [T_c, Vp]
   void* dZt;  // fp32 only
   void* Wt;
@@ -81,7 +84,7 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   WsPlan P;
   P.base = base;
   LmWs x;
-  x.Z = (float*)P.take(sizeof(float) * s.Tcm * s.Vp);
+  x.Z = P.take((s.fused_stats ? 2 : sizeof(float)) * s.Tcm * s.Vp);
   x.Wt = P.take(s.esz * s.d * s.Vp);
   if (s.kmajor) {
     x.dZ = P.take(s.esz * s.G * s.Tcm * s.Vp);
@@ -95,6 +98,7 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   x.lse = (float*)P.take(sizeof(float) * s.Tcm);
   x.loss_part = (float*)P.take(sizeof(float) * s.T);
   x.parts = s.fused_stats ? (float2*)P.take(sizeof(float2) * s.Tcm * s.nparts) : nullptr;
+  x.ztgt = s.fused_stats ? (float*)P.take(sizeof(float) * s.Tcm) : nullptr;
   x.prep.n_valid = (int*)P.take(sizeof(int));
   x.prep.inv_norm = (float*)P.take(sizeof(float));
   x.prep.none_active = (int*)P.take(sizeof(int));
@@ -220,19 +224,24 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
     if (s.fused_stats) {
       g1.row_stats = w.parts;
       g1.ld_stats = s.nparts;
-      SBP_TRY(gemm_nt(dtype, EPI_F32_LSE, g1, GEMM_TILE_RING, str, "gemm_logits"));
-      SBP_TRY(ce_merge(w.parts, s.nparts, s.nparts, w.Z, s.Vp, targets, weights, s0, Tc, w.lse,
+      g1.row_target = targets + s0;
+      g1.target_out = w.ztgt;
+      SBP_TRY(gemm_nt(dtype, EPI_REL16_LSE, g1, GEMM_TILE_RING, str, "gemm_logits"));
+      SBP_TRY(ce_merge(w.parts, s.nparts, s.nparts, w.ztgt, targets, weights, s0, Tc, w.lse,
                        w.loss_part, token_loss, str));
     } else {
       SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
-      SBP_TRY(ce_stats(w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part, token_loss, str));
+      SBP_TRY(ce_stats((const float*)w.Z, s.Vp, targets, weights, s0, Tc, V, w.lse, w.loss_part,
+                       token_loss, str));
     }
     if (s.kmajor) {
-      SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
-                      dZc, s.Vp, nullptr, 0, 0, slot_act, str));
+      SBP_TRY(ce_grad(dtype, w.Z, s.fused_stats ? w.parts : nullptr, s.nparts, s.Vp, targets,
+                      weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp, dZc, s.Vp, nullptr, 0, 0,
+                      slot_act, str));
     } else {
-      SBP_TRY(ce_grad(dtype, w.Z, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp,
-                      dZc, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp, slot_act, str));
+      SBP_TRY(ce_grad(dtype, w.Z, nullptr, 0, s.Vp, targets, weights, w.prep.inv_norm, w.lse, s0,
+                      Tc, V, s.Vp, dZc, s.Vp, (char*)w.dZt + j * s.Tcp * s.esz, s.Kg, s.Tcp,
+                      slot_act, str));
       SBP_TRY(transpose_pad(dtype, Hb + s0 * d * s.esz, d, Tc, d, (char*)w.Ht + j * s.Tcp * s.esz, s.Kg,
                             s.Tcp, slot_act, str));
     }
