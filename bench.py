@@ -68,7 +68,7 @@ KERNEL_SYMBOLS = {
     "gemm_dW": "gemm_nt_bf16_ring_kernel<1, true, true>",
     "gemm_layer_dW": "gemm_nt_bf16_ring_kernel<1, true, true>",
     "gemm_logits_lp": "gemm_nt_bf16_ring_kernel<6, false, false>",
-    "ce_grad": "ce_grad_kernel<unsigned short, false>",
+    "ce_grad": "ce_grad_kernel<unsigned short, false, true>",
     "attn_dkdv": "attn_dkdv_kernel<128>",
     "attn_dq": "attn_dq_kernel<128>",
     "attn_fwd": "attn_fwd_kernel<128>",
