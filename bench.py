@@ -146,6 +146,68 @@ def traffic_record(args):
         print(f"| `{name}` | {n} | {fk:.0f} | {wk:.0f} | {fk * fscale / gib_kib:.3f} | {wk * wscale / gib_kib:.3f} |")
 
 
+def peak_bytes(idx, T, D, D_lm=None):
+    """Peak device bytes of one call of workload `idx` at sequence length T
+    and chunk count D: its inputs, outputs, weights, gradients and the
+    workspace the library asks for (the library allocates nothing else)."""
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    c = synthetic.WORKLOADS[idx]
+    bf = torch.bfloat16
+    if c["kind"] == "lmhead":
+        d, V = c["d"], c["V"]
+        ws = sbp.lmhead_ce_workspace_size(T, d, V, D, bf)
+        return 2 * (2 * T * d) + 2 * V * d + 4 * V * d + 4 * T + ws + (4 * T if c.get("weighted") else 0)
+    if c["kind"] == "layer":
+        d, F, kd, qd = c["d"], c["F"], c["Hkv"] * c["dh"], c["Hq"] * c["dh"]
+        P = qd * d + 2 * kd * d + d * qd + 3 * F * d
+        ws = sbp.layer_bwd_workspace_size(T, d, c["Hq"], c["Hkv"], c["dh"], F, D, bf)
+        return 3 * (2 * T * d) + 2 * P + 4 * P + 2 * 4 * d + 2 * 2 * d + ws
+    if c["kind"] == "model":
+        d, F, V, L = c["d"], c["F"], c["V"], c["n_layers"]
+        kd, qd = c["Hkv"] * c["dh"], c["Hq"] * c["dh"]
+        P = qd * d + 2 * kd * d + d * qd + 3 * F * d + 2 * d
+        ws = sbp.model_bwd_workspace_size(T, d, c["Hq"], c["Hkv"], c["dh"], F, L, V, D_lm or D, D,
+                                          False, bf, 1e-6, c["rope_theta"])
+        return (L + 2) * (2 * T * d) + L * 6 * P + 6 * V * d + 6 * d + 4 * T + ws
+    raise ValueError(c["kind"])
+
+
+def max_t_report(budget=288e9, margin=2e9):
+    """Largest T whose call fits `budget` bytes of HBM (less a margin for the
+    runtime), chunked at the workload's chunk length and unchunked (D = 1)."""
+    import synthetic
+    out = []
+    for idx, tc in ((1, 2048), (3, 4096), (8, 4096)):
+        c = synthetic.WORKLOADS[idx]
+        tc_lm = 2048
+
+        def fits(T, chunked):
+            if chunked:
+                D = max(1, T // tc)
+                Dl = max(1, T // tc_lm) if c["kind"] == "model" else None
+            else:
+                D, Dl = 1, (1 if c["kind"] == "model" else None)
+            return peak_bytes(idx, T, D, Dl) <= budget - margin
+
+        row = {"workload": c["name"]}
+        for chunked in (True, False):
+            lo, hi = tc, tc
+            while fits(hi * 2, chunked):
+                hi *= 2
+            hi *= 2
+            while hi - lo > tc:  # bisection on multiples of the chunk length
+                mid = (lo + hi) // 2 // tc * tc
+                if mid <= lo:
+                    break
+                lo, hi = (mid, hi) if fits(mid, chunked) else (lo, mid)
+            row["max_T_chunked" if chunked else "max_T_D1"] = lo
+        row["ratio"] = round(row["max_T_chunked"] / row["max_T_D1"], 2)
+        out.append(row)
+    print(json.dumps({"budget_bytes": budget, "margin_bytes": margin, "rows": out}), flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -160,6 +222,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--max-t", action="store_true",
+                   help="(no GPU) largest T whose call fits 288 GB, chunked and unchunked")
     p.add_argument("--traffic-record", action="store_true",
                    help="(no GPU) write the workload's HBM traffic record from four --pmc CSVs")
     p.add_argument("--fetch-csv")
@@ -439,6 +503,9 @@ def main():
     args = parse()
     if args.traffic_record:
         traffic_record(args)
+        return
+    if args.max_t:
+        max_t_report()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
