@@ -326,3 +326,15 @@ def test_layer_qk_norm_arguments():
     # keys before their norm [T, kd], one chunk's q [T_c, qd] (bf16), gain partials
     extra = 2 * 4096 * 256 + 2 * 1024 * 1024 + 4 * 1024 * 128
     assert 0 <= sizes[1] - sizes[0] - extra < 1024
+
+
+def test_peak_memory_model_is_chunk_sized():
+    """The library allocates nothing, so a call's peak is inputs + outputs +
+    weights + gradients + reported workspace (bench.peak_bytes); chunking at
+    the workloads' chunk lengths must keep it below the unchunked call's and
+    let a longer sequence fit 288 GB."""
+    import bench
+    for idx, T, D in ((1, 32768, 16), (3, 65536, 16)):
+        assert bench.peak_bytes(idx, T, D) < bench.peak_bytes(idx, T, 1)
+        assert bench.peak_bytes(idx, 2 * T, 2 * D) > bench.peak_bytes(idx, T, D)
+    assert bench.peak_bytes(8, 16384, 4, 8) < bench.peak_bytes(8, 16384, 1, 1)
