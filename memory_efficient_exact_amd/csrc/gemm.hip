@@ -206,11 +206,13 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
   const int lin = xcd * base + (xcd < rem ? xcd : rem) + idx;
   split = lin / ntile;
   const int t = lin - split * ntile;
-  // Grouped order: 8 tile rows at a time, m fastest inside the group, so an
-  // XCD's ~32 concurrent blocks cover about 8 x 4 tiles and share their A
+  // Grouped order: 4 tile rows at a time, m fastest inside the group, so an
+  // XCD's ~32 concurrent blocks cover about 4 x 8 tiles and share their A
   // and B panels through its L2 (operand panels of long-K products are
-  // megabytes, so reuse has to be concurrent rather than over time).
-  constexpr int GM = 8;
+  // megabytes, so reuse has to be concurrent rather than over time).  Same-box
+  // A/B over groups of 1, 2, 4, 8 and 16 rows: 4 is fastest on the LM-head,
+  // layer and model workloads (1-3% over 8; 1 and 16 are the slowest).
+  constexpr int GM = 4;
   const int g = t / (GM * p.tiles_n);
   const int rows = min(GM, p.tiles_m - g * GM);
   const int tl = t - g * GM * p.tiles_n;
