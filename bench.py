@@ -222,6 +222,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--library-gemm", action="store_true",
+                   help="time torch's library bf16 GEMMs on the LM head's three products")
     p.add_argument("--max-t", action="store_true",
                    help="(no GPU) largest T whose call fits 288 GB, chunked and unchunked")
     p.add_argument("--traffic-record", action="store_true",
@@ -248,6 +250,61 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
                       "launches": 3}), flush=True)
+
+
+def library_gemm(dev, reps=10):
+    """torch's library bf16 GEMMs (hipBLASLt on ROCm) on the LM head's three
+    products at T_c = 2048, a weight-gradient group of K = 4096 tokens, d =
+    4096, V = 128256, timed with events on torch's stream: a same-box context
+    for the path's own GEMM kernels, not part of the path.  Operands are
+    contiguous; the fp32 weight-gradient case reads the fp32 C and writes a
+    fresh fp32 result (the same HBM traffic as the path's read-modify-write)."""
+    import torch
+    Tc, Kg, d, V = 2048, 4096, 4096, 128256
+    g = torch.Generator(device=dev).manual_seed(0)
+    bf = torch.bfloat16
+
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * 0.1).to(bf)
+
+    H = rnd(Tc, d)
+    Wt = rnd(d, V)
+    W = rnd(V, d)
+    dZ = rnd(Tc, V)
+    dZt = rnd(V, Kg)
+    Hg = rnd(Kg, d)
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev)
+    cases = [
+        ("logits Z = H W^T, bf16 out", lambda: torch.mm(H, Wt), 2.0 * Tc * V * d),
+        ("input grad dH = dZ W, bf16 out", lambda: torch.mm(dZ, W), 2.0 * Tc * V * d),
+        ("input grad dH = dZ W, fp32 out", lambda: torch.mm(dZ, W, out_dtype=torch.float32),
+         2.0 * Tc * V * d),
+        ("weight grad dW += dZ^T H, fp32 accumulate",
+         lambda: torch.addmm(dW, dZt, Hg, out_dtype=torch.float32),
+         2.0 * V * d * Kg),
+        ("weight grad dZ^T H, bf16 out", lambda: torch.mm(dZt, Hg), 2.0 * V * d * Kg),
+    ]
+    rows = []
+    for name, fn, flops in cases:
+        try:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            rows.append({"product": name, "ms": round(ms, 4),
+                         "tflops": round(flops / ms / 1e9, 1)})
+        except RuntimeError as e:
+            rows.append({"product": name, "error": str(e).splitlines()[0][:200]})
+        print(json.dumps(rows[-1]), flush=True)
+    print(json.dumps({"library_gemm": rows, "T_c": Tc, "K_g": Kg, "d": d, "V": V,
+                      "torch": torch.__version__}), flush=True)
 
 
 def lmhead_setup(cfg, dev):
@@ -528,6 +585,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(dev)
+        return
+    if args.library_gemm:
+        library_gemm(dev)
         return
 
     idx = args.workload
