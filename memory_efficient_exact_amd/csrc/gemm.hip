@@ -794,10 +794,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
           const float4 q = *reinterpret_cast<const float4*>(Wr + ((j + lane) & 15) * 4);
           m = fmaxf(m, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
         }
+        // exp(x - m) = 2^(x log2 e - m log2 e): one fma and one exp2 each
+        constexpr float L2E = 1.4426950408889634f;
+        const float ml = m * L2E;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float4 q = *reinterpret_cast<const float4*>(Wr + ((j + lane) & 15) * 4);
-          sx += (__expf(q.x - m) + __expf(q.y - m)) + (__expf(q.z - m) + __expf(q.w - m));
+          sx += (__builtin_amdgcn_exp2f(__builtin_fmaf(q.x, L2E, -ml)) +
+                 __builtin_amdgcn_exp2f(__builtin_fmaf(q.y, L2E, -ml))) +
+                (__builtin_amdgcn_exp2f(__builtin_fmaf(q.z, L2E, -ml)) +
+                 __builtin_amdgcn_exp2f(__builtin_fmaf(q.w, L2E, -ml)));
         }
       } else
       // one pass, online: the running sum is rescaled when a float4 raises
