@@ -1,12 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the StreamBP hot path on one MI355X.
 
-Default workload: the chunked LM head + cross-entropy forward/backward at
-T=32768, d=4096, V=128256, D=16 in bf16 (fp32 accumulation), synthetic
-N(0,1) hidden states and N(0, 0.02^2) weights with uniform targets.  A
-"step" is one full call of the path on that batch (logits GEMM, softmax-CE
-row kernels, dH and dW GEMMs for every chunk, loss reduction), inputs
-resident in HBM.
+Default workload: the weighted-token chunked LM head + cross-entropy
+forward/backward, the largest single-GPU configuration: T=131072 tokens
+packed as 8 sequences of 16384, d=3584, V=152064, D=32 in bf16 (fp32
+accumulation); synthetic N(0,1) hidden states, N(0, 0.02^2) weights and
+uniform targets, the first 25% of every sequence loss-masked, one N(0,1)
+weight per sequence, loss normalised by the unmasked count.  A "step" is
+one full call of the path on that batch (logits GEMM, softmax-CE row
+kernels, dH and dW GEMMs for every chunk that holds a target, loss
+reduction), inputs resident in HBM.
 
 Prints ONE JSON line: tokens/s, ms per step, peak HBM bytes of the call,
 the fraction of bf16 MFMA peak over the whole step, the roofline of the
@@ -16,7 +19,8 @@ library's kernel timer), and the CPU oracle timed on a bounded sample.
     python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
 
 Workloads (--workload): 0..4 the LM-head, attention and layer configurations
-(1 is the default), 5 the forward-only per-token log-probability on the
+(4 is the default; 1 the unweighted LM head at T=32768, d=4096, V=128256,
+D=16), 5 the forward-only per-token log-probability on the
 weighted LM-head shapes, 6 and 7 the attention and layer workloads over 8
 packed sequences of random lengths, 8 the whole-model backward (4 layers
 with rotary embedding under the LM head; the layer inputs come from an
@@ -213,7 +217,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--workload", type=int, default=1)
+    p.add_argument("--workload", type=int, default=4)
     p.add_argument("--D", type=int, default=None, help="override the chunk count")
     p.add_argument("--D-lm", type=int, default=None,
                    help="override the LM head's chunk count (whole-model workload)")

@@ -92,8 +92,12 @@ typedef enum {
  *
  * H        [T, d]   dtype       hidden states
  * W        [V, d]   dtype       LM-head weight
- * targets  [T]      int32       target ids in [0, V); < 0 = ignored token
- *                               (ids >= V are a caller error, checked only in debug mode)
+ * targets  [T]      int32       target ids in [0, V); < 0 = ignored token.
+ *                               An id >= V is a caller error: without debug
+ *                               mode nothing is read out of bounds and the
+ *                               loss, dH and dW come out NaN (token_loss of
+ *                               that token NaN); debug mode rejects it before
+ *                               any launch (SBP_ERR_INVALID_ARG)
  * weights  [T]      fp32 or NULL  per-token weights w_t (GRPO advantage, DPO
  *                               sequence weight); NULL = all ones
  * loss     [1]      fp32 out    the loss above
@@ -129,8 +133,10 @@ sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* ta
  *   Z = H W^T,  lse_t = logsumexp(Z_t),  logprob_t = Z_{t,y_t} - lse_t
  *
  * H, W, targets  as in (1)
- * logprob  [T]      fp32 out    logprob_t; 0 for ignored tokens (y_t < 0)
- * lse      [T]      fp32 out or NULL  lse_t; 0 for ignored tokens
+ * logprob  [T]      fp32 out    logprob_t; 0 for ignored tokens (y_t < 0);
+ *                               NaN for an id >= V (caller error; rejected
+ *                               before any launch in debug mode)
+ * lse      [T]      fp32 out or NULL  lse_t; 0 for ignored tokens, NaN for ids >= V
  * Chunks with no valid token are skipped on the device.
  * ---------------------------------------------------------------------- */
 sbp_status sbp_lmhead_logprob_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,

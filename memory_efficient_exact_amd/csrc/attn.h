@@ -60,4 +60,14 @@ sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st);
 sbp_status attn_seq_bounds(const int32_t* cu, int nseq, int64_t T, int* seq_lo, int* seq_hi,
                            hipStream_t st);
 
+// The chunked attention backward of sbp_attn_bwd_chunked on a given
+// workspace (every argument checked first), and the size that workspace
+// needs (SBP_OK and *bytes set, or an argument error).
+sbp_status attn_bwd_ws_size(int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh, int32_t D,
+                            int32_t dtype, size_t* bytes);
+sbp_status attn_bwd_run(const void* Q, const void* K, const void* V, const void* dO, const void* O,
+                        const float* lse, int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
+                        float scale, int32_t D, int32_t dtype, int32_t accumulate, void* dQ,
+                        float* dK, float* dV, void* ws, size_t ws_bytes, hipStream_t str);
+
 }  // namespace sbp

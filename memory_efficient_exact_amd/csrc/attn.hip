@@ -672,10 +672,19 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
 // dQ.  Block: 4 waves, 128 queries (32 per wave), one q head; key tiles of
 // 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
+// Sum of the 8 bf16 values of an operand fragment (exact in fp32 pairs).
+__device__ __forceinline__ float frag_sum(const uint4& u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += __uint_as_float(w[k] << 16) + __uint_as_float(w[k] & 0xffff0000u);
+  return s;
+}
+
 template <int DH, bool MASK>
 __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol,
                                         int klo, int lane, float c2, float lse2, float dl, const uint4 (&qf)[DH / 16],
-                                        const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32]) {
+                                        const uint4 (&of)[DH / 16], f32x16_t (&dq)[DH / 32], float& rs) {
   constexpr int NB = DH / 32, KS = DH / 16;
   f32x16_t st[2], dpt[2];
 #pragma unroll
@@ -696,12 +705,14 @@ __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, co
       const float p = (!MASK || (key <= qcol && key >= klo)) ? __builtin_amdgcn_exp2f(st[kb][e] * c2 - lse2) : 0.f;
       dpt[kb][e] = p * (dpt[kb][e] - dl);
     }
-  // dQ[q, dh] += dS[q, key] K[key, dh]
+  // dQ[q, dh] += dS[q, key] K[key, dh]; rs: this lane's share of the row sum
+  // of dS as rounded to bf16 for the product
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint4 da = pack_frag(dpt[kb], i);
+      rs += frag_sum(da);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         dq[nb] = mma(da, lo.tr_frag(kt, kb * 32 + 16 * i, nb), dq[nb]);
@@ -741,6 +752,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   f32x16_t dq[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) dq[i] = f32x16_t{};
+  float rs = 0.f;
 
   const SeqRange sr = seq_range(a, q0, qw, qcol);
   const int kend = min(q0 + 128, a.e);
@@ -755,19 +767,39 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
     dma_barrier();
     issue(K1, V1, min(t + 1, ntiles - 1));
     switch (sr.kind(t * 64)) {
-      case 1: dq_tile<DH, false>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
-      case 2: dq_tile<DH, true>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      case 1: dq_tile<DH, false>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq, rs); break;
+      case 2: dq_tile<DH, true>(lo, K0, V0, t * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq, rs); break;
       default: break;
     }
     dma_barrier();
     issue(K0, V0, min(t + 2, ntiles - 1));
     if (t + 1 < ntiles) switch (sr.kind((t + 1) * 64)) {
-      case 1: dq_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
-      case 2: dq_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq); break;
+      case 1: dq_tile<DH, false>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq, rs); break;
+      case 2: dq_tile<DH, true>(lo, K1, V1, (t + 1) * 64, qcol, sr.klo, lane, c2, lse2, dl, qf, of, dq, rs); break;
       default: break;
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS at exit
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS
+  __syncthreads();                // every wave's share of the last tile landed
+  // Every row of dS sums to zero (sum_j P_ij dP_ij = rowsum(dO O) = Delta_i),
+  // so dQ_i = s sum_j dS_ij (K_j - c) for any vector c.  The product above
+  // used dS rounded to bf16, whose row sums rs_i are not zero; where K has a
+  // large component shared by the keys a row attends to, that rounding is
+  // amplified.  Subtract rs_i c with c the mean of the block's last key tile
+  // (the diagonal keys, which the loop leaves in both buffers; rows past the
+  // block's last key repeat that key -- any constant c is exact): as an MFMA
+  // with A = -rs_i / 64 on every row of the tile.
+  rs += __shfl_xor(rs, 32, 64);
+  {
+    const uint32_t w = pk_bf16(-rs * (1.f / 64.f), -rs * (1.f / 64.f));
+    const uint4 ca = make_uint4(w, w, w, w);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dq[nb] = mma(ca, lo.tr_frag(K0, kb * 32 + 16 * i, nb), dq[nb]);
+  }
   // result blocks [32 queries x 32 dh]: lane = dh column, rows = queries
   bf16_t* dQb = a.dQ + (int64_t)b * a.q_bs / ldq * a.lddq + (int64_t)h * DH;
 #pragma unroll
@@ -959,6 +991,22 @@ sbp_status attn_run(const void* Q, const void* K, const void* V, const void* dO,
 }
 
 }  // namespace
+
+sbp_status attn_bwd_ws_size(int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh, int32_t D,
+                            int32_t dtype, size_t* bytes) {
+  sbp_status st = attn_check(B, T, Hq, Hkv, dh, D, dtype);
+  if (st == SBP_OK) *bytes = attn_ws(B, T, Hq, dh, D, dtype);
+  return st;
+}
+
+sbp_status attn_bwd_run(const void* Q, const void* K, const void* V, const void* dO, const void* O,
+                        const float* lse, int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
+                        float scale, int32_t D, int32_t dtype, int32_t accumulate, void* dQ,
+                        float* dK, float* dV, void* ws, size_t ws_bytes, hipStream_t str) {
+  return attn_run(Q, K, V, dO, O, lse, nullptr, 0, B, T, Hq, Hkv, dh, scale, D, dtype, accumulate,
+                  dQ, dK, dV, ws, ws_bytes, str);
+}
+
 }  // namespace sbp
 
 using namespace sbp;

@@ -27,18 +27,21 @@
 namespace sbp {
 
 __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict__ y, int64_t T,
-                                                       int32_t D, int32_t G, int reduction,
-                                                       int accumulate, LmPrep pr) {
+                                                       int64_t V, int32_t D, int32_t G,
+                                                       int reduction, int accumulate, LmPrep pr) {
   __shared__ int s_cnt[16];
+  __shared__ int s_bad;
   __shared__ int s_first[16];
   const int tid = threadIdx.x;
   const int64_t size = T / D;
   for (int c = tid; c < D; c += blockDim.x) pr.chunk_active[c] = 0;
+  if (tid == 0) s_bad = 0;
   __syncthreads();
-  int cnt = 0;
+  int cnt = 0, bad = 0;
   for (int64_t t = tid; t < T; t += blockDim.x) {
     if (y[t] >= 0) {
       ++cnt;
+      bad |= y[t] >= V;
       int64_t c = t / size;
       if (c > D - 1) c = D - 1;
       pr.chunk_active[c] = 1;
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict
   // block sum of cnt
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
   if ((tid & 63) == 0) s_cnt[tid >> 6] = cnt;
+  if (bad) s_bad = 1;
   __syncthreads();
   int first = D;
   for (int c = tid; c < D; c += blockDim.x)
@@ -63,7 +67,10 @@ __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict
     s_cnt[0] = n;
     s_first[0] = f;
     *pr.n_valid = n;
-    *pr.inv_norm = reduction == SBP_SUM ? 1.f : (n > 0 ? 1.f / (float)n : 0.f);
+    // a target id >= V (caller error) makes the normaliser NaN, and with it
+    // the loss and every gradient the call writes
+    *pr.inv_norm = s_bad ? __builtin_nanf("")
+                         : (reduction == SBP_SUM ? 1.f : (n > 0 ? 1.f / (float)n : 0.f));
     *pr.none_active = (f == D) ? 1 : 0;
   }
   __syncthreads();
@@ -77,10 +84,10 @@ __global__ __launch_bounds__(1024) void lm_prep_kernel(const int32_t* __restrict
   }
 }
 
-sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int reduction,
-                   int accumulate, const LmPrep& pr, hipStream_t st) {
+sbp_status lm_prep(const int32_t* targets, int64_t T, int64_t V, int32_t D, int32_t G,
+                   int reduction, int accumulate, const LmPrep& pr, hipStream_t st) {
   ProfScope prof("lm_prep", st, 0.0, 4.0 * T);
-  hipLaunchKernelGGL(lm_prep_kernel, dim3(1), dim3(1024), 0, st, targets, T, D, G, reduction,
+  hipLaunchKernelGGL(lm_prep_kernel, dim3(1), dim3(1024), 0, st, targets, T, V, D, G, reduction,
                      accumulate, pr);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
@@ -170,7 +177,8 @@ __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__
   block_lse(m, s);
   if (tid == 0) {
     const float lse = m + __logf(s);
-    const float ell = lse - z[y];
+    // ids >= V are a caller error: the read stays inside the row, the loss is NaN
+    const float ell = y < V ? lse - z[y] : __builtin_nanf("");
     const float w = weights ? weights[t] : 1.f;
     lse_out[r] = lse;
     loss_part[t] = w * ell;
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
                                                        int nparts, const float* __restrict__ ztgt,
                                                        const int32_t* __restrict__ targets,
                                                        const float* __restrict__ weights, int64_t s0,
-                                                       float* __restrict__ lse_out,
+                                                       int64_t V, float* __restrict__ lse_out,
                                                        float* __restrict__ loss_part,
                                                        float* __restrict__ token_loss) {
   const int r = blockIdx.x;
@@ -220,7 +228,8 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
   block_lse(m, sx);
   if (tid == 0) {
     const float lse = m + __logf(sx);
-    const float ell = lse - ztgt[r];
+    // an id >= V has no target logit (caller error): NaN loss
+    const float ell = y < V ? lse - ztgt[r] : __builtin_nanf("");
     const float w = weights ? weights[t] : 1.f;
     lse_out[r] = lse;
     loss_part[t] = w * ell;
@@ -229,11 +238,11 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const float2* __restrict_
 }
 
 sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* zt,
-                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
-                    float* loss_part, float* token_loss, hipStream_t st) {
+                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, int64_t V,
+                    float* lse, float* loss_part, float* token_loss, hipStream_t st) {
   ProfScope prof("ce_merge", st, 0.0, 8.0 * (double)Tc * nparts);
   hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)Tc), dim3(256), 0, st, parts, ldp, nparts, zt,
-                     targets, weights, s, lse, loss_part, token_loss);
+                     targets, weights, s, V, lse, loss_part, token_loss);
   SBP_LAUNCH_CHECK();
   return SBP_OK;
 }
@@ -252,10 +261,12 @@ __global__ __launch_bounds__(256) void lp_rows_kernel(const float2* __restrict__
   const int64_t t = s0 + r;
   const int tid = threadIdx.x;
   const int y = targets[t];
-  if (y < 0) {
+  if (y < 0 || y >= V) {
+    // ignored token: zeros; an id >= V (caller error): NaN, nothing read
     if (tid == 0) {
-      logprob[t] = 0.f;
-      if (lse_out) lse_out[t] = 0.f;
+      const float f = y < 0 ? 0.f : __builtin_nanf("");
+      logprob[t] = f;
+      if (lse_out) lse_out[t] = f;
     }
     return;
   }

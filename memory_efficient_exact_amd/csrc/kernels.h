@@ -66,21 +66,22 @@ sbp_status gemm_nt(int dtype, int epi, GemmParams p, int tile, hipStream_t st, c
 // ------------------------------------------------------- LM head + CE ----
 struct LmPrep {   // device-side scalars written by lm_prep
   int* n_valid;       // [1]
-  float* inv_norm;    // [1]  1/N (mean_valid, N>0), 1 (sum), 0 (N == 0)
+  float* inv_norm;    // [1]  1/N (mean_valid, N>0), 1 (sum), 0 (N == 0), NaN (a target >= V)
   int* chunk_active;  // [D]
   int* group_active;  // [ceil(D/G)]  1 if a chunk of dW group g (chunks gG .. gG+G-1) is active
   int* beta_zero;     // [ceil(D/G)]  1 for the group whose dW GEMM must overwrite
   int* none_active;   // [1]  1 if no chunk has a valid token
 };
-sbp_status lm_prep(const int32_t* targets, int64_t T, int32_t D, int32_t G, int reduction,
-                   int accumulate, const LmPrep& pr, hipStream_t st);
+// A target id >= V (a caller error) sets inv_norm to NaN.
+sbp_status lm_prep(const int32_t* targets, int64_t T, int64_t V, int32_t D, int32_t G,
+                   int reduction, int accumulate, const LmPrep& pr, hipStream_t st);
 // Per-row log-sum-exp and per-token loss for rows [s, s+Tc) of one chunk.
 // Row statistics from the logits GEMM's per-64-column partials (nparts per
 // row, pitch ldp): lse, l_t = lse - z_t[y_t], c_t l_t, with z_t[y_t] the fp32
 // target logit the GEMM wrote into zt [Tc].
 sbp_status ce_merge(const float2* parts, int64_t ldp, int nparts, const float* zt,
-                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, float* lse,
-                    float* loss_part, float* token_loss, hipStream_t st);
+                    const int32_t* targets, const float* weights, int64_t s, int64_t Tc, int64_t V,
+                    float* lse, float* loss_part, float* token_loss, hipStream_t st);
 sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const float* weights,
                     int64_t s, int64_t Tc, int64_t V, float* lse, float* loss_part,
                     float* token_loss, hipStream_t st);
@@ -96,7 +97,7 @@ sbp_status ce_grad(int dtype, const void* Z, const float2* parts, int64_t ldp, i
                    hipStream_t st);
 // Per-token target log-probability of rows [s, s+Tc) of one chunk:
 // logprob[s+r] = z_r[y] - lse_r and (if lse_out is not NULL) lse_out[s+r] =
-// lse_r, both 0 where y = targets[s+r] < 0.  From the logits GEMM's
+// lse_r, both 0 where y = targets[s+r] < 0 and NaN where y >= V.  From the logits GEMM's
 // per-64-column partials and target logits zt[r] when parts is not NULL,
 // else from a pass over the fp32 logits Z [Tc, ldz] (V columns).
 sbp_status lp_rows(const float2* parts, int64_t ldp, int nparts, const float* zt, const float* Z,

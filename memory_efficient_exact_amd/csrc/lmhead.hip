@@ -196,7 +196,7 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
     if (_s != SBP_OK) return _s;     \
   } while (0)
 
-  SBP_TRY(lm_prep(targets, T, D, s.G, reduction, accumulate, w.prep, str));
+  SBP_TRY(lm_prep(targets, T, V, D, s.G, reduction, accumulate, w.prep, str));
   // W^T [d, Vp], zero columns V..Vp (they meet the zero pad of dZ in the dH
   // GEMM)
   SBP_TRY(transpose_pad(dtype, W, d, V, d, w.Wt, s.Vp, s.Vp, nullptr, str));
@@ -230,7 +230,7 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
       g1.row_target = targets + s0;
       g1.target_out = w.ztgt;
       SBP_TRY(gemm_nt(dtype, EPI_REL16_LSE, g1, GEMM_TILE_RING, str, "gemm_logits"));
-      SBP_TRY(ce_merge(w.parts, s.nparts, s.nparts, w.ztgt, targets, weights, s0, Tc, w.lse,
+      SBP_TRY(ce_merge(w.parts, s.nparts, s.nparts, w.ztgt, targets, weights, s0, Tc, V, w.lse,
                        w.loss_part, token_loss, str));
     } else {
       SBP_TRY(gemm_nt(dtype, EPI_F32, g1, GEMM_TILE_RING, str, "gemm_logits"));
@@ -324,7 +324,7 @@ static sbp_status lmhead_logprob_impl(const void* H, const void* W, const int32_
   lp_plan(s, (char*)ws, &w);
   hipStream_t str = (hipStream_t)stream;
   const char* Hb = (const char*)H;
-  sbp_status r = lm_prep(targets, T, D, 1, SBP_SUM, 0, w.prep, str);
+  sbp_status r = lm_prep(targets, T, V, D, 1, SBP_SUM, 0, w.prep, str);
   for (int32_t c = 0; c < D && r == SBP_OK; ++c) {
     int64_t s0, e0;
     chunk_bounds(T, D, c, &s0, &e0);

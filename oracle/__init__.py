@@ -37,12 +37,12 @@ central finite differences, against independent torch fp64 autograd, against
 closed forms and special cases, and against hand-derived golden values.
 No function here is "parity unpinned".
 """
-from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_logprob, lmhead_logprob_rows
+from .lmhead import lmhead_ce, lmhead_ce_rows, lmhead_dW_rows, lmhead_logprob, lmhead_logprob_rows
 from .attention import attn_fwd, attn_bwd, attn_bwd_sampled, attn_bwd_packed
 from .layer import layer_fwd, layer_bwd, rmsnorm_fwd, rmsnorm_bwd, rope, rope_positions
 from .model import model_fwd, model_bwd, model_bwd_at
 from . import chunked
 
-__all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
+__all__ = ["lmhead_ce", "lmhead_ce_rows", "lmhead_dW_rows", "lmhead_logprob", "lmhead_logprob_rows", "attn_fwd", "attn_bwd",
            "attn_bwd_sampled", "attn_bwd_packed", "layer_fwd", "layer_bwd", "rmsnorm_fwd",
            "rmsnorm_bwd", "rope", "rope_positions", "model_fwd", "model_bwd", "model_bwd_at", "chunked"]

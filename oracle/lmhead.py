@@ -44,6 +44,7 @@ read here as the plain log-softmax of the logits at the target::
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 
 def _as64(a):
@@ -145,6 +146,49 @@ def lmhead_ce_rows(H, W, targets, weights, rows, N, reduction="mean_valid"):
         dZ = (c / n)[:, None] * P
     dZ[~valid] = 0.0
     return dZ @ W, ell, np.where(valid, lse, np.nan)
+
+
+def lmhead_dW_rows(H, W, targets, weights, vrows, reduction="mean_valid", row_block=1024):
+    """Selected rows of dW at any T, for full-size spot checks.
+
+    dW[v] = sum_t dZ_tv h_t with dZ_tv = (c_t/N)(exp(Z_tv - lse_t) - [y_t = v]).
+    Column v of dZ needs lse_t of every token, and lse_t needs the whole
+    logits row t, so every valid row's logits are formed over fixed blocks of
+    ``row_block`` rows (a host-memory bound only, independent of any chunk
+    count; each softmax row complete), but only the columns ``vrows`` of dZ
+    are kept.  Rows with c_t = 0 (ignored, or weight 0) add nothing and are
+    skipped.  Returns ``(dW_rows [len(vrows), d], loss, scale)`` with
+    ``scale = (1/N) sum_t |c_t| l_t``, the size of the loss before signed
+    weights cancel.
+    """
+    H = np.asarray(H)
+    W = _as64(W)
+    vrows = np.asarray(vrows, dtype=np.int64)
+    d = W.shape[1]
+    y, valid, c, N = _coeffs(targets, weights, reduction)
+    out = np.zeros((vrows.shape[0], d))
+    if N == 0:
+        return out, 0.0, 0.0
+    live = np.nonzero(c != 0.0)[0]
+    total = 0.0
+    total_abs = 0.0
+    rb = int(row_block)
+    for b0 in range(0, live.shape[0], rb):
+        rows = live[b0:b0 + rb]
+        Hb = _as64(H[rows])
+        Z = Hb @ W.T
+        # the same log-sum-exp as _logsumexp_rows, through torch's threaded
+        # fp64 routine (the pass over T x V logits dominates at full size)
+        lse = torch.logsumexp(torch.from_numpy(Z), dim=1).numpy()
+        yb = y[rows]
+        ell = lse - Z[np.arange(rows.shape[0]), yb]
+        total += float((c[rows] * ell).sum())
+        total_abs += float((np.abs(c[rows]) * ell).sum())
+        Ps = np.exp(Z[:, vrows] - lse[:, None])            # softmax columns vrows
+        del Z
+        Ps -= (yb[:, None] == vrows[None, :])              # one-hot at the target
+        out += (Ps * (c[rows] / N)[:, None]).T @ Hb
+    return out, total / N, total_abs / N
 
 
 def lmhead_logprob(H, W, targets, row_block=None):

@@ -1,7 +1,9 @@
 """Debug mode (SBP_DEBUG=1): device-side checks of target ids and packed
 sequence boundaries before any of a call's own kernels run, and a stream
-synchronisation after them.  Bad inputs are only ever passed with debug
-mode on: without it they are caller errors the kernels do not look at."""
+synchronisation after them.  Bad packed-sequence bounds are only ever
+passed with debug mode on (without it the kernels clamp them but do not
+check them); target ids past the vocabulary without debug mode are covered
+in test_gpu_edge.py (NaN outputs, every read in bounds)."""
 import pytest
 import torch
 

@@ -1,6 +1,8 @@
 """Degenerate shapes on the GPU against the oracle: a single token, a
 one-word vocabulary (loss and every gradient exactly zero), and one-token
 layer, forward and model calls with rotary embedding and QK-norm."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -91,3 +93,29 @@ def test_single_token_model():
     assert normwise(dgf.cpu().numpy(), rdg) <= TOL
     for k in ("Wv", "Wo", "W1", "W2", "W3", "g2"):
         assert normwise(grads[0][k].cpu().numpy(), rgr[0][k]) <= TOL, k
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_target_id_beyond_vocabulary_is_loud_not_out_of_bounds(d):
+    # a target id >= V is a caller error; without debug mode every read stays
+    # in bounds and the error shows as NaN: the loss, dH, dW and that token's
+    # loss (d = 128: fused row statistics; d = 64: the fp32 logits pass)
+    inp = synthetic.lmhead_inputs(256, d, 512, "bf16", seed=44, w_std=0.05)
+    inp.targets[17] = 512
+    inp.targets[200] = 1 << 30
+    H, W, tg = inp.H.to(DEV), inp.W.to(DEV), inp.targets.to(DEV)
+    loss, dH, dW, tl = sbp.lmhead_ce(H, W, tg, D=3, token_loss=True)
+    lp, ls = sbp.lmhead_logprob(H, W, tg, D=3, lse=True)
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item())
+    assert torch.isnan(dH.float()).all() and torch.isnan(dW).all()
+    assert torch.isnan(tl[17]) and torch.isnan(tl[200])
+    # the forward log-prob marks exactly the bad tokens
+    bad = torch.zeros(256, dtype=torch.bool)
+    bad[[17, 200]] = True
+    assert torch.isnan(lp.cpu()[bad]).all() and torch.isnan(ls.cpu()[bad]).all()
+    assert torch.isfinite(lp.cpu()[~bad]).all() and torch.isfinite(ls.cpu()[~bad]).all()
+    tgt = inp.targets.clone()
+    tgt[bad] = -1
+    rlp, rls = oracle.lmhead_logprob(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W), tgt.numpy())
+    assert normwise(lp.cpu().numpy()[~bad.numpy()], rlp[~bad.numpy()]) <= TOL

@@ -109,6 +109,19 @@ def test_full_size_T65536_prefix():
     _check(dx[:P], gr, rdx, rgr)
 
 
+def test_full_width_dense_upstream_T4096():
+    """The decoder-layer workload's full width (d=4096, 32/8 heads of 128,
+    F=14336) at T=4096 with D=16 and a dense N(0,1) upstream gradient on
+    every token: all 16 chunks add live gradients into dK/dV and every fp32
+    weight and gain gradient, compared element by element with the fp64
+    oracle on the whole sequence."""
+    L = synthetic.layer_inputs(4096, 4096, 32, 8, 128, 14336, "bf16", seed=4096, w_std=0.02,
+                               gain_std=0.1)
+    dx, gr = _gpu(L, 16)
+    rdx, rgr, _ = _oracle(L)
+    _check(dx, gr, rdx, rgr)
+
+
 # ---- packed independent sequences (sbp_layer_bwd_packed) -----------------
 def _gpu_packed(L, D, cu, grads=None, accumulate=False):
     dev = torch.device("cuda:0")

@@ -137,9 +137,29 @@ def test_gpu_D_invariance_bf16():
 
 
 # ---- full-size workloads: sampled rows + size-free identities ------------
-def _full_size(index, rows):
+def _vocab_sample(V, y, rng, n_rand=16):
+    """dW rows to compare: the first and last rows, rows on both sides of
+    256-row tile edges (one early, one at the last full tile), the rows that
+    are the target of the most tokens, and random rows."""
+    last_tile = (V // 256) * 256
+    edges = [0, 1, 255, 256, 8191, 8192, last_tile - 1, min(last_tile, V - 1), V - 1]
+    counts = np.bincount(y[y >= 0], minlength=V)
+    heavy = np.argsort(counts, kind="stable")[-4:]
+    return np.unique(np.concatenate([edges, heavy, rng.integers(0, V, n_rand)]))
+
+
+def _check_dW_rows(inp, dW, vrows, tol=2e-2):
+    ref, _, _ = oracle.lmhead_dW_rows(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                      inp.targets.numpy(), synthetic.to_f64(inp.weights), vrows)
+    got = dW[torch.from_numpy(vrows).cuda()].double().cpu().numpy()
+    e = normwise(got, ref)
+    assert e <= tol, e
+    return e
+
+
+def _full_size(index, rows, vrows=None, inp=None):
     cfg = synthetic.WORKLOADS[index]
-    inp = synthetic.workload_inputs(index)
+    inp = synthetic.workload_inputs(index) if inp is None else inp
     loss, dH, dW, tl = _run(inp, cfg["D"])
     y = inp.targets.numpy()
     N = int((y >= 0).sum())
@@ -161,13 +181,49 @@ def _full_size(index, rows):
     c = np.where(y >= 0, 1.0 if inp.weights is None else inp.weights.numpy(), 0.0)
     L = float((c * tl.double().cpu().numpy()).sum()) / N
     assert abs(loss.item() - L) <= 1e-4 * max(abs(L), 1e-3)
+    if vrows is not None:
+        # dW rows element by element: every token's lse enters each column
+        _check_dW_rows(inp, dW, vrows)
     return inp
 
 
 def test_full_size_bf16_T32768_V128256():
     rng = np.random.default_rng(0)
     rows = np.concatenate([[0, 1, 2047, 2048, 32767], rng.integers(0, 32768, 27)])
-    _full_size(1, rows)
+    inp = synthetic.workload_inputs(1)
+    # two vocab rows made the target of many tokens, spread over all chunks
+    # (their one-hot terms are summed across every dW group)
+    y = inp.targets
+    y[rng.integers(0, 32768, 600)] = 77777
+    y[rng.integers(0, 32768, 60)] = 128255
+    vrows = _vocab_sample(128256, y.numpy(), rng)
+    _full_size(1, rows, vrows, inp=inp)
+
+
+@pytest.mark.parametrize("D,n_seq", [(8, 2), (32, 8)])
+def test_dW_rows_weighted_masked_V152064_d3584(D, n_seq):
+    # the weighted workload's vocabulary and width at T = 16384: packed
+    # sequences, first quarter of each masked (whole chunks skipped on the
+    # device, dW groups mixing skipped and live chunks), one N(0,1) weight
+    # per sequence; dW rows element by element and dH on sampled rows
+    T = 16384
+    inp = synthetic.lmhead_inputs(T, 3584, 152064, "bf16", seed=1004 + D, w_std=0.02,
+                                  n_seq=n_seq, masked_frac=0.25, weighted=True)
+    loss, dH, dW, tl = _run(inp, D)
+    rng = np.random.default_rng(D)
+    y = inp.targets.numpy()
+    vrows = _vocab_sample(152064, y, rng)
+    ref_rows, L, scale = oracle.lmhead_dW_rows(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                               y, synthetic.to_f64(inp.weights), vrows)
+    got = dW[torch.from_numpy(vrows).cuda()].double().cpu().numpy()
+    assert normwise(got, ref_rows) <= 2e-2, normwise(got, ref_rows)
+    N = int((y >= 0).sum())
+    rows = np.concatenate([[0, T // n_seq // 4 - 1, T // n_seq // 4, T - 1], rng.integers(0, T, 28)])
+    rH, rtl, _ = oracle.lmhead_ce_rows(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W), y,
+                                       synthetic.to_f64(inp.weights), rows, N)
+    assert normwise(dH[torch.from_numpy(rows).cuda()].float().cpu().numpy(), rH) <= 2e-2
+    assert abs(loss.item() - L) <= 2e-2 * max(abs(L), scale), (loss.item(), L, scale)
+    assert (dH[torch.from_numpy(y < 0).cuda()] == 0).all()
 
 
 def test_full_size_weighted_T131072_V152064():

@@ -142,6 +142,34 @@ def test_sampled_rows_match_full():
     np.testing.assert_array_equal(np.isnan(lser), np.isnan(lse[rows]))
 
 
+@pytest.mark.parametrize("reduction", ["mean_valid", "sum"])
+@pytest.mark.parametrize("row_block", [1, 4, 1024])
+def test_sampled_dW_rows_match_full(reduction, row_block):
+    # selected vocab rows of dW, every row's lse over blocks of rows, against
+    # the full gradient; rows 0 and V-1 and one that is the target of many
+    # tokens (its one-hot term is summed over all of them)
+    H, W, y, w = _rand(T=41, d=6, V=23, seed=21)
+    y[::3] = 7
+    vrows = np.array([0, 7, 11, 22, 7])
+    L, _, dW, tl, _ = oracle.lmhead_ce(H, W, y, w, reduction)
+    dWr, Lr, Sr = oracle.lmhead_dW_rows(H, W, y, w, vrows, reduction, row_block=row_block)
+    np.testing.assert_allclose(dWr, dW[vrows], rtol=0, atol=1e-14)
+    assert abs(Lr - L) < 1e-12
+    N = int((y >= 0).sum()) if reduction == "mean_valid" else 1
+    assert abs(Sr - float((np.abs(np.where(y >= 0, w, 0.0)) * tl).sum()) / N) < 1e-12
+
+
+def test_sampled_dW_rows_zero_weights_and_all_ignored():
+    H, W, y, w = _rand(T=20, d=5, V=9, seed=22)
+    w[:10] = 0.0
+    _, _, dW, _, _ = oracle.lmhead_ce(H, W, y, w)
+    dWr, _, _ = oracle.lmhead_dW_rows(H, W, y, w, np.arange(9), row_block=3)
+    np.testing.assert_allclose(dWr, dW, rtol=0, atol=1e-14)
+    y[:] = -1
+    dWr, Lr, Sr = oracle.lmhead_dW_rows(H, W, y, w, np.arange(9))
+    assert Lr == 0.0 and Sr == 0.0 and (dWr == 0).all()
+
+
 @pytest.mark.parametrize("T,D", [(13, 1), (13, 2), (13, 3), (13, 13), (64, 5)])
 def test_chunked_equals_unchunked(T, D):
     H, W, y, w = _rand(T=T, d=6, V=17, seed=T + D)
