@@ -181,6 +181,29 @@ sbp_status sbp_attn_bwd_chunked(const void* Q, const void* K, const void* V, con
                                 float* dV, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 2a. The attention backward of (2) without a workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight training or serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, computation and results as sbp_attn_bwd_chunked, minus
+ * `ws` and `ws_bytes`: the call allocates nothing, and its scratch (the
+ * per-chunk LSE and Delta rows, 8 * B * Hq * (chunk length rounded up to 64,
+ * plus 64) bytes) lives in a static device array of 16 MiB that each GPU the
+ * library runs on holds until the process ends.  A call whose scratch would
+ * exceed 16 MiB returns SBP_ERR_UNSUPPORTED before any launch (raise D, or
+ * use sbp_attn_bwd_chunked).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (several streams or host threads) race, and
+ * must be ordered by the caller.  The first call on a device looks up that
+ * device's copy of the array (it must be the current device).
+ * ---------------------------------------------------------------------- */
+sbp_status sbp_attn_bwd_chunked_noalloc(const void* Q, const void* K, const void* V,
+                                        const void* dO, const void* O, const float* lse,
+                                        int64_t B, int64_t T, int32_t Hq, int32_t Hkv,
+                                        int32_t dh, float scale, int32_t D, int32_t dtype,
+                                        int32_t accumulate, void* dQ, float* dK, float* dV,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------
  * 2b. Causal GQA attention backward over packed independent sequences.
  *
  * Passage: skill page, "Practical Guidance" -- attention masks must hold

@@ -46,6 +46,8 @@ SIGNATURES = {
     "sbp_attn_bwd_workspace_size": (i32, [i64, i64, i32, i32, i32, i32, i32, C.POINTER(sz)]),
     "sbp_attn_bwd_chunked": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32,
                                    i32, i32, vp, vp, vp, vp, sz, vp]),
+    "sbp_attn_bwd_chunked_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32,
+                                           i32, i32, i32, vp, vp, vp, vp]),
     "sbp_attn_bwd_packed_workspace_size": (i32, [i64, i32, i32, i32, i32, i32, C.POINTER(sz)]),
     "sbp_attn_bwd_packed": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, i32,
                                   i32, i32, vp, vp, vp, vp, sz, vp]),
