@@ -169,7 +169,8 @@ sbp_status sbp_lmhead_logprob_fwd(const void* H, const void* W, const int32_t* t
  *                                        the scaled scores)
  * dQ     [B, T, Hq, dh]  dtype out
  * dK, dV [B, T, Hkv, dh] fp32 out  (accumulate semantics)
- * Supported: dh in {64, 128}; Hq % Hkv == 0.
+ * Supported: dtype SBP_BF16 or SBP_F32 (fp32: every array fp32, every
+ * product an fp32 multiply-add); dh in {64, 128}; Hq % Hkv == 0.
  * ---------------------------------------------------------------------- */
 sbp_status sbp_attn_bwd_workspace_size(int64_t B, int64_t T, int32_t Hq, int32_t Hkv,
                                        int32_t dh, int32_t D, int32_t dtype, size_t* bytes);
@@ -270,7 +271,9 @@ sbp_status sbp_attn_bwd_packed(const void* Q, const void* K, const void* V, cons
  *   Wq [Hq*dh, d]; Wk, Wv [Hkv*dh, d]; Wo [d, Hq*dh]; W1, W3 [F, d]; W2 [d, F]
  * grads   (host struct of device pointers, fp32, same shapes; accumulate
  *          semantics)
- * Supported: dh in {64, 128}; Hq % Hkv == 0; d % 8 == 0; F % 8 == 0.
+ * Supported: desc->dtype SBP_BF16 or SBP_F32 (fp32: x, dy, dx, weights and
+ * every intermediate fp32); dh in {64, 128}; Hq % Hkv == 0; d % 8 == 0;
+ * F % 8 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t T, d;

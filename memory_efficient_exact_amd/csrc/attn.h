@@ -60,6 +60,13 @@ sbp_status attn_bwd_chunk(const AttnArgs& a, int dh, int B, hipStream_t st);
 sbp_status attn_seq_bounds(const int32_t* cu, int nseq, int64_t T, int* seq_lo, int* seq_hi,
                            hipStream_t st);
 
+// fp32 mode (attn_f32.hip): the same three steps with AttnArgs whose array
+// pointers hold fp32 data (Q, K, V, dO, O, dQ), every product an fp32 FMA.
+sbp_status attn_fwd_f32(const AttnArgs& a, int dh, int B, hipStream_t st);
+sbp_status attn_delta_f32(const AttnArgs& a, const void* O, const float* lse_src, int64_t lsb,
+                          int64_t lst, int dh, int B, hipStream_t st);
+sbp_status attn_bwd_chunk_f32(const AttnArgs& a, int dh, int B, hipStream_t st);
+
 // The chunked attention backward of sbp_attn_bwd_chunked on a given
 // workspace (every argument checked first), and the size that workspace
 // needs (SBP_OK and *bytes set, or an argument error).

@@ -908,7 +908,6 @@ sbp_status attn_check(int64_t B, int64_t T, int32_t Hq, int32_t Hkv, int32_t dh,
   if (D < 1 || D > T) return set_error(SBP_ERR_INVALID_ARG, "need 1 <= D <= T (D=%d, T=%lld)", D, (long long)T);
   if (Hq % Hkv) return set_error(SBP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (dh != 64 && dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", dh);
-  if (dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "attention backward is implemented for bf16 only");
   if (T > (1ll << 30) || B > 65535 || Hq > 65535) return set_error(SBP_ERR_UNSUPPORTED, "size out of supported range");
   return SBP_OK;
 }
@@ -977,14 +976,16 @@ sbp_status attn_run(const void* Q, const void* K, const void* V, const void* dO,
     a.delta = w_dl; a.dl_sb = (int64_t)Hq * Lp; a.dl_sh = Lp; a.dl_st = 1;
     a.lse = w_lse; a.lse_sb = (int64_t)Hq * Lp; a.lse_sh = Lp; a.lse_st = 1;
     a.seq_lo = seq_lo; a.seq_hi = seq_hi;
+    const bool f32 = dtype == SBP_F32;  // the pointers then hold fp32 arrays
     if (lse) {
       // caller's O and LSE ([B, T, Hq]): Delta, and LSE copied into the chunk layout
-      st = attn_delta(a, O, lse, T * Hq, Hq, dh, (int)B, str);
+      st = f32 ? attn_delta_f32(a, O, lse, T * Hq, Hq, dh, (int)B, str)
+               : attn_delta(a, O, lse, T * Hq, Hq, dh, (int)B, str);
     } else {
-      st = attn_fwd(a, dh, (int)B, str);
+      st = f32 ? attn_fwd_f32(a, dh, (int)B, str) : attn_fwd(a, dh, (int)B, str);
     }
     if (st != SBP_OK) return st;
-    st = attn_bwd_chunk(a, dh, (int)B, str);
+    st = f32 ? attn_bwd_chunk_f32(a, dh, (int)B, str) : attn_bwd_chunk(a, dh, (int)B, str);
     if (st != SBP_OK) return st;
   }
   return SBP_OK;

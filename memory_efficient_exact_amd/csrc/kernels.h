@@ -119,19 +119,23 @@ sbp_status fill_zero_f32(float* p, int64_t n, const int* when, hipStream_t st);
 sbp_status fill_zero_bytes(void* p, int64_t nbytes, hipStream_t st);
 
 // ------------------------------------------------------- decoder layer ----
+// Token-wise kernels take bf16 rows, or fp32 rows with dtype SBP_F32.
 sbp_status rmsnorm_fwd(const void* x, int64_t ldx, const void* g, int64_t rows, int64_t d,
-                       float eps, void* out, int64_t ldo, float* rinv, hipStream_t st);
+                       float eps, void* out, int64_t ldo, float* rinv, hipStream_t st,
+                       int dtype = SBP_BF16);
 // out = resid + RMSNorm'(dn) (resid may be NULL)
 sbp_status rmsnorm_bwd(const void* x, int64_t ldx, const void* g, const float* dn, int64_t ldn,
                        const float* rinv, const void* resid, int64_t ldr, int64_t rows, int64_t d,
-                       void* out, int64_t ldo, hipStream_t st);
+                       void* out, int64_t ldo, hipStream_t st, int dtype = SBP_BF16);
 // part: gain_grad_splits(rows) * d floats of scratch
 int gain_grad_splits(int64_t rows);
 sbp_status gain_grad(const float* dn, int64_t ldn, const void* x, int64_t ldx, const float* rinv,
-                     int64_t rows, int64_t d, float* dg, int beta, float* part, hipStream_t st);
-sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStream_t st);
+                     int64_t rows, int64_t d, float* dg, int beta, float* part, hipStream_t st,
+                     int dtype = SBP_BF16);
+sbp_status swiglu_fwd(const void* ug, int64_t rows, int64_t F, void* m, hipStream_t st,
+                      int dtype = SBP_BF16);
 sbp_status swiglu_bwd(const void* dm, const void* ug, int64_t rows, int64_t F, void* dudg,
-                      hipStream_t st);
+                      hipStream_t st, int dtype = SBP_BF16);
 sbp_status rows_to_bf16(const float* src, int64_t lds_, int64_t rows, int64_t cols, void* dst,
                         int64_t ldd, hipStream_t st);
 sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols, float* dst,
@@ -142,19 +146,30 @@ sbp_status rows_to_f32(const void* src, int64_t lds_, int64_t rows, int64_t cols
 // adds) through part [HEADNORM_PARTS, dh] floats of scratch.
 constexpr int HEADNORM_PARTS = 1024;
 sbp_status headnorm_fwd(const void* x, int64_t ldx, void* out, int64_t ldo, int64_t rows, int H,
-                        int dh, const void* g, float eps, hipStream_t st);
+                        int dh, const void* g, float eps, hipStream_t st, int dtype = SBP_BF16);
 sbp_status headnorm_bwd(const void* x, int64_t ldx, const void* dy, int64_t ldy, void* dx,
                         int64_t ldd, int64_t rows, int H, int dh, const void* g, float eps,
-                        float* dg, int beta, float* part, hipStream_t st);
+                        float* dg, int beta, float* part, hipStream_t st, int dtype = SBP_BF16);
 // Rotary embedding: tab [P, dh/2] of (cos, sin) for positions 0 .. P-1;
 // rope_apply turns rows [0, rows) of src (H heads of width dh, fp32 or bf16,
-// pitch lds_) into dst (bf16, pitch ldd; dst == src allowed for bf16), row r
+// pitch lds_) into dst (bf16, or fp32 from fp32 with dst_f32; pitch ldd;
+// dst == src allowed when the types match), row r
 // at position row0 + r - seq_lo[row0 + r] (seq_lo NULL: row0 + r);
 // inverse turns by the negative angle.
 sbp_status rope_table(float2* tab, int64_t P, int dh, double theta, hipStream_t st);
 sbp_status rope_apply(const void* src, bool src_f32, int64_t lds_, void* dst, int64_t ldd,
                       int64_t rows, int H, int dh, int64_t row0, const int* seq_lo,
-                      const float2* tab, bool inverse, hipStream_t st);
+                      const float2* tab, bool inverse, hipStream_t st, bool dst_f32 = false);
+
+// ------------------------------------------- decoder layer, fp32 mode ----
+// (layer_f32.hip) Workspace bytes and the two runs; the arguments are
+// checked by the entry points in layer.hip.
+size_t layer_f32_ws(const sbp_layer_desc* desc, int32_t D, bool bwd, bool packed);
+sbp_status layer_f32_bwd(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq, const void* x,
+                         const void* dy, const sbp_layer_weights* w, int32_t D, int32_t accumulate,
+                         void* dx, sbp_layer_grads* g, void* ws, hipStream_t st);
+sbp_status layer_f32_fwd(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq, const void* x,
+                         const sbp_layer_weights* w, int32_t D, void* y, void* ws, hipStream_t st);
 
 // ------------------------------------------------------------ debug mode ----
 // SBP_DEBUG set (and not "0"): device-side input checks before a call's

@@ -130,7 +130,6 @@ sbp_status layer_check(const sbp_layer_desc* L, int32_t D) {
   if (L->qk_norm != 0 && L->qk_norm != 1) return set_error(SBP_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
   if (L->dh != 64 && L->dh != 128) return set_error(SBP_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", L->dh);
   if (L->d % 8 || L->F % 8) return set_error(SBP_ERR_UNSUPPORTED, "d and F must be multiples of 8");
-  if (L->dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "the decoder-layer backward is implemented for bf16 only");
   if (L->T > (1ll << 30) || L->d > (1ll << 20) || L->F > (1ll << 24)) return set_error(SBP_ERR_UNSUPPORTED, "size out of supported range");
   return SBP_OK;
 }
@@ -155,9 +154,11 @@ sbp_status layer_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t nseq
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   const LayerShape S = layer_shape(desc, D);
   const bool packed = cu != nullptr;
-  const size_t need = layer_plan(S, packed, nullptr, nullptr);
+  const bool f32 = desc->dtype == SBP_F32;
+  const size_t need = f32 ? layer_f32_ws(desc, D, true, packed) : layer_plan(S, packed, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (f32) return layer_f32_bwd(desc, cu, nseq, x, dy, w, D, accumulate, dx, g, ws, str);
   LayerWs W;
   layer_plan(S, packed, (char*)ws, &W);
   const int64_t d = S.d, F = S.F, qd = S.qd, kd = S.kd, qkvd = S.qkvd;
@@ -410,9 +411,11 @@ sbp_status layer_fwd_run(const sbp_layer_desc* desc, const int32_t* cu, int32_t 
   if (cu && nseq < 1) return set_error(SBP_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
   if (x == y) return set_error(SBP_ERR_INVALID_ARG, "y must not alias x");
   const LayerShape S = layer_shape(desc, D);
-  const size_t need = layer_fwd_plan(S, nullptr, nullptr);
+  const bool f32 = desc->dtype == SBP_F32;
+  const size_t need = f32 ? layer_f32_ws(desc, D, false, true) : layer_fwd_plan(S, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (f32) return layer_f32_fwd(desc, cu, nseq, x, w, D, y, ws, str);
   LayerFwdWs W;
   layer_fwd_plan(S, (char*)ws, &W);
   const int64_t d = S.d, F = S.F, qd = S.qd, kd = S.kd;
@@ -504,7 +507,8 @@ extern "C" sbp_status sbp_layer_fwd_workspace_size(const sbp_layer_desc* desc, i
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = layer_check(desc, D);
   if (st != SBP_OK) return st;
-  *bytes = layer_fwd_plan(layer_shape(desc, D), nullptr, nullptr);
+  *bytes = desc->dtype == SBP_F32 ? layer_f32_ws(desc, D, false, true)
+                                  : layer_fwd_plan(layer_shape(desc, D), nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -526,7 +530,8 @@ extern "C" sbp_status sbp_layer_bwd_workspace_size(const sbp_layer_desc* desc, i
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = layer_check(desc, D);
   if (st != SBP_OK) return st;
-  *bytes = layer_plan(layer_shape(desc, D), false, nullptr, nullptr);
+  *bytes = desc->dtype == SBP_F32 ? layer_f32_ws(desc, D, true, false)
+                                  : layer_plan(layer_shape(desc, D), false, nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -546,7 +551,8 @@ extern "C" sbp_status sbp_layer_bwd_packed_workspace_size(const sbp_layer_desc* 
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = layer_check(desc, D);
   if (st != SBP_OK) return st;
-  *bytes = layer_plan(layer_shape(desc, D), true, nullptr, nullptr);
+  *bytes = desc->dtype == SBP_F32 ? layer_f32_ws(desc, D, true, true)
+                                  : layer_plan(layer_shape(desc, D), true, nullptr, nullptr);
   return SBP_OK;
 }
 

@@ -195,3 +195,62 @@ def test_packed_full_size_T16384_sampled_sequences():
         assert normwise(dQ[:, a:b].float().cpu().numpy(), rQ) <= TOL, n
         assert normwise(dK[:, a:b].cpu().numpy(), rK) <= TOL, n
         assert normwise(dV[:, a:b].cpu().numpy(), rV) <= TOL, n
+
+
+# ---- fp32 mode: every product in fp32, normwise <= 1e-4 -------------------
+TOL_F32 = 1e-4
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,dh,D", [
+    (1, 300, 4, 2, 64, 3),      # ragged T and chunks, GQA
+    (2, 257, 4, 1, 128, 1),     # B > 1, one chunk, MQA
+    (1, 96, 2, 2, 64, 96),      # D = T
+    (1, 1000, 4, 4, 128, 7),    # MHA, several key tiles per chunk
+])
+def test_parity_fp32(B, T, Hq, Hkv, dh, D):
+    inp = synthetic.attn_inputs(B, T, Hq, Hkv, dh, "f32", seed=3 * T + Hq + dh + D)
+    s = 1.0 / math.sqrt(dh)
+    dQ, dK, dV = _gpu(inp, D)
+    assert dQ.dtype == torch.float32
+    rQ, rK, rV, _, _ = _ref(inp, s)
+    errs = (normwise(dQ.cpu().numpy(), rQ), normwise(dK.cpu().numpy(), rK),
+            normwise(dV.cpu().numpy(), rV))
+    assert all(e <= TOL_F32 for e in errs), errs
+
+
+def test_fp32_single_token():
+    # one token attends only to itself: P = 1, so dS = P (dP - Delta) is 0 in
+    # exact arithmetic and dQ = dK = 0 (the reference is exactly zero, so a
+    # normwise ratio is undefined); in fp32, dP and Delta are sums in
+    # different orders and leave a residue of the order of fp32 rounding of
+    # the terms dO . V; dV = dO summed over the group
+    inp = synthetic.attn_inputs(1, 1, 2, 1, 128, "f32", seed=5)
+    dQ, dK, dV = _gpu(inp, 1)
+    rQ, rK, rV, _, _ = _ref(inp, 1.0 / math.sqrt(128))
+    assert not rQ.any() and not rK.any()
+    s = 1.0 / math.sqrt(128)
+    f = synthetic.to_f64
+    term = np.abs(f(inp.dO)).max() * np.abs(f(inp.V)).max() * 128
+    assert np.abs(dQ.cpu().numpy()).max() <= 1e-6 * s * term * np.abs(f(inp.K)).max() * 128
+    assert np.abs(dK.cpu().numpy()).max() <= 1e-6 * s * term * np.abs(f(inp.Q)).max() * 128 * 2
+    assert normwise(dV.cpu().numpy(), rV) <= TOL_F32
+
+
+def test_fp32_given_forward_statistics_and_packed():
+    B, T, Hq, Hkv, dh = 1, 400, 4, 2, 64
+    inp = synthetic.attn_inputs(B, T, Hq, Hkv, dh, "f32", seed=12)
+    s = 1.0 / math.sqrt(dh)
+    rQ, rK, rV, rO, rL = _ref(inp, s)
+    dev = torch.device("cuda:0")
+    O = torch.from_numpy(rO).to(torch.float32).to(dev)
+    L = torch.from_numpy(rL).to(torch.float32).to(dev).contiguous()
+    dQ, dK, dV = _gpu(inp, 3, O=O, lse=L)
+    for g, r in ((dQ, rQ), (dK, rK), (dV, rV)):
+        assert normwise(g.cpu().numpy(), r) <= TOL_F32
+    cu = [0, 70, 71, 250, 400]
+    c = torch.tensor(cu, dtype=torch.int32, device=dev)
+    dQ, dK, dV = _gpu(inp, 4, cu_seqlens=c)
+    f = synthetic.to_f64
+    pQ, pK, pV = oracle.attn_bwd_packed(f(inp.Q), f(inp.K), f(inp.V), f(inp.dO), s, cu)[:3]
+    for g, r in ((dQ, pQ), (dK, pK), (dV, pV)):
+        assert normwise(g.cpu().numpy(), r) <= TOL_F32

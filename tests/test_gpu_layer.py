@@ -250,3 +250,44 @@ def test_qk_norm_full_size_T65536_prefix():
     _check(dx[:P], gr, rdx, rgr)
     for k in ("qn", "kn"):
         assert normwise(gr[k].cpu().numpy(), rgr[k]) <= TOL, k
+
+
+# ---- fp32 mode: every tensor and product fp32, normwise <= 1e-4 -----------
+TOL_F32 = 1e-4
+
+
+@pytest.mark.parametrize("T,d,Hq,Hkv,dh,F,D,theta,qk,cu", [
+    (300, 256, 4, 2, 64, 512, 3, 0.0, False, None),                    # ragged chunks, GQA
+    (257, 128, 2, 1, 128, 256, 1, 0.0, False, None),                   # one chunk, MQA, dh 128
+    (64, 64, 2, 2, 64, 128, 64, 0.0, False, None),                     # D = T
+    (400, 256, 4, 2, 128, 512, 4, 1e4, True, None),                    # rotary + QK-norm
+    (640, 256, 4, 2, 64, 512, 5, 1e4, False, [0, 1, 1, 333, 639, 640]),  # packed, rotary
+])
+def test_parity_fp32(T, d, Hq, Hkv, dh, F, D, theta, qk, cu):
+    L = synthetic.layer_inputs(T, d, Hq, Hkv, dh, F, "f32", seed=5 * T + d + D, w_std=0.05,
+                               gain_std=0.1, qk_norm=qk)
+    dx, gr = _gpu_rope(L, D, theta, cu)
+    assert dx.dtype == torch.float32
+    rdx, rgr, _ = _oracle_rope(L, theta, cu)
+    _check(dx, gr, rdx, rgr, tol=TOL_F32)
+    if qk:
+        for k in ("qn", "kn"):
+            assert normwise(gr[k].cpu().numpy(), rgr[k]) <= TOL_F32, k
+
+
+def test_fp32_accumulate_and_forward():
+    L = synthetic.layer_inputs(200, 128, 2, 1, 64, 256, "f32", seed=21, w_std=0.05, gain_std=0.1)
+    dx1, g1 = _gpu(L, 2)
+    g0 = {k: v.clone() for k, v in g1.items()}
+    _, g2 = _gpu(L, 3, grads=g1, accumulate=True)
+    for k in NAMES:
+        assert normwise(g2[k].cpu().numpy(), 2 * g0[k].cpu().numpy()) < 1e-5, k
+    dev = torch.device("cuda:0")
+    w = {k: v.to(dev) for k, v in L.w.items()}
+    y = sbp.layer_fwd(L.x.to(dev), w, L.Hq, L.Hkv, L.dh, L.eps, D=3, rope_theta=1e4)
+    torch.cuda.synchronize()
+    _, _, ry = oracle.layer_bwd(synthetic.to_f64(L.x), synthetic.to_f64(L.dy),
+                                {k: synthetic.to_f64(v) for k, v in L.w.items()}, L.Hq, L.Hkv,
+                                L.dh, L.eps, rope_theta=1e4)
+    assert y.dtype == torch.float32
+    assert normwise(y.cpu().numpy(), ry) <= TOL_F32
