@@ -150,10 +150,12 @@ def traffic_record(args):
         print(f"| `{name}` | {n} | {fk:.0f} | {wk:.0f} | {fk * fscale / gib_kib:.3f} | {wk * wscale / gib_kib:.3f} |")
 
 
-def peak_bytes(idx, T, D, D_lm=None):
+def peak_bytes(idx, T, D, D_lm=None, dw_group=None):
     """Peak device bytes of one call of workload `idx` at sequence length T
     and chunk count D: its inputs, outputs, weights, gradients and the
-    workspace the library asks for (the library allocates nothing else)."""
+    workspace the library asks for (the library allocates nothing else).
+    LM head: weight-gradient groups of `dw_group` chunks (None: the largest
+    the call uses, about 4096 tokens)."""
     import torch
     import synthetic
     import memory_efficient_exact_amd as sbp
@@ -161,7 +163,8 @@ def peak_bytes(idx, T, D, D_lm=None):
     bf = torch.bfloat16
     if c["kind"] == "lmhead":
         d, V = c["d"], c["V"]
-        ws = sbp.lmhead_ce_workspace_size(T, d, V, D, bf)
+        g = sbp.lmhead_ce_max_group(T, D) if dw_group is None else dw_group
+        ws = sbp.lmhead_ce_workspace_size(T, d, V, D, bf, g)
         return 2 * (2 * T * d) + 2 * V * d + 4 * V * d + 4 * T + ws + (4 * T if c.get("weighted") else 0)
     if c["kind"] == "layer":
         d, F, kd, qd = c["d"], c["F"], c["Hkv"] * c["dh"], c["Hq"] * c["dh"]
@@ -222,6 +225,8 @@ def parse():
     p.add_argument("--D-lm", type=int, default=None,
                    help="override the LM head's chunk count (whole-model workload)")
     p.add_argument("--T", type=int, default=None, help="override the sequence length")
+    p.add_argument("--dw-group", type=int, default=None,
+                   help="LM head: chunks per weight-gradient GEMM (default: about 4096 tokens)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
@@ -238,7 +243,57 @@ def parse():
     p.add_argument("--copy-write-csv")
     p.add_argument("--traffic-kernels", default="gemm_logits,ce_grad,gemm_dH,gemm_dW")
     p.add_argument("--traffic-sources", default="gemm")
+    p.add_argument("--sweep-D", default=None,
+                   help="LM-head workloads: comma-separated chunk counts; one JSON line per "
+                        "(D, weight-gradient group) with tokens/s and peak HBM bytes")
     return p.parse_args()
+
+
+def sweep_d(args, dev):
+    """Peak HBM bytes and tokens/s of an LM-head workload over D, for the
+    smallest workspace (one chunk per weight-gradient GEMM) and the largest
+    group the call uses (about 4096 tokens); inputs drawn once."""
+    import torch
+    import synthetic
+    import memory_efficient_exact_amd as sbp
+    cfg = dict(synthetic.WORKLOADS[args.workload])
+    if cfg["kind"] != "lmhead":
+        raise SystemExit("--sweep-D is for the LM-head workloads")
+    T = args.T or cfg["T"]
+    d, V = cfg["d"], cfg["V"]
+    inp = synthetic.workload_inputs(args.workload, T=T)
+    H, W, tg = inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev)
+    w = None if inp.weights is None else inp.weights.to(dev)
+    dW = torch.empty(V, d, dtype=torch.float32, device=dev)
+    y = inp.targets
+    for D in [int(x) for x in args.sweep_D.split(",")]:
+        rows = sum(e - s for s, e in sbp.chunk_table(T, D) if (y[s:e] >= 0).any())
+        for G in sorted({1, sbp.lmhead_ce_max_group(T, D)}):
+            ws = torch.empty(sbp.lmhead_ce_workspace_size(T, d, V, D, H.dtype, G),
+                             dtype=torch.uint8, device=dev)
+
+            def step():
+                return sbp.lmhead_ce(H, W, tg, w, D=D, dW=dW, workspace=ws)
+
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            print(json.dumps({"workload": cfg["name"], "T": T, "D": D, "T_c": T // D,
+                              "dw_group": G, "workspace_bytes": ws.numel(),
+                              "peak_hbm_bytes": torch.cuda.max_memory_allocated(dev),
+                              "ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms / 1e3), 1),
+                              "mfma_frac_step": round(6.0 * rows * V * d / (ms / 1e3) / 1e12 / 2500.0, 4)}),
+                  flush=True)
+            del ws
 
 
 def copy_calibration(dev):
@@ -320,7 +375,11 @@ def lmhead_setup(cfg, dev):
     w = None if inp.weights is None else inp.weights.to(dev)
     T, d, V, D = cfg["T"], cfg["d"], cfg["V"], cfg["D"]
     dW = torch.empty(V, d, dtype=torch.float32, device=dev)
-    ws = torch.empty(sbp.lmhead_ce_workspace_size(T, d, V, D, H.dtype), dtype=torch.uint8,
+    # weight-gradient group: the largest the call uses (about 4096 tokens)
+    # unless --dw-group asks for another
+    G = sbp.lmhead_ce_max_group(T, D) if cfg.get("dw_group") is None else cfg["dw_group"]
+    cfg["dw_group"] = G
+    ws = torch.empty(sbp.lmhead_ce_workspace_size(T, d, V, D, H.dtype, G), dtype=torch.uint8,
                      device=dev)
     red = "mean_valid"
 
@@ -593,6 +652,9 @@ def main():
     if args.library_gemm:
         library_gemm(dev)
         return
+    if args.sweep_D:
+        sweep_d(args, dev)
+        return
 
     idx = args.workload
     cfg = dict(synthetic.WORKLOADS[idx])
@@ -603,6 +665,8 @@ def main():
         cfg["D_lm"] = args.D_lm
     if args.T:
         cfg["T"] = args.T
+    if args.dw_group:
+        cfg["dw_group"] = args.dw_group
     n_valid = None
     if cfg["kind"] == "lmhead":
         step, flops, inp, n_valid = lmhead_setup(cfg, dev)

@@ -111,6 +111,17 @@ typedef enum {
 sbp_status sbp_lmhead_ce_workspace_size(int64_t T, int64_t d, int64_t V, int32_t D,
                                         int32_t dtype, size_t* bytes);
 
+/* Workspace size when the weight gradient is taken once per group of G
+ * consecutive chunks (G >= 1; dW += dZ_g^T H_g over the group's tokens).
+ * The call uses the largest G whose workspace fits in ws_bytes, up to a
+ * group of about 4096 tokens (G <= max(1, 4096 / (T_c rounded up to 128)));
+ * sbp_lmhead_ce_workspace_size is this size for G = 1, the smallest
+ * workspace, which falls with D.  A larger G holds G chunks of dZ (G T_c V
+ * bf16) and makes the weight-gradient GEMM longer in K, so its fp32
+ * read-modify-write of dW is paid once per group. */
+sbp_status sbp_lmhead_ce_workspace_size_grouped(int64_t T, int64_t d, int64_t V, int32_t D,
+                                                int32_t dtype, int32_t G, size_t* bytes);
+
 sbp_status sbp_lmhead_ce_fwd_bwd(const void* H, const void* W, const int32_t* targets,
                                  const float* weights, int64_t T, int64_t d, int64_t V,
                                  int32_t D, int32_t dtype, int32_t reduction,

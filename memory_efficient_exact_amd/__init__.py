@@ -69,21 +69,33 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 # ----------------------------------------------------------------------------
-def lmhead_ce_workspace_size(T, d, V, D, dtype=torch.bfloat16) -> int:
+def lmhead_ce_workspace_size(T, d, V, D, dtype=torch.bfloat16, dw_group: int = 1) -> int:
+    """Workspace bytes of ``lmhead_ce`` when the weight gradient is taken once
+    per ``dw_group`` chunks (1: the smallest workspace)."""
     out = C.c_size_t(0)
-    check(load().sbp_lmhead_ce_workspace_size(T, d, V, D, _DT[dtype], C.byref(out)))
+    check(load().sbp_lmhead_ce_workspace_size_grouped(T, d, V, D, _DT[dtype], int(dw_group),
+                                                      C.byref(out)))
     return out.value
+
+
+def lmhead_ce_max_group(T, D) -> int:
+    """The largest weight-gradient group the call uses: about 4096 tokens."""
+    tcp = -(-(T - (D - 1) * (T // D)) // 128) * 128
+    return max(1, min(D, 4096 // tcp))
 
 
 def lmhead_ce(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
               weights: Optional[torch.Tensor] = None, D: int = 1,
               reduction: str = "mean_valid", dW: Optional[torch.Tensor] = None,
               accumulate: bool = False, token_loss: bool = False,
-              workspace: Optional[torch.Tensor] = None):
+              workspace: Optional[torch.Tensor] = None, dw_group: int = 1):
     """Chunked LM head + cross-entropy.  Returns ``(loss, dH, dW, token_loss)``.
 
     ``loss`` is a 1-element fp32 tensor; ``token_loss`` is None unless asked.
     ``dW`` may be passed in (fp32 [V, d]) to accumulate into it.
+    ``dw_group``: chunks per weight-gradient GEMM the allocated workspace is
+    sized for (1: least memory; the call uses the largest group a given
+    ``workspace`` holds, up to about 4096 tokens).
     """
     lib = load()
     _dev(H, W, targets, weights, dW)
@@ -102,7 +114,7 @@ def lmhead_ce(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     elif dW.shape != (V, d) or dW.dtype != torch.float32:
         raise ValueError("dW must be fp32 [V, d]")
     tl = torch.empty(T, dtype=torch.float32, device=dev) if token_loss else None
-    nb = lmhead_ce_workspace_size(T, d, V, D, H.dtype)
+    nb = lmhead_ce_workspace_size(T, d, V, D, H.dtype, dw_group)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _ws(nb, dev)
     check(lib.sbp_lmhead_ce_fwd_bwd(_ptr(H), _ptr(W), _ptr(targets), _ptr(weights), T, d, V, D,
                                     dt, _RED[reduction], int(accumulate), _ptr(loss), _ptr(tl),

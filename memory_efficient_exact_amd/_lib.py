@@ -41,6 +41,7 @@ SIGNATURES = {
     "sbp_lmhead_ce_workspace_size": (i32, [i64, i64, i64, i32, i32, C.POINTER(sz)]),
     "sbp_lmhead_ce_fwd_bwd": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, sz, vp]),
+    "sbp_lmhead_ce_workspace_size_grouped": (i32, [i64, i64, i64, i32, i32, i32, C.POINTER(sz)]),
     "sbp_lmhead_logprob_workspace_size": (i32, [i64, i64, i64, i32, i32, C.POINTER(sz)]),
     "sbp_lmhead_logprob_fwd": (i32, [vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp, sz, vp]),
     "sbp_attn_bwd_workspace_size": (i32, [i64, i64, i32, i32, i32, i32, i32, C.POINTER(sz)]),

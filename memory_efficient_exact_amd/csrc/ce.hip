@@ -325,14 +325,16 @@ __device__ __forceinline__ void store8<float>(float* p, const float* v) {
 // Tile: 64 rows (tokens of the chunk) x 128 columns (vocab).  With TR the
 // tile is also written transposed (dZt, vocab-major).
 // REL16: Z holds fp16 values relative to the max of their 64-column group
-// (parts[r][v / 64].x), the logits GEMM's EPI_REL16_LSE output.
+// (parts[r][v / 64].x), the logits GEMM's EPI_REL16_LSE output; dZ may then
+// be Z itself (ldg == ldz): every thread writes exactly the 8 elements it
+// read, after reading them.
 template <typename OutT, bool TR, bool REL16>
 __global__ __launch_bounds__(256) void ce_grad_kernel(
-    const void* __restrict__ Zv, const float2* __restrict__ parts, int64_t ldp, int64_t ldz,
+    const void* Zv, const float2* __restrict__ parts, int64_t ldp, int64_t ldz,
     const int32_t* __restrict__ targets,
     const float* __restrict__ weights, const float* __restrict__ inv_norm,
     const float* __restrict__ lse, int64_t s0, int64_t Tc, int64_t V, int64_t Vp,
-    OutT* __restrict__ dZ, int64_t ldg, OutT* __restrict__ dZt, int64_t ldgt, int64_t Tcp,
+    OutT* dZ, int64_t ldg, OutT* __restrict__ dZt, int64_t ldgt, int64_t Tcp,
     const int* __restrict__ active) {
   if (active && *active == 0) return;
   __shared__ float tile[TR ? 64 : 1][129];

@@ -89,7 +89,7 @@ sbp_status ce_stats(const float* Z, int64_t ldz, const int32_t* targets, const f
 // one chunk; zero pads (columns V .. Vp of dZ, columns Tc .. Tcp of dZ^T).
 // Z: fp32 logits [Tc, ldz], or, when parts is not NULL, the fp16 relative
 // logits of EPI_REL16_LSE with their group maxima in parts [Tc, ldp] (bf16
-// output without dZ^T only).
+// output without dZ^T only; dZ may then be Z, ldg == ldz: in place).
 sbp_status ce_grad(int dtype, const void* Z, const float2* parts, int64_t ldp, int64_t ldz,
                    const int32_t* targets, const float* weights, const float* inv_norm,
                    const float* lse, int64_t s, int64_t Tc, int64_t V, int64_t Vp, void* dZ,

@@ -18,9 +18,17 @@
 // W^T is formed once per call (dH contracts over W's rows).  bf16: the dW
 // GEMM reads dZ_g and H_g ([tokens, .], contracted over tokens) K-major, in
 // place: dZ_c is written into a group buffer whose rows are the group's
-// tokens in order, and H_g is a row range of H.  fp32 (NT GEMMs only):
-// dZ_c^T and H_c^T side by side in K per group (slots of T_c rounded up to
-// the K granule).  Workspace O(G T_c V + V d).
+// tokens in order, and H_g is a row range of H.  With fused statistics the
+// logits GEMM writes the chunk's fp16 relative logits into the chunk's rows
+// of that buffer and ce_grad turns them into dZ_c in place (same element
+// size and layout), so no separate logits buffer exists.  fp32 (NT GEMMs
+// only): dZ_c^T and H_c^T side by side in K per group (slots of T_c rounded
+// up to the K granule).  Workspace O(G T_c V + V d).
+//
+// G, the chunks per dW GEMM, is the largest the caller's workspace holds, up
+// to a group of about 4096 tokens: sbp_lmhead_ce_workspace_size gives the
+// smallest workspace (G = 1, peak memory falling with D), and
+// sbp_lmhead_ce_workspace_size_grouped the one for a given G.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +36,8 @@ namespace sbp {
 namespace {
 
 struct LmWs {
-  void* Z;    // fp16 relative logits [T_c, Vp] (fused statistics) or fp32 logits
+  void* Z;    // fp32 logits [T_c, Vp] (no fused statistics); with them, NULL:
+              // each chunk's fp16 relative logits sit in its rows of dZ
   float* ztgt;  // fused statistics: each row's target logit, fp32 [T_c]
   void* dZ;   // bf16: the group buffer [G T_c, Vp]; fp32: [T_c, Vp]
   void* dZt;  // fp32 only
@@ -50,12 +59,14 @@ struct LmShape {
   bool fused_stats;  // the logits GEMM writes the row statistics partials
   int nparts;
   int G;  // chunks per dW GEMM
+  int Gmax;  // largest group used: about 4096 tokens
   int64_t Kg;  // fp32: K extent of the dW group buffers, G * Tcp
   bool kmajor;  // bf16: GEMM operands read K-major in place
+  bool inplace;  // the fused logits live in the dZ group buffer
   size_t esz;
 };
 
-LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
+LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype, int G) {
   LmShape s;
   s.T = T; s.d = d; s.V = V; s.D = D; s.dtype = dtype;
   s.esz = dtype == SBP_BF16 ? 2 : 4;
@@ -72,13 +83,15 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype) {
   S = std::max<int64_t>(1, std::min<int64_t>(S, 16));
   S = std::min<int64_t>(S, std::max<int64_t>(1, s.Vp / 512));
   s.S = (int)S;
-  // dW group: about 4096 tokens of K per weight-gradient GEMM (its fp32
-  // read-modify-write of the V x d gradient then costs a quarter byte per
-  // flop or less); a function of the shape only.
-  s.G = (int)std::max<int64_t>(1, std::min<int64_t>(D, 4096 / s.Tcp));
+  // dW group: up to about 4096 tokens of K per weight-gradient GEMM (its
+  // fp32 read-modify-write of the V x d gradient then costs a quarter byte
+  // per flop or less); G itself is chosen from the workspace (lm_group).
+  s.Gmax = (int)std::max<int64_t>(1, std::min<int64_t>(D, 4096 / s.Tcp));
+  s.G = std::max(1, std::min(G, s.Gmax));
   s.Kg = s.G * s.Tcp;
   s.kmajor = dtype == SBP_BF16;
   s.fused_stats = dtype == SBP_BF16 && d % 128 == 0;
+  s.inplace = s.fused_stats && s.kmajor;
   s.nparts = (int)(4 * cdiv(V, 256));
   return s;
 }
@@ -87,7 +100,7 @@ size_t lm_plan(const LmShape& s, char* base, LmWs* w) {
   WsPlan P;
   P.base = base;
   LmWs x;
-  x.Z = P.take((s.fused_stats ? 2 : sizeof(float)) * s.Tcm * s.Vp);
+  x.Z = s.inplace ? nullptr : P.take((s.fused_stats ? 2 : sizeof(float)) * s.Tcm * s.Vp);
   x.Wt = P.take(s.esz * s.d * s.Vp);
   if (s.kmajor) {
     x.dZ = P.take(s.esz * s.G * s.Tcm * s.Vp);
@@ -141,6 +154,15 @@ size_t lp_plan(const LmShape& s, char* base, LpWs* w) {
 
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// The largest dW group (<= Gmax) whose workspace fits in ws_bytes; 0 if
+// not even G = 1 fits.
+int lm_group(int64_t T, int64_t d, int64_t V, int32_t D, int dtype, size_t ws_bytes) {
+  const int gmax = lm_shape(T, d, V, D, dtype, 1).Gmax;
+  for (int g = gmax; g >= 1; --g)
+    if (lm_plan(lm_shape(T, d, V, D, dtype, g), nullptr, nullptr) <= ws_bytes) return g;
+  return 0;
+}
+
 sbp_status lm_check_sizes(int64_t T, int64_t d, int64_t V, int32_t D, int32_t dtype) {
   if (dtype != SBP_F32 && dtype != SBP_BF16) return set_error(SBP_ERR_INVALID_ARG, "dtype %d is not SBP_F32 or SBP_BF16", dtype);
   if (T < 1 || d < 1 || V < 1) return set_error(SBP_ERR_INVALID_ARG, "T, d, V must be >= 1 (got %lld, %lld, %lld)", (long long)T, (long long)d, (long long)V);
@@ -162,7 +184,19 @@ extern "C" sbp_status sbp_lmhead_ce_workspace_size(int64_t T, int64_t d, int64_t
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = lm_check_sizes(T, d, V, D, dtype);
   if (st != SBP_OK) return st;
-  *bytes = lm_plan(lm_shape(T, d, V, D, dtype), nullptr, nullptr);
+  *bytes = lm_plan(lm_shape(T, d, V, D, dtype, 1), nullptr, nullptr);
+  return SBP_OK;
+}
+
+extern "C" sbp_status sbp_lmhead_ce_workspace_size_grouped(int64_t T, int64_t d, int64_t V,
+                                                           int32_t D, int32_t dtype, int32_t G,
+                                                           size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
+  sbp_status st = lm_check_sizes(T, d, V, D, dtype);
+  if (st != SBP_OK) return st;
+  if (G < 1) return set_error(SBP_ERR_INVALID_ARG, "G must be >= 1 (got %d)", G);
+  *bytes = lm_plan(lm_shape(T, d, V, D, dtype, G), nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -181,10 +215,12 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
   if (misaligned(H) || misaligned(W) || misaligned(targets) || misaligned(loss) || misaligned(dH) ||
       misaligned(dW) || misaligned(weights) || misaligned(token_loss) || misaligned(ws))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  const LmShape s = lm_shape(T, d, V, D, dtype);
-  const size_t need = lm_plan(s, nullptr, nullptr);
-  if (!ws || ws_bytes < need)
+  const int G = ws ? lm_group(T, d, V, D, dtype, ws_bytes) : 0;
+  if (G == 0) {
+    const size_t need = lm_plan(lm_shape(T, d, V, D, dtype, 1), nullptr, nullptr);
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  }
+  const LmShape s = lm_shape(T, d, V, D, dtype, G);
   LmWs w;
   lm_plan(s, (char*)ws, &w);
   hipStream_t str = (hipStream_t)stream;
@@ -217,10 +253,13 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
     const int* slot_act = s.G == 1 ? act : nullptr;
     char* dZc = (char*)w.dZ + (s.kmajor ? (s0 - s_group) * s.Vp * s.esz : 0);
 
+    // the chunk's logits: in its own rows of the dZ group buffer when the
+    // statistics are fused (turned into dZ_c in place by ce_grad)
+    void* Zc = s.inplace ? (void*)dZc : w.Z;
     GemmParams g1;
     g1.A = Hb + s0 * d * s.esz; g1.lda = d;
     g1.B = W; g1.ldb = d;
-    g1.C = w.Z; g1.ldc = s.Vp;
+    g1.C = Zc; g1.ldc = s.Vp;
     g1.M = (int)Tc; g1.N = (int)V; g1.K = (int)d;
     g1.active = act;
     g1.m_fastest = 1;
@@ -238,7 +277,7 @@ static sbp_status lmhead_ce_impl(const void* H, const void* W, const int32_t* ta
                        token_loss, str));
     }
     if (s.kmajor) {
-      SBP_TRY(ce_grad(dtype, w.Z, s.fused_stats ? w.parts : nullptr, s.nparts, s.Vp, targets,
+      SBP_TRY(ce_grad(dtype, Zc, s.fused_stats ? w.parts : nullptr, s.nparts, s.Vp, targets,
                       weights, w.prep.inv_norm, w.lse, s0, Tc, V, s.Vp, dZc, s.Vp, nullptr, 0, 0,
                       slot_act, str));
     } else {
@@ -296,7 +335,7 @@ extern "C" sbp_status sbp_lmhead_logprob_workspace_size(int64_t T, int64_t d, in
   if (!bytes) return set_error(SBP_ERR_INVALID_ARG, "bytes is NULL");
   sbp_status st = lm_check_sizes(T, d, V, D, dtype);
   if (st != SBP_OK) return st;
-  *bytes = lp_plan(lm_shape(T, d, V, D, dtype), nullptr, nullptr);
+  *bytes = lp_plan(lm_shape(T, d, V, D, dtype, 1), nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -316,7 +355,7 @@ static sbp_status lmhead_logprob_impl(const void* H, const void* W, const int32_
   if (misaligned(H) || misaligned(W) || misaligned(targets) || misaligned(logprob) || misaligned(lse) ||
       misaligned(ws))
     return set_error(SBP_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  const LmShape s = lm_shape(T, d, V, D, dtype);
+  const LmShape s = lm_shape(T, d, V, D, dtype, 1);
   const size_t need = lp_plan(s, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);

@@ -53,7 +53,27 @@ def test_lmhead_workspace_is_chunk_sized():
     assert st1 == st16 == 0
     full_logits_fp32 = 32768 * 128256 * 4
     assert w16 < full_logits_fp32 / 4
-    assert w1 > full_logits_fp32
+    assert w1 > full_logits_fp32 / 2   # unchunked: the whole [T, V] dZ (bf16)
+
+
+@pytest.mark.parametrize("T,d,V", [(32768, 4096, 128256), (131072, 3584, 152064)])
+def test_lmhead_workspace_falls_with_D_and_grows_with_the_group(T, d, V):
+    # the smallest workspace (one chunk per weight-gradient GEMM) falls
+    # strictly as D grows; a group of G chunks holds G chunks of dZ
+    lib = sbp.load()
+    sizes = [_ws(lib.sbp_lmhead_ce_workspace_size, T, d, V, D, 1)[1] for D in (1, 2, 4, 8, 16, 32, 64, 128, 256)]
+    assert all(b < a for a, b in zip(sizes, sizes[1:])), sizes
+    for D in (16, 64, 256):
+        g1 = _ws(lib.sbp_lmhead_ce_workspace_size, T, d, V, D, 1)[1]
+        gmax = sbp.lmhead_ce_max_group(T, D)
+        gr = [_ws(lib.sbp_lmhead_ce_workspace_size_grouped, T, d, V, D, 1, G)[1]
+              for G in range(1, gmax + 3)]
+        assert gr[0] == g1
+        assert all(b - a > 0.99 * (T // D) * V * 2 for a, b in zip(gr[:gmax], gr[1:gmax]))
+        assert gr[gmax - 1] == gr[gmax] == gr[gmax + 1]  # groups stop at ~4096 tokens
+        assert gmax * -(-(T // D) // 128) * 128 <= max(4096, -(-(T // D) // 128) * 128)
+    st, _ = _ws(lib.sbp_lmhead_ce_workspace_size_grouped, T, d, V, 16, 1, 0)
+    assert st == _lib.SBP_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("T,d,V,D,dt,code", [

@@ -20,12 +20,13 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def _run(inp, D, reduction="mean_valid", accumulate=False, dW=None):
+def _run(inp, D, reduction="mean_valid", accumulate=False, dW=None, dw_group=1):
     dev = torch.device("cuda:0")
     H, W, tg = inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev)
     w = None if inp.weights is None else inp.weights.to(dev)
     loss, dH, dWo, tl = sbp.lmhead_ce(H, W, tg, w, D=D, reduction=reduction,
-                                      accumulate=accumulate, dW=dW, token_loss=True)
+                                      accumulate=accumulate, dW=dW, token_loss=True,
+                                      dw_group=dw_group)
     torch.cuda.synchronize()
     return loss, dH, dWo, tl
 
@@ -97,11 +98,36 @@ def test_weight_gradient_groups_first_group_inactive():
     L, rH, rW, _, _ = oracle.lmhead_ce(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
                                        inp.targets.numpy())
     dW0 = torch.full((512, 64), 7.0, device="cuda:0")
-    loss, dH, dW, _ = _run(inp, 16, dW=dW0)
+    loss, dH, dW, _ = _run(inp, 16, dW=dW0, dw_group=4)
     assert abs(loss.item() - L) / abs(L) <= TOL["bf16"]
     assert normwise(dH.float().cpu().numpy(), rH) <= TOL["bf16"]
     assert normwise(dW.cpu().numpy(), rW) <= TOL["bf16"]
     assert (dH[:4096] == 0).all()
+
+
+@pytest.mark.parametrize("d", [256, 136])
+def test_weight_gradient_group_chosen_by_the_workspace(d):
+    # groups of 1, 2 and 4 chunks (T_c = 1024) and a workspace larger than
+    # any group needs: the same gradients (d = 256: the chunk's logits sit in
+    # the dZ group buffer and become dZ in place; d = 136: fp32 logits)
+    inp = synthetic.lmhead_inputs(4096, d, 3000, "bf16", seed=13, w_std=0.05, ignore_frac=0.1)
+    L, rH, rW, _, _ = oracle.lmhead_ce(synthetic.to_f64(inp.H), synthetic.to_f64(inp.W),
+                                       inp.targets.numpy())
+    outs = [_run(inp, 4, dw_group=g) for g in (1, 2, 4)]
+    dev = torch.device("cuda:0")
+    big = torch.empty(sbp.lmhead_ce_workspace_size(4096, d, 3000, 4, torch.bfloat16, 4) + 12345,
+                      dtype=torch.uint8, device=dev)
+    outs.append(sbp.lmhead_ce(inp.H.to(dev), inp.W.to(dev), inp.targets.to(dev), D=4,
+                              workspace=big, token_loss=True))
+    torch.cuda.synchronize()
+    for loss, dH, dW, _ in outs:
+        assert abs(loss.item() - L) / abs(L) <= TOL["bf16"]
+        assert normwise(dH.float().cpu().numpy(), rH) <= TOL["bf16"]
+        assert normwise(dW.cpu().numpy(), rW) <= TOL["bf16"]
+    # the group changes only the summation order of dW
+    for o in outs[1:]:
+        assert normwise(o[2].cpu().numpy(), outs[0][2].cpu().numpy()) <= 1e-5
+        assert torch.equal(o[1], outs[0][1])
 
 
 def test_sum_reduction():
@@ -160,7 +186,8 @@ def _check_dW_rows(inp, dW, vrows, tol=2e-2):
 def _full_size(index, rows, vrows=None, inp=None):
     cfg = synthetic.WORKLOADS[index]
     inp = synthetic.workload_inputs(index) if inp is None else inp
-    loss, dH, dW, tl = _run(inp, cfg["D"])
+    # the launch configuration the benchmark times: groups of ~4096 tokens
+    loss, dH, dW, tl = _run(inp, cfg["D"], dw_group=sbp.lmhead_ce_max_group(cfg["T"], cfg["D"]))
     y = inp.targets.numpy()
     N = int((y >= 0).sum())
     rows = np.asarray(rows)
