@@ -132,10 +132,12 @@ template <int DH>
 struct LdsOff {
   static constexpr int KS = DH / 16, NB = DH / 32, ROWB = DH * 2;
   int row[KS], tr[NB][2];
-  __device__ __forceinline__ explicit LdsOff(int lane) {
+  // rbase (a multiple of 16, wave-uniform): a row offset folded into the
+  // lane offsets, so that reads of a wave's fixed rows need no address add
+  __device__ __forceinline__ explicit LdsOff(int lane, int rbase = 0) {
     const int g = lane >> 5, r = lane & 31, f = swz<DH>(r);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) row[ks] = r * ROWB + 16 * ((2 * ks + g) ^ f);
+    for (int ks = 0; ks < KS; ++ks) row[ks] = (rbase + r) * ROWB + 16 * ((2 * ks + g) ^ f);
     const int G = (lane >> 4) & 3, j = lane & 15;
     const int rr = 4 * (G >> 1) + (j >> 2), colc = 2 * (G & 1) + ((j & 3) >> 1);
 #pragma unroll
@@ -143,7 +145,7 @@ struct LdsOff {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rw = rr + 8 * h;
-        tr[nb][h] = rw * ROWB + 16 * ((4 * nb + colc) ^ swz<DH>(rw)) + 8 * (j & 1);
+        tr[nb][h] = (rbase + rw) * ROWB + 16 * ((4 * nb + colc) ^ swz<DH>(rw)) + 8 * (j & 1);
       }
   }
   // 16-byte row read: row rbase + l%32, columns 16 ks + 8 (l/32) .. + 8
@@ -457,37 +459,12 @@ __device__ __forceinline__ void dma_tile64_w8(char* lds, const bf16_t* __restric
   }
 }
 
-// One wave's share of a 64-query tile: its 32 queries (tile rows qrow ..
-// qrow + 31) against its 32 keys (K / V tile rows krow .. krow + 31).
-template <int DH>
-__device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int krow,
-                                          const char* qt, const char* ot, const float* ls,
-                                          const float* dl, int qrow, int q0, int kcol, int qlim, int lane,
-                                          float c2, bool mask, f32x16_t (&dk)[DH / 32],
-                                          f32x16_t (&dv)[DH / 32]) {
-  constexpr int NB = DH / 32, KS = DH / 16;
-  // S = Q K^T and dP = dO V^T: [32 queries x 32 keys], fragments one step ahead
-  f32x16_t sp = f32x16_t{}, dp = f32x16_t{};
-  {
-    uint4 fq[2], fk[2], fo[2], fv[2];
-    auto ld = [&](int ks) {
-      fq[ks & 1] = lo.row_frag(qt, qrow, ks);
-      fk[ks & 1] = lo.row_frag(kt, krow, ks);
-      fo[ks & 1] = lo.row_frag(ot, qrow, ks);
-      fv[ks & 1] = lo.row_frag(vt, krow, ks);
-    };
-    ld(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) ld(ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      sp = mma(fq[ks & 1], fk[ks & 1], sp);
-      dp = mma(fo[ks & 1], fv[ks & 1], dp);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // P = exp(s S - LSE), dS = P (dP - Delta); elements 4j..4j+3 are rows
-  // 8j + 4(l/32) + 0..3 of the wave's 32 queries
+// Softmax step of a dK/dV tile: P = exp(s S - LSE), dS = P (dP - Delta) in
+// place; elements 4j..4j+3 are rows 8j + 4(l/32) + 0..3 of the wave's 32
+// queries.  MASK zeroes the pairs a query does not see.
+template <bool MASK>
+__device__ __forceinline__ void dkdv_softmax(f32x16_t& sp, f32x16_t& dp, const float* ls, const float* dl,
+                                             int qrow, int q0, int kcol, int qlim, int lane, float c2) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r0 = qrow + 8 * j + 4 * (lane >> 5);
@@ -499,8 +476,7 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, 
       const int e_ = 4 * j + i;
       float p = __builtin_amdgcn_exp2f(sp[e_] * c2 - lv[i]);
       float g = p * (dp[e_] - dv_[i]);
-      if (mask) {  // wave-uniform: a scalar branch
-        asm volatile("" : "+v"(p), "+v"(g));  // keep both unconditional (no branches)
+      if constexpr (MASK) {
         // statistics rows past the chunk are padding (any value): select, do
         // not multiply, so that they cannot leak in.  qlim: the end of the
         // chunk or of the key's sequence, whichever comes first
@@ -513,13 +489,52 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lo, const char* kt, 
       dp[e_] = g;
     }
   }
+}
+
+// One wave's share of a 64-query tile: its 32 queries (tile rows qrow ..
+// qrow + 31) against its 32 keys (K / V tile rows krow .. krow + 31).  The
+// matrix phases are shared by masked and unmasked tiles; the softmax between
+// them is one straight-line block of either kind (one wave-uniform branch).
+// lq / lk: fragment offsets with the wave's query rows (qrow) and key rows
+// folded in.
+template <int DH>
+__device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lq, const LdsOff<DH>& lk, const char* kt,
+                                          const char* vt, const char* qt, const char* ot, const float* ls,
+                                          const float* dl, int qrow, int q0, int kcol, int qlim, int lane,
+                                          float c2, bool mask, f32x16_t (&dk)[DH / 32],
+                                          f32x16_t (&dv)[DH / 32]) {
+  constexpr int NB = DH / 32, KS = DH / 16;
+  // S = Q K^T and dP = dO V^T: [32 queries x 32 keys], fragments one step ahead
+  f32x16_t sp = f32x16_t{}, dp = f32x16_t{};
+  {
+    uint4 fq[2], fk[2], fo[2], fv[2];
+    auto ld = [&](int ks) {
+      fq[ks & 1] = lq.row_frag(qt, 0, ks);
+      fk[ks & 1] = lk.row_frag(kt, 0, ks);
+      fo[ks & 1] = lq.row_frag(ot, 0, ks);
+      fv[ks & 1] = lk.row_frag(vt, 0, ks);
+    };
+    ld(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) ld(ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      sp = mma(fq[ks & 1], fk[ks & 1], sp);
+      dp = mma(fo[ks & 1], fv[ks & 1], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (mask)  // wave-uniform
+    dkdv_softmax<true>(sp, dp, ls, dl, qrow, q0, kcol, qlim, lane, c2);
+  else
+    dkdv_softmax<false>(sp, dp, ls, dl, qrow, q0, kcol, qlim, lane, c2);
   // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
   {
     uint4 tq[2], to[2];
     auto ld = [&](int st) {
-      const int r = qrow + (st / NB) * 16, nb = st % NB;
-      to[st & 1] = lo.tr_frag(ot, r, nb);
-      tq[st & 1] = lo.tr_frag(qt, r, nb);
+      const int r = (st / NB) * 16, nb = st % NB;
+      to[st & 1] = lq.tr_frag(ot, r, nb);
+      tq[st & 1] = lq.tr_frag(qt, r, nb);
     };
     ld(0);
     uint4 pa, da;
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
   const int kg = wave & 3, qh = wave >> 2;
   const KBlock kbk = k_block(a.Hkv);
   const int kv = kbk.kv, b = blockIdx.z;
-  const LdsOff<DH> lo(lane);
+  const LdsOff<DH> lq(lane, (wave >> 2) * 32), lk(lane, (wave & 3) * 32);
   const int kbase = kbk.kblk * 128;
   const int kw = kbase + kg * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
@@ -588,10 +603,26 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
   dma_tile64_w8<DH>(Vt + TB, Vb + 64 * ldk, ldk, kvalid - 64, wave, lane);
   // each wave: 2 x (64 rows of Q and dO) / 8 waves, plus one quarter row of
   // LSE (waves 0-3) or Delta (waves 4-7)
-  auto issue = [&](char* qd, char* od, float* ld_, float* dd, int it) {
-    const int hh = it / nqt;
-    const int q0 = a.s + (j0 + it % nqt) * 64;
-    const int h = kv * a.G + hh;
+  // Iteration it = hh nqt + jq: q head kv G + hh, query tile s + 64 (j0 +
+  // jq).  Two cursors walk it without divisions: the next tile to fetch
+  // (which stays on the last tile once there, so the trailing fetch repeats
+  // it into a buffer nobody reads) and the next tile to compute.
+  struct Cur {
+    int hh, jq;
+  };
+  auto advance = [&](Cur& c) {
+    if (++c.jq == nqt) {
+      c.jq = 0;
+      ++c.hh;
+    }
+  };
+  Cur ci{0, 0}, ct{0, 0};
+  int fetched = 0;  // tiles whose fetch has been issued
+  auto issue = [&](char* qd, char* od, float* ld_, float* dd) {
+    if (fetched > 0 && fetched < n) advance(ci);
+    ++fetched;
+    const int q0 = a.s + (j0 + ci.jq) * 64;
+    const int h = kv * a.G + ci.hh;
     const int64_t qo = (int64_t)b * a.q_bs + (int64_t)(q0 - a.qoff) * ldq + (int64_t)h * DH;
     dma_tile64_w8<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
     dma_tile64_w8<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
@@ -600,24 +631,24 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
     else
       dma_f32x16(dd, a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (q0 - a.s), wave - 4, lane);
   };
-  auto qstart = [&](int it) { return a.s + (j0 + it % nqt) * 64; };
-  auto tile = [&](const char* qt, const char* ot, const float* ls, const float* dl, int it) {
-    const int q0 = qstart(it), qw = q0 + qrow;
+  auto tile = [&](const char* qt, const char* ot, const float* ls, const float* dl) {
+    const int q0 = a.s + (j0 + ct.jq) * 64, qw = q0 + qrow;
+    advance(ct);
     // only the wave's queries at or after its keys and before the last
     // key's limit; those wholly after the keys and before every key's limit
     // need no mask
     if (qw + 31 >= kw && qw < wq_hi)
-      dkdv_tile<DH>(lo, Kt, Vt, kg * 32, qt, ot, ls, dl, qrow, q0, kcol, qlim, lane, c2,
+      dkdv_tile<DH>(lq, lk, Kt, Vt, qt, ot, ls, dl, qrow, q0, kcol, qlim, lane, c2,
                     !(qw >= kw + 31 && qw + 32 <= wq_lo), dk, dv);
   };
-  if (n > 0) issue(Q0, O0, L0, E0, 0);
+  if (n > 0) issue(Q0, O0, L0, E0);
   for (int it = 0; it < n; it += 2) {
     dma_barrier();  // tile it (and K, V) landed; everyone is done with the other buffers
-    issue(Q1, O1, L1, E1, min(it + 1, n - 1));
-    tile(Q0, O0, L0, E0, it);
+    issue(Q1, O1, L1, E1);  // tile it + 1 (or the last again)
+    tile(Q0, O0, L0, E0);
     dma_barrier();
-    issue(Q0, O0, L0, E0, min(it + 2, n - 1));
-    if (it + 1 < n) tile(Q1, O1, L1, E1, it + 1);
+    issue(Q0, O0, L0, E0);  // tile it + 2 (or the last again)
+    if (it + 1 < n) tile(Q1, O1, L1, E1);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target LDS
   __syncthreads();                // every wave is done with K, V
