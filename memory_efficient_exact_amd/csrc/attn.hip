@@ -703,12 +703,14 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
 // dQ.  Block: 4 waves, 128 queries (32 per wave), one q head; key tiles of
 // 64 up to the diagonal, double-buffered by DMA like the forward.
 // ---------------------------------------------------------------------------
-// Sum of the 8 bf16 values of an operand fragment (exact in fp32 pairs).
-__device__ __forceinline__ float frag_sum(const uint4& u) {
+// s + the sum of the 8 bf16 values of an operand fragment: four bf16 dot
+// products with (1, 1), each adding a word's two values (exact products,
+// fp32 accumulation).
+__device__ __forceinline__ float frag_sum(const uint4& u, float s) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  float s = 0.f;
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) s += __uint_as_float(w[k] << 16) + __uint_as_float(w[k] & 0xffff0000u);
+  for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), one, s, false);
   return s;
 }
 
@@ -743,7 +745,7 @@ __device__ __forceinline__ void dq_tile(const LdsOff<DH>& lo, const char* kt, co
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint4 da = pack_frag(dpt[kb], i);
-      rs += frag_sum(da);
+      rs = frag_sum(da, rs);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         dq[nb] = mma(da, lo.tr_frag(kt, kb * 32 + 16 * i, nb), dq[nb]);
