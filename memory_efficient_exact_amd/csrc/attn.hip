@@ -99,6 +99,34 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The DMA of dma_tile64 for tiles whose 64 rows all exist, from per-lane byte
+// offsets formed once (dma64_offsets): only the wave-uniform tile base
+// changes from tile to tile, so each DMA is a scalar base plus a fixed
+// 32-bit lane offset (64 rows of a pitch below 2^25 elements).
+template <int DH, int NW>
+struct Dma64Off {
+  static constexpr int ROWB = DH * 2, RPI = 1024 / ROWB, NI = 64 / RPI, PER = NI / NW;
+  uint32_t off[PER];
+  __device__ __forceinline__ Dma64Off(int64_t ld, int wave, int lane) {
+    constexpr int CPR = DH / 8;
+    const int rr = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int r = (wave + NW * j) * RPI + rr;
+      off[j] = (uint32_t)((int64_t)r * ld + 8 * (pc ^ swz<DH>(r))) * 2u;
+    }
+  }
+};
+template <int DH, int NW>
+__device__ __forceinline__ void dma_tile64_full(char* lds, const bf16_t* __restrict__ src, const Dma64Off<DH, NW>& o,
+                                                int wave) {
+  const char* base = reinterpret_cast<const char*>(src);
+#pragma unroll
+  for (int j = 0; j < Dma64Off<DH, NW>::PER; ++j)
+    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(base + o.off[j]),
+                                     (SBP_LDS void*)(lds + (wave + NW * j) * 1024), 16, 0, 0);
+}
+
 // Block -> work mapping for the 8 XCDs.  Workgroups are dispatched
 // round-robin over the XCDs in linear order (x fastest), so the kv head is
 // taken from the low part of the linear id: when Hkv divides 8 every block
@@ -339,10 +367,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const SeqRange sr = seq_range(a, q0, qw, qcol);
   const int kend = min(q0 + 128, a.e);
   const int ntiles = (kend + 63) / 64, t0 = sr.kfirst / 64;
+  const Dma64Off<DH, 4> kvoff(ldk, wave, lane);
   auto issue = [&](char* kd, char* vd, int t) {
     const int k0 = t * 64;
-    dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
-    dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+    if (kend - k0 >= 64) {  // wave-uniform
+      dma_tile64_full<DH, 4>(kd, Kb + (int64_t)k0 * ldk, kvoff, wave);
+      dma_tile64_full<DH, 4>(vd, Vb + (int64_t)k0 * ldk, kvoff, wave);
+    } else {
+      dma_tile64<DH>(kd, Kb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+      dma_tile64<DH>(vd, Vb + (int64_t)k0 * ldk, ldk, kend - k0, wave, lane);
+    }
   };
   issue(K0, V0, t0);
   for (int t = t0; t < ntiles; t += 2) {
@@ -617,6 +651,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
     }
   };
   Cur ci{0, 0}, ct{0, 0};
+  const Dma64Off<DH, 8> qoff(ldq, wave, lane);
   int fetched = 0;  // tiles whose fetch has been issued
   auto issue = [&](char* qd, char* od, float* ld_, float* dd) {
     if (fetched > 0 && fetched < n) advance(ci);
@@ -624,8 +659,13 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
     const int q0 = a.s + (j0 + ci.jq) * 64;
     const int h = kv * a.G + ci.hh;
     const int64_t qo = (int64_t)b * a.q_bs + (int64_t)(q0 - a.qoff) * ldq + (int64_t)h * DH;
-    dma_tile64_w8<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
-    dma_tile64_w8<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
+    if (a.e - q0 >= 64) {  // wave-uniform
+      dma_tile64_full<DH, 8>(qd, a.Q + qo, qoff, wave);
+      dma_tile64_full<DH, 8>(od, a.dO + qo, qoff, wave);
+    } else {
+      dma_tile64_w8<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
+      dma_tile64_w8<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
+    }
     if (wave < 4)
       dma_f32x16(ld_, a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (q0 - a.s), wave, lane);
     else
