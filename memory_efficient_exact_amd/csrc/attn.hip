@@ -591,18 +591,26 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lq, const LdsOff<DH>
 template <int DH>
 __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
   constexpr int NB = DH / 32, TB = 64 * DH * 2;
-  __shared__ __attribute__((aligned(16))) char Kt[2 * TB];  // 128 keys
-  __shared__ __attribute__((aligned(16))) char Vt[2 * TB];
-  __shared__ __attribute__((aligned(16))) char Q0[TB];
-  __shared__ __attribute__((aligned(16))) char O0[TB];  // dO tile
-  __shared__ __attribute__((aligned(16))) char Q1[TB];
-  __shared__ __attribute__((aligned(16))) char O1[TB];
-  __shared__ __attribute__((aligned(16))) float L0[64], E0[64], L1[64], E1[64];
+  // One LDS array, laid out so that every fragment read is a lane register
+  // plus an immediate below 64 KB: the Q / dO double buffers first (read
+  // 48 times per tile), then K and V of the block's 128 keys (their base is
+  // folded into the lane offsets of lk), then the LSE / Delta rows.
+  __shared__ __attribute__((aligned(16))) char smem[8 * TB + 4 * 64 * sizeof(float)];
+  char* const Q0 = smem;
+  char* const O0 = smem + TB;  // dO tile
+  char* const Q1 = smem + 2 * TB;
+  char* const O1 = smem + 3 * TB;
+  char* const Kt = smem + 4 * TB;  // 128 keys
+  char* const Vt = smem + 6 * TB;
+  float* const L0 = reinterpret_cast<float*>(smem + 8 * TB);
+  float* const E0 = L0 + 64;
+  float* const L1 = L0 + 128;
+  float* const E1 = L0 + 192;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave & 3, qh = wave >> 2;
   const KBlock kbk = k_block(a.Hkv);
   const int kv = kbk.kv, b = blockIdx.z;
-  const LdsOff<DH> lq(lane, (wave >> 2) * 32), lk(lane, (wave & 3) * 32);
+  const LdsOff<DH> lq(lane, (wave >> 2) * 32), lk(lane, 4 * TB / (2 * DH) + (wave & 3) * 32);
   const int kbase = kbk.kblk * 128;
   const int kw = kbase + kg * 32;
   const int kcol = kw + (lane & 31);  // this lane's key (result column)
@@ -678,7 +686,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
     // key's limit; those wholly after the keys and before every key's limit
     // need no mask
     if (qw + 31 >= kw && qw < wq_hi)
-      dkdv_tile<DH>(lq, lk, Kt, Vt, qt, ot, ls, dl, qrow, q0, kcol, qlim, lane, c2,
+      dkdv_tile<DH>(lq, lk, smem, smem + 2 * TB, qt, ot, ls, dl, qrow, q0, kcol, qlim, lane, c2,
                     !(qw >= kw + 31 && qw + 32 <= wq_lo), dk, dv);
   };
   if (n > 0) issue(Q0, O0, L0, E0);
