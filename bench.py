@@ -667,6 +667,8 @@ def main():
         cfg["T"] = args.T
     if args.dw_group:
         cfg["dw_group"] = args.dw_group
+    # a counter record describes the workload's own shapes only
+    own_shapes = not (args.D or args.D_lm or args.T or args.dw_group)
     n_valid = None
     if cfg["kind"] == "lmhead":
         step, flops, inp, n_valid = lmhead_setup(cfg, dev)
@@ -732,13 +734,14 @@ def main():
         ach = k["flops"] / (k["ms"] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dtype],
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dtype], 4),
-                "traffic": measured_traffic(cfg["name"], name),
+                "traffic": measured_traffic(cfg["name"], name) if own_shapes else None,
                 "kernel": name, "avg_launch_ms": round(k["ms"] / k["launches"], 4),
                 "flops_per_launch": k["flops"] / k["launches"]}
     else:
         ach = k["bytes"] / (k["ms"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(cfg["name"], name),
+                "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(cfg["name"], name) if own_shapes else None,
                 "kernel": name,
                 "avg_launch_ms": round(k["ms"] / k["launches"], 4),
                 "bytes_per_launch": k["bytes"] / k["launches"]}
