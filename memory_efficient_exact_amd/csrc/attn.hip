@@ -56,6 +56,31 @@ __device__ __forceinline__ int swz(int r) {
 
 #define SBP_AS1 __attribute__((address_space(1)))
 
+// LDS DMA as inline assembly: global_load_lds_dwordx4, lane l's 16 bytes
+// landing at M0 + 16 l.  Issued this way the compiler does not track the
+// LDS writes.  It could not tell a tile's fragment reads from the next tile's
+// fill in flight (one LDS array, computed offsets), and would wait for that
+// fill before the tile's first read, exposing its whole latency every tile.
+// The kernels order fills and reads themselves: dma_barrier before a buffer
+// is read, a full wait before LDS is reused for anything else.  s_nop 4: the
+// wait states gfx9 needs between an SGPR written by a vector instruction (a
+// readfirstlane) and a memory instruction that reads it; they also cover the
+// one an M0 write needs before an LDS DMA.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)p;  // low half of a generic LDS address
+}
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// uniform 64-bit base plus a per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 // DMA rows [0, 64) of a [rows][DH] bf16 tile (global row pitch ld elements)
 // into a swizzled LDS tile: each 1 KB global_load_lds covers 1024 / (2 DH)
 // rows, lane i filling 16-byte slot i, so the swizzle is applied to the
@@ -80,9 +105,7 @@ __device__ __forceinline__ void dma_tile64(char* lds, const bf16_t* __restrict__
 // aligned, in bounds) with lanes 0..3: four waves fetch one row together, so
 // that every wave issues the same number of DMAs.
 __device__ __forceinline__ void dma_f32x16(float* lds, const float* __restrict__ src, int q, int lane) {
-  if (lane < 4)
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + q * 16 + lane * 4),
-                                     (SBP_LDS void*)(lds + q * 16), 16, 0, 0);
+  if (lane < 4) dma16(src + q * 16 + lane * 4, lds_u32(lds + q * 16));
 }
 
 // Double-buffer hand-over.  The DMA writes of a tile are counted by each
@@ -120,11 +143,8 @@ struct Dma64Off {
 template <int DH, int NW>
 __device__ __forceinline__ void dma_tile64_full(char* lds, const bf16_t* __restrict__ src, const Dma64Off<DH, NW>& o,
                                                 int wave) {
-  const char* base = reinterpret_cast<const char*>(src);
 #pragma unroll
-  for (int j = 0; j < Dma64Off<DH, NW>::PER; ++j)
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(base + o.off[j]),
-                                     (SBP_LDS void*)(lds + (wave + NW * j) * 1024), 16, 0, 0);
+  for (int j = 0; j < Dma64Off<DH, NW>::PER; ++j) dma16_s(src, o.off[j], lds_u32(lds + (wave + NW * j) * 1024));
 }
 
 // Block -> work mapping for the 8 XCDs.  Workgroups are dispatched
@@ -488,8 +508,7 @@ __device__ __forceinline__ void dma_tile64_w8(char* lds, const bf16_t* __restric
     const int r = i * RPI + rr;
     const int c = pc ^ swz<DH>(r);
     const int gr = r < nvalid ? r : nvalid - 1;
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + (int64_t)gr * ld + c * 8),
-                                     (SBP_LDS void*)(lds + i * 1024), 16, 0, 0);
+    dma16(src + (int64_t)gr * ld + c * 8, lds_u32(lds + i * 1024));
   }
 }
 
