@@ -514,15 +514,18 @@ __device__ __forceinline__ void dma_tile64_w8(char* lds, const bf16_t* __restric
 
 // Softmax step of a dK/dV tile: P = exp(s S - LSE), dS = P (dP - Delta) in
 // place; elements 4j..4j+3 are rows 8j + 4(l/32) + 0..3 of the wave's 32
-// queries.  MASK zeroes the pairs a query does not see.
+// queries.  MASK zeroes the pairs a query does not see.  The LSE / Delta rows
+// of j = 0, 1 come in registers (read during the last score step), those of
+// j = 2, 3 from the LDS rows ls / dl.
 template <bool MASK>
-__device__ __forceinline__ void dkdv_softmax(f32x16_t& sp, f32x16_t& dp, const float* ls, const float* dl,
-                                             int qrow, int q0, int kcol, int qlim, int lane, float c2) {
+__device__ __forceinline__ void dkdv_softmax(f32x16_t& sp, f32x16_t& dp, const float4 (&l4s)[2],
+                                             const float4 (&d4s)[2], const float* ls, const float* dl, int qrow,
+                                             int q0, int kcol, int qlim, int lane, float c2) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r0 = qrow + 8 * j + 4 * (lane >> 5);
-    const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
-    const float4 d4 = *reinterpret_cast<const float4*>(dl + r0);
+    const float4 l4 = j < 2 ? l4s[j & 1] : *reinterpret_cast<const float4*>(ls + r0);
+    const float4 d4 = j < 2 ? d4s[j & 1] : *reinterpret_cast<const float4*>(dl + r0);
     const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv_[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -559,6 +562,15 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lq, const LdsOff<DH>
   constexpr int NB = DH / 32, KS = DH / 16;
   // S = Q K^T and dP = dO V^T: [32 queries x 32 keys], fragments one step ahead
   f32x16_t sp = f32x16_t{}, dp = f32x16_t{};
+  // LSE / Delta rows of j = 0, 1, read in the last score step (into the
+  // fragment registers it frees) so that the softmax does not start on an LDS
+  // wait; reading all four there spills
+  float4 l4s[2], d4s[2];
+  auto ldle = [&](int j) {
+    const int r0 = qrow + 8 * j + 4 * (lane >> 5);
+    l4s[j] = *reinterpret_cast<const float4*>(ls + r0);
+    d4s[j] = *reinterpret_cast<const float4*>(dl + r0);
+  };
   {
     uint4 fq[2], fk[2], fo[2], fv[2];
     auto ld = [&](int ks) {
@@ -570,7 +582,12 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lq, const LdsOff<DH>
     ld(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) ld(ks + 1);
+      if (ks + 1 < KS) {
+        ld(ks + 1);
+      } else {
+        ldle(0);
+        ldle(1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       sp = mma(fq[ks & 1], fk[ks & 1], sp);
       dp = mma(fo[ks & 1], fv[ks & 1], dp);
@@ -578,9 +595,9 @@ __device__ __forceinline__ void dkdv_tile(const LdsOff<DH>& lq, const LdsOff<DH>
     }
   }
   if (mask)  // wave-uniform
-    dkdv_softmax<true>(sp, dp, ls, dl, qrow, q0, kcol, qlim, lane, c2);
+    dkdv_softmax<true>(sp, dp, l4s, d4s, ls, dl, qrow, q0, kcol, qlim, lane, c2);
   else
-    dkdv_softmax<false>(sp, dp, ls, dl, qrow, q0, kcol, qlim, lane, c2);
+    dkdv_softmax<false>(sp, dp, l4s, d4s, ls, dl, qrow, q0, kcol, qlim, lane, c2);
   // dV[key, dh] += P^T[key, q] dO[q, dh];  dK[key, dh] += dS^T[key, q] Q[q, dh]
   {
     uint4 tq[2], to[2];
