@@ -54,15 +54,15 @@ __device__ __forceinline__ int swz(int r) {
   return DH == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-#define SBP_AS1 __attribute__((address_space(1)))
-
 // LDS DMA as inline assembly: global_load_lds_dwordx4, lane l's 16 bytes
 // landing at M0 + 16 l.  Issued this way the compiler does not track the
-// LDS writes.  It could not tell a tile's fragment reads from the next tile's
-// fill in flight (one LDS array, computed offsets), and would wait for that
-// fill before the tile's first read, exposing its whole latency every tile.
-// The kernels order fills and reads themselves: dma_barrier before a buffer
-// is read, a full wait before LDS is reused for anything else.  s_nop 4: the
+// LDS writes.  Tracked, it could not tell a tile's fragment reads from the
+// next tile's fill in flight (one LDS array, computed offsets) and waited for
+// that fill before the tile's first read, exposing its whole latency every
+// tile; and any fill it tracked made it wait for every outstanding LDS read
+// (lgkmcnt(0)) before each MFMA, where a count of the reads still needed
+// suffices.  The kernels order fills and reads themselves: dma_barrier before
+// a buffer is read, a full wait before LDS is reused for anything else.  s_nop 4: the
 // wait states gfx9 needs between an SGPR written by a vector instruction (a
 // readfirstlane) and a memory instruction that reads it; they also cover the
 // one an M0 write needs before an LDS DMA.
@@ -96,8 +96,7 @@ __device__ __forceinline__ void dma_tile64(char* lds, const bf16_t* __restrict__
     const int r = i * RPI + rr;
     const int c = pc ^ swz<DH>(r);
     const int gr = r < nvalid ? r : nvalid - 1;
-    __builtin_amdgcn_global_load_lds((const SBP_AS1 void*)(src + (int64_t)gr * ld + c * 8),
-                                     (SBP_LDS void*)(lds + i * 1024), 16, 0, 0);
+    dma16(src + (int64_t)gr * ld + c * 8, lds_u32(lds + i * 1024));
   }
 }
 
@@ -112,9 +111,7 @@ __device__ __forceinline__ void dma_f32x16(float* lds, const float* __restrict__
 // wave's own vmcnt, so every wave first waits for its share of the tile about
 // to be read, and the barrier then makes all shares visible (it also ends
 // every wave's reads of the buffer about to be refilled).  The wave index is
-// made wave-uniform (readfirstlane) so that the DMA issue branches are scalar
-// and the compiler does not wait on the fresh refill before reading the other
-// buffer.
+// made wave-uniform (readfirstlane) so that the DMA issue branches are scalar.
 __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -268,9 +265,8 @@ __device__ __forceinline__ SeqRange seq_range(const AttnArgs& a, int q0, int qw,
 
 // ---------------------------------------------------------------------------
 // Forward statistics.  Block: 4 waves, 128 queries (32 per wave), one q head.
-// Key/value tiles of 64 rows are double-buffered in two distinct LDS arrays
-// (so the compiler can tell the DMA into one from the reads of the other):
-// tile t+1 is fetched while tile t is used.
+// Key/value tiles of 64 rows are double-buffered in two LDS arrays: tile t+1
+// is fetched while tile t is used.
 // ---------------------------------------------------------------------------
 template <int DH, bool MASK>
 __device__ __forceinline__ void fwd_tile(const LdsOff<DH>& lo, const char* kt, const char* vt, int k0, int qcol,
