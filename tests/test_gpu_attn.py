@@ -34,6 +34,9 @@ def _ref(inp, scale):
     (1, 64, 2, 2, 64, 64),      # D = T: one query per chunk
     (1, 1000, 4, 4, 128, 7),    # MHA, several key tiles per chunk
     (1, 1, 2, 1, 64, 1),        # a single token
+    (1, 700, 6, 3, 128, 2),     # Hkv = 3 (kv heads do not divide the 8 XCDs)
+    (1, 520, 16, 2, 64, 2),     # G = 8 query heads per kv head
+    (1, 400, 16, 16, 64, 3),    # Hkv = 16 > 8 XCDs
 ])
 def test_parity(B, T, Hq, Hkv, dh, D):
     inp = synthetic.attn_inputs(B, T, Hq, Hkv, dh, "bf16", seed=T + Hq + dh + D)
