@@ -690,26 +690,39 @@ __global__ __launch_bounds__(512) void attn_dkdv_kernel(AttnArgs a) {
       ++c.hh;
     }
   };
-  Cur ci{0, 0}, ct{0, 0};
+  Cur ct{0, 0};
   const Dma64Off<DH, 8> qoff(ldq, wave, lane);
-  int fetched = 0;  // tiles whose fetch has been issued
+  // The fetch cursor carries its Q / dO offset and its statistics row (LSE
+  // for waves 0-3, Delta for 4-7): a tile step adds 64 rows, a head step
+  // goes back to the first tile and on by one head.
+  int fjq = 0, fq0 = a.s + j0 * 64, fetched = 0;  // fetched: tiles whose fetch has been issued
+  int64_t fqo = (int64_t)b * a.q_bs + (int64_t)(fq0 - a.qoff) * ldq + (int64_t)kv * a.G * DH;
+  const float* fst = wave < 4 ? a.lse + (int64_t)b * a.lse_sb + (int64_t)kv * a.G * a.lse_sh + j0 * 64
+                              : a.delta + (int64_t)b * a.dl_sb + (int64_t)kv * a.G * a.dl_sh + j0 * 64;
+  const int64_t fst_h = (wave < 4 ? a.lse_sh : a.dl_sh) - (int64_t)(nqt - 1) * 64;
+  const int64_t fqo_h = (int64_t)DH - (int64_t)(nqt - 1) * 64 * ldq;
   auto issue = [&](char* qd, char* od, float* ld_, float* dd) {
-    if (fetched > 0 && fetched < n) advance(ci);
-    ++fetched;
-    const int q0 = a.s + (j0 + ci.jq) * 64;
-    const int h = kv * a.G + ci.hh;
-    const int64_t qo = (int64_t)b * a.q_bs + (int64_t)(q0 - a.qoff) * ldq + (int64_t)h * DH;
-    if (a.e - q0 >= 64) {  // wave-uniform
-      dma_tile64_full<DH, 8>(qd, a.Q + qo, qoff, wave);
-      dma_tile64_full<DH, 8>(od, a.dO + qo, qoff, wave);
-    } else {
-      dma_tile64_w8<DH>(qd, a.Q + qo, ldq, a.e - q0, wave, lane);
-      dma_tile64_w8<DH>(od, a.dO + qo, ldq, a.e - q0, wave, lane);
+    if (fetched > 0 && fetched < n) {
+      if (++fjq == nqt) {
+        fjq = 0;
+        fq0 = a.s + j0 * 64;
+        fqo += fqo_h;
+        fst += fst_h;
+      } else {
+        fq0 += 64;
+        fqo += 64 * ldq;
+        fst += 64;
+      }
     }
-    if (wave < 4)
-      dma_f32x16(ld_, a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (q0 - a.s), wave, lane);
-    else
-      dma_f32x16(dd, a.delta + (int64_t)b * a.dl_sb + (int64_t)h * a.dl_sh + (q0 - a.s), wave - 4, lane);
+    ++fetched;
+    if (a.e - fq0 >= 64) {  // wave-uniform
+      dma_tile64_full<DH, 8>(qd, a.Q + fqo, qoff, wave);
+      dma_tile64_full<DH, 8>(od, a.dO + fqo, qoff, wave);
+    } else {
+      dma_tile64_w8<DH>(qd, a.Q + fqo, ldq, a.e - fq0, wave, lane);
+      dma_tile64_w8<DH>(od, a.dO + fqo, ldq, a.e - fq0, wave, lane);
+    }
+    dma_f32x16(wave < 4 ? ld_ : dd, fst, wave & 3, lane);
   };
   auto tile = [&](const char* qt, const char* ot, const float* ls, const float* dl) {
     const int q0 = a.s + (j0 + ct.jq) * 64, qw = q0 + qrow;
