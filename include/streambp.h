@@ -374,19 +374,21 @@ sbp_status sbp_layer_fwd(const sbp_layer_desc* desc, const int32_t* cu_seqlens, 
  * the LM head over D_lm chunks (never the [T, V] logits), the final norm's
  * backward, then every layer's streamed backward over D_layer chunks, last
  * layer first.  Transient memory: the larger of the LM-head and layer
- * workspaces plus three [T, d] bf16 buffers.
+ * workspaces plus three [T, d] buffers of the dtype.
  *
- * desc        layer shape (bf16 only), rope_theta included
+ * desc        layer shape, rope_theta included; desc->dtype SBP_BF16 or
+ *             SBP_F32 (fp32: the activations, weights, g_final, W_lm and dx0
+ *             fp32, every product in fp32, as in the fp32 modes of (1), (3))
  * n_layers    L >= 0 (0: final norm under the LM head)
  * cu_seqlens  packed-sequence boundaries as in 2b, or NULL (one causal row)
- * x_layers    host array of L + 1 device pointers [T, d] bf16: the input of
- *             every layer, then the last layer's output
+ * x_layers    host array of L + 1 device pointers [T, d] dtype: the input
+ *             of every layer, then the last layer's output
  * layers      host array of L weight structs (as in 3); grads host array of
  *             L grad structs (fp32, accumulate semantics)
- * g_final     [d] bf16; dg_final [d] fp32 out (accumulate semantics)
- * W_lm        [V, d] bf16; dW_lm [V, d] fp32 out (accumulate semantics)
+ * g_final     [d] dtype; dg_final [d] fp32 out (accumulate semantics)
+ * W_lm        [V, d] dtype; dW_lm [V, d] fp32 out (accumulate semantics)
  * targets, weights, reduction, loss, token_loss   as in (1)
- * dx0         [T, d] bf16 out; must not alias any x_layers entry
+ * dx0         [T, d] dtype out; must not alias any x_layers entry
  * Errors: as in (1) and (3); argument errors are returned before any launch.
  * ---------------------------------------------------------------------- */
 sbp_status sbp_model_bwd_workspace_size(const sbp_layer_desc* desc, int32_t n_layers,

@@ -9,14 +9,15 @@
 //   loss = CE(h W^T; targets, weights)
 // Given the layer inputs x_0 .. x_{L-1} and the last output x_L (a forward
 // pass with sbp_layer_fwd keeps them), the call runs:
-//   h = RMSNorm(x_L; g_f)                              one [T, d] bf16 buffer
+//   h = RMSNorm(x_L; g_f)                              one [T, d] buffer
 //   LM head + CE over D_lm chunks -> loss, dh, dW      (sbp_lmhead_ce_fwd_bwd)
 //   dx_L = RMSNorm'(dh), dg_f +=                       D_layer chunks
 //   dx_l = Layer_l'(x_l, dx_{l+1}), l = L-1 .. 0       (sbp_layer_bwd)
-// Upstream gradients alternate between two [T, d] bf16 buffers; the LM-head
-// and layer calls run one after another on the caller's stream and share one
-// workspace region, so the call's transient memory is the larger of theirs
-// plus three [T, d] bf16 buffers.
+// Activations and upstream gradients are of the call's dtype (bf16, or fp32
+// throughout); the upstream gradients alternate between two [T, d] buffers.
+// The LM-head and layer calls run one after another on the caller's stream
+// and share one workspace region, so the call's transient memory is the
+// larger of theirs plus three [T, d] buffers.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,22 +25,25 @@ namespace sbp {
 namespace {
 
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+inline size_t dtype_size(int dtype) { return dtype == SBP_F32 ? sizeof(float) : sizeof(bf16_t); }
 
 struct ModelWs {
-  bf16_t *h, *gA, *gB;
+  char *h, *gA, *gB;  // [T, d] of the call's dtype
   float *rinv, *dn, *gpart;
   char* sub;
 };
 
-size_t model_plan(int64_t T, int64_t d, int64_t Tcm, size_t sub_bytes, char* base, ModelWs* w) {
+// es: bytes per element of the dtype.  dn (the final norm's upstream
+// gradient of a chunk in fp32) is needed only when dh is bf16.
+size_t model_plan(int64_t T, int64_t d, int64_t Tcm, size_t es, size_t sub_bytes, char* base, ModelWs* w) {
   WsPlan P;
   P.base = base;
   ModelWs x;
-  x.h = (bf16_t*)P.take(sizeof(bf16_t) * T * d);
-  x.gA = (bf16_t*)P.take(sizeof(bf16_t) * T * d);
-  x.gB = (bf16_t*)P.take(sizeof(bf16_t) * T * d);
+  x.h = (char*)P.take(es * T * d);
+  x.gA = (char*)P.take(es * T * d);
+  x.gB = (char*)P.take(es * T * d);
   x.rinv = (float*)P.take(sizeof(float) * T);
-  x.dn = (float*)P.take(sizeof(float) * Tcm * d);
+  x.dn = es == sizeof(float) ? nullptr : (float*)P.take(sizeof(float) * Tcm * d);
   x.gpart = (float*)P.take(sizeof(float) * gain_grad_splits(Tcm) * d);
   x.sub = (char*)P.take(sub_bytes);
   if (w) *w = x;
@@ -50,7 +54,7 @@ size_t model_plan(int64_t T, int64_t d, int64_t Tcm, size_t sub_bytes, char* bas
 sbp_status model_sub_bytes(const sbp_layer_desc* desc, bool packed, int64_t V, int32_t D_lm,
                            int32_t D_layer, size_t* out) {
   size_t lm = 0, lay = 0;
-  sbp_status st = sbp_lmhead_ce_workspace_size(desc->T, desc->d, V, D_lm, SBP_BF16, &lm);
+  sbp_status st = sbp_lmhead_ce_workspace_size(desc->T, desc->d, V, D_lm, desc->dtype, &lm);
   if (st != SBP_OK) return st;
   st = packed ? sbp_layer_bwd_packed_workspace_size(desc, D_layer, &lay)
               : sbp_layer_bwd_workspace_size(desc, D_layer, &lay);
@@ -64,7 +68,8 @@ sbp_status model_check(const sbp_layer_desc* desc, int32_t n_layers, int64_t V, 
   if (!desc) return set_error(SBP_ERR_INVALID_ARG, "desc is NULL");
   if (n_layers < 0 || n_layers > 4096) return set_error(SBP_ERR_INVALID_ARG, "n_layers must be in [0, 4096] (got %d)", n_layers);
   if (V < 1) return set_error(SBP_ERR_INVALID_ARG, "V must be >= 1");
-  if (desc->dtype != SBP_BF16) return set_error(SBP_ERR_UNSUPPORTED, "the model backward is implemented for bf16 only");
+  if (desc->dtype != SBP_BF16 && desc->dtype != SBP_F32)
+    return set_error(SBP_ERR_INVALID_ARG, "dtype must be SBP_BF16 or SBP_F32 (got %d)", desc->dtype);
   if (D_lm < 1 || D_lm > desc->T || D_layer < 1 || D_layer > desc->T)
     return set_error(SBP_ERR_INVALID_ARG, "need 1 <= D_lm, D_layer <= T");
   return SBP_OK;
@@ -85,7 +90,8 @@ extern "C" sbp_status sbp_model_bwd_workspace_size(const sbp_layer_desc* desc, i
   size_t sub = 0;
   st = model_sub_bytes(desc, packed != 0, V, D_lm, D_layer, &sub);
   if (st != SBP_OK) return st;
-  *bytes = model_plan(desc->T, desc->d, max_chunk_len(desc->T, D_layer), sub, nullptr, nullptr);
+  *bytes = model_plan(desc->T, desc->d, max_chunk_len(desc->T, D_layer), dtype_size(desc->dtype), sub,
+                      nullptr, nullptr);
   return SBP_OK;
 }
 
@@ -120,12 +126,15 @@ extern "C" sbp_status sbp_model_bwd(const sbp_layer_desc* desc, int32_t n_layers
   st = model_sub_bytes(desc, packed, V, D_lm, D_layer, &sub);
   if (st != SBP_OK) return st;
   const int64_t T = desc->T, d = desc->d;
+  const int dt = desc->dtype;
+  const size_t es = dtype_size(dt);
   const int64_t Tcm = max_chunk_len(T, D_layer);
-  const size_t need = model_plan(T, d, Tcm, sub, nullptr, nullptr);
+  const size_t need = model_plan(T, d, Tcm, es, sub, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return set_error(SBP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   ModelWs W;
-  model_plan(T, d, Tcm, sub, (char*)ws, &W);
+  model_plan(T, d, Tcm, es, sub, (char*)ws, &W);
+  auto row = [&](const void* p, int64_t r) { return (const char*)p + (int64_t)es * r * d; };
 #define SBP_TRY(e_)                  \
   do {                               \
     sbp_status _s = (e_);            \
@@ -133,26 +142,32 @@ extern "C" sbp_status sbp_model_bwd(const sbp_layer_desc* desc, int32_t n_layers
   } while (0)
 
   // final norm and the LM head; dh lands in gA
-  const bf16_t* xL = (const bf16_t*)x_layers[n_layers];
-  SBP_TRY(rmsnorm_fwd(xL, d, g_final, T, d, desc->eps, W.h, d, W.rinv, str));
-  SBP_TRY(sbp_lmhead_ce_fwd_bwd(W.h, W_lm, targets, weights, T, d, V, D_lm, SBP_BF16, reduction,
+  const void* xL = x_layers[n_layers];
+  SBP_TRY(rmsnorm_fwd(xL, d, g_final, T, d, desc->eps, W.h, d, W.rinv, str, dt));
+  SBP_TRY(sbp_lmhead_ce_fwd_bwd(W.h, W_lm, targets, weights, T, d, V, D_lm, dt, reduction,
                                 accumulate, loss, token_loss, W.gA, dW_lm, W.sub, sub, stream));
-  // dx_L = RMSNorm'(dh) into gB (into dx0 if there are no layers), dg_f +=
-  bf16_t* up = n_layers > 0 ? W.gB : (bf16_t*)dx0;
+  // dx_L = RMSNorm'(dh) into gB (into dx0 if there are no layers), dg_f +=;
+  // the norm's backward takes dh in fp32: converted per chunk from bf16, or
+  // read in place in fp32 mode
+  char* up = n_layers > 0 ? W.gB : (char*)dx0;
   for (int32_t c = 0; c < D_layer; ++c) {
     int64_t s0, e0;
     chunk_bounds(T, D_layer, c, &s0, &e0);
     const int64_t Tc = e0 - s0;
-    SBP_TRY(rows_to_f32(W.gA + s0 * d, d, Tc, d, W.dn, d, str));
-    SBP_TRY(rmsnorm_bwd(xL + s0 * d, d, g_final, W.dn, d, W.rinv + s0, nullptr, 0, Tc, d,
-                        up + s0 * d, d, str));
-    SBP_TRY(gain_grad(W.dn, d, xL + s0 * d, d, W.rinv + s0, Tc, d, dg_final,
-                      c == 0 ? (accumulate ? 1 : 0) : 1, W.gpart, str));
+    const float* dn = (const float*)row(W.gA, s0);
+    if (dt == SBP_BF16) {
+      SBP_TRY(rows_to_f32(row(W.gA, s0), d, Tc, d, W.dn, d, str));
+      dn = W.dn;
+    }
+    SBP_TRY(rmsnorm_bwd(row(xL, s0), d, g_final, dn, d, W.rinv + s0, nullptr, 0, Tc, d,
+                        (void*)row(up, s0), d, str, dt));
+    SBP_TRY(gain_grad(dn, d, row(xL, s0), d, W.rinv + s0, Tc, d, dg_final,
+                      c == 0 ? (accumulate ? 1 : 0) : 1, W.gpart, str, dt));
   }
   // layers, last to first
-  bf16_t* other = W.gA;
+  char* other = W.gA;
   for (int32_t l = n_layers - 1; l >= 0; --l) {
-    bf16_t* out = l == 0 ? (bf16_t*)dx0 : other;
+    char* out = l == 0 ? (char*)dx0 : other;
     if (packed)
       SBP_TRY(sbp_layer_bwd_packed(desc, cu_seqlens, nseq, x_layers[l], up, &layers[l], D_layer,
                                    accumulate, out, &grads[l], W.sub, sub, stream));

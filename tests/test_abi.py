@@ -324,6 +324,14 @@ def test_model_bwd_argument_errors():
     assert lib.sbp_layer_bwd_workspace_size(C.byref(desc), 2, C.byref(lay)) == 0
     # three [T, d] bf16 buffers plus the inner calls' workspace (at least a layer's)
     assert out.value >= lay.value + 3 * 64 * 64 * 2
+    # fp32 mode: three fp32 buffers, and the fp32 layer's (larger) workspace
+    d32 = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 0, 1e4)
+    o32, l32 = C.c_size_t(0), C.c_size_t(0)
+    assert lib.sbp_model_bwd_workspace_size(C.byref(d32), L, 0, 100, 2, 2, C.byref(o32)) == 0
+    assert lib.sbp_layer_bwd_workspace_size(C.byref(d32), 2, C.byref(l32)) == 0
+    assert o32.value >= l32.value + 3 * 64 * 64 * 4
+    bad = _lib.LayerDesc(64, 64, 4, 2, 64, 128, 1e-6, 2, 1e4)
+    assert lib.sbp_model_bwd_workspace_size(C.byref(bad), L, 0, 100, 2, 2, C.byref(o32)) == _lib.SBP_ERR_INVALID_ARG
 
 
 def test_layer_qk_norm_arguments():

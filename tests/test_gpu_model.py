@@ -2,7 +2,7 @@
 then sbp_model_bwd) against the fp64 oracle's model backward on the same
 inputs (bf16 with fp32 accumulation): normwise max|gpu - ref| / max|ref| <=
 2e-2 on dx0, the final gain, the LM head and every layer gradient; the loss
-relative to max(|L|, (1/N) sum |c_t| l_t)."""
+relative to max(|L|, (1/N) sum |c_t| l_t).  fp32 mode: 1e-4 normwise."""
 import numpy as np
 import pytest
 import torch
@@ -100,6 +100,36 @@ def test_qk_norm_parity():
     for l, g in enumerate(out[2]):
         for k in ("qn", "kn"):
             assert normwise(g[k].cpu().numpy(), ref[2][l][k]) <= TOL, (l, k)
+
+
+@pytest.mark.parametrize("L,T,D_lm,D_layer,theta,cu,qk", [
+    (2, 300, 3, 2, 1e4, None, False),                       # ragged chunks, rotary
+    (2, 257, 1, 257, 0.0, None, True),                       # one token per layer chunk, QK-norm
+    (1, 200, 2, 3, 5e5, [0, 70, 71, 200], False),            # packed sequences
+    (0, 96, 96, 2, 0.0, None, False),                        # no layers: norm + head
+])
+def test_parity_fp32(L, T, D_lm, D_layer, theta, cu, qk):
+    """fp32 mode (every tensor and product fp32): the backward at the layer
+    inputs the fp32 chunked forward gives, against the oracle's backward at
+    those inputs (exact upcast), within 1e-4 normwise."""
+    M = synthetic.model_inputs(T, 128, 4, 2, 64, 256, 500, L, "f32", seed=11 * T + L,
+                               w_std=0.05, gain_std=0.1, rope_theta=theta, ignore_frac=0.1,
+                               lm_w_std=0.1, qk_norm=qk)
+    out = _gpu(M, D_lm, D_layer, cu)
+    xs = [synthetic.to_f64(x.cpu()) for x in _gpu.xs]
+    f = synthetic.to_f64
+    ref = oracle.model_bwd_at(xs, [{k: f(v) for k, v in w.items()} for w in M.layers],
+                              f(M.g_final), f(M.W), M.targets.numpy(), Hq=M.Hq, Hkv=M.Hkv,
+                              dh=M.dh, eps=M.eps, cu_seqlens=cu, rope_theta=M.rope_theta)
+    loss, dx0, grads, dgf, dW, _ = out
+    errs = {"loss": abs(loss.item() - ref[0]) / abs(ref[0]), "dx0": normwise(dx0.cpu().numpy(), ref[1]),
+            "dg_final": normwise(dgf.cpu().numpy(), ref[3]), "dW_lm": normwise(dW.cpu().numpy(), ref[4])}
+    for l, g in enumerate(grads):
+        for k in g:
+            errs[f"{l}.{k}"] = normwise(g[k].cpu().numpy(), ref[2][l][k])
+    print("errors:", {k: f"{v:.2e}" for k, v in sorted(errs.items())}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= 1e-4}
+    assert not bad, errs
 
 
 def test_accumulate_adds_into_every_gradient():
