@@ -149,13 +149,19 @@ __device__ __forceinline__ void dma_tile64_full(char* lds, const bf16_t* __restr
 // taken from the low part of the linear id: when Hkv divides 8 every block
 // of one kv head runs on the same XCD and the K / V (or Q / dO) it streams
 // stays in that XCD's L2.  Query blocks are issued heaviest (most keys)
-// first.
+// first.  A grid that fits the chip in one round at two blocks per CU (512
+// blocks or fewer) puts the first half of its blocks one per CU and the
+// second half into the CUs' second slots; that half is issued lightest
+// first, so that a CU's two blocks sum to about the same work.
 struct QBlock {
   int h, qblk;
 };
 __device__ __forceinline__ QBlock q_block(int Hkv, int G) {
   const int lin = blockIdx.x + gridDim.x * blockIdx.y;
-  const int kv = lin % Hkv, r = lin / Hkv;
+  const int kv = lin % Hkv;
+  int r = lin / Hkv;               // rank by work, heaviest first
+  const int R = (int)gridDim.x * G;
+  if (gridDim.x * gridDim.y * gridDim.z <= 512 && r >= R / 2) r = R / 2 + (R - 1 - r);
   return {kv * G + r % G, (int)gridDim.x - 1 - r / G};
 }
 struct KBlock {
