@@ -748,7 +748,7 @@ def main():
     kernels = {n: {"launches": v["launches"] // args.steps,
                    "ms_per_step": round(v["ms"] / args.steps, 3),
                    "tflops": round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1) if v["flops"] else None,
-                   "gbs": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1) if not v["flops"] else None}
+                   "gbs": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1) if v["bytes"] and not v["flops"] else None}
                for n, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
 
     out = {

@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 
 sbp_status fill_zero_f32(float* p, int64_t n, const int* when, hipStream_t st) {
   if (n <= 0) return SBP_OK;
-  ProfScope prof("fill_zero", st, 0.0, 4.0 * n);
+  // a conditional fill is credited no bytes: whether it writes is decided on
+  // the device (it returns at once unless *when != 0)
+  ProfScope prof("fill_zero", st, 0.0, when ? 0.0 : 4.0 * n);
   const unsigned grid = (unsigned)std::min<int64_t>(cdiv(n, 256), 8192);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, st, p, n, when);
   SBP_LAUNCH_CHECK();
