@@ -32,6 +32,11 @@
 
 namespace sbp {
 
+// Native vectors for the nontemporal loads and stores of the epilogues
+// (the builtins take no struct types).
+typedef float ntf4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int ntu2_t __attribute__((ext_vector_type(2)));
+
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
   static constexpr int EPC = 8;  // elements per 16-byte chunk
@@ -649,15 +654,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     // loaded two row blocks ahead (into two register sets), so that their
     // loads overlap the staging and stores of the blocks before them (1%
     // faster on the LM-head weight gradient than loading each block's own
-    // old values after staging it).
+    // old values after staging it).  C is read once and written once per
+    // launch, so both go nontemporal and do not evict the operand panels
+    // that other blocks of the launch still stream through L2 (LM-head
+    // weight gradient 2% faster).
     if (full && beta != 0.f) {  // wave-uniform
       float4 ob[2][16];
       auto ld = [&](int fm, float4 (&o)[16]) __attribute__((always_inline)) {
         const int64_t rc0 = (int64_t)(m0 + wm * WT + fm * 32 + (lane >> 5));
         const int c0 = n0 + wn * WT + (lane & 31) * 4;
 #pragma unroll
-        for (int bq = 0; bq < 16; ++bq)
-          o[bq] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + (rc0 + 2 * bq) * p.ldc + c0);
+        for (int bq = 0; bq < 16; ++bq) {
+          const ntf4_t t = __builtin_nontemporal_load(
+              reinterpret_cast<const ntf4_t*>(reinterpret_cast<const float*>(p.C) + (rc0 + 2 * bq) * p.ldc + c0));
+          o[bq] = make_float4(t.x, t.y, t.z, t.w);
+        }
       };
       ld(0, ob[0]);
       ld(1, ob[1]);
@@ -678,9 +689,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
           const int lr = bq * 2 + (lane >> 5);
           const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + (lane & 31) * 4]);
           const float4 o = ob[fm & 1][bq];
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + (rc0 + 2 * bq) * p.ldc + c0) =
-              make_float4(p.alpha * v4.x + beta * o.x, p.alpha * v4.y + beta * o.y,
-                          p.alpha * v4.z + beta * o.z, p.alpha * v4.w + beta * o.w);
+          const ntf4_t r = {p.alpha * v4.x + beta * o.x, p.alpha * v4.y + beta * o.y,
+                            p.alpha * v4.z + beta * o.z, p.alpha * v4.w + beta * o.w};
+          __builtin_nontemporal_store(r, reinterpret_cast<ntf4_t*>(reinterpret_cast<float*>(p.C) + (rc0 + 2 * bq) * p.ldc + c0));
         }
         if (fm + 2 < 4) ld(fm + 2, ob[fm & 1]);
         __builtin_amdgcn_wave_barrier();
@@ -878,7 +889,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
     }
     if constexpr (EPI == EPI_REL16_LSE) {
       // every value minus the max of its 64-column quarter, as fp16, in
-      // row-contiguous 8-byte stores (quarter maxima from the pass above)
+      // row-contiguous 8-byte stores (quarter maxima from the pass above);
+      // nontemporal: the chunk's logits are read back by the row kernel
+      // only after the whole launch
       __builtin_amdgcn_wave_barrier();
       const int q = (lane & 31) >> 4;  // the lane's quarter of the wave's 128 columns
       const int c0 = n0 + wn * WT + (lane & 31) * 4;
@@ -891,8 +904,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16_ring_kernel(GemmParams p)
         const float4 v4 = *reinterpret_cast<const float4*>(&W[lr * 128 + (lane & 31) * 4]);
         const float v[4] = {v4.x - mq, v4.y - mq, v4.z - mq, v4.w - mq};
         if (full || (row < p.M && vec_ok && c0 + 4 <= p.N)) {
-          *reinterpret_cast<uint2*>(C16 + (int64_t)row * p.ldc + c0) =
-              make_uint2(pk_f16(v[0], v[1]), pk_f16(v[2], v[3]));
+          const ntu2_t u = {pk_f16(v[0], v[1]), pk_f16(v[2], v[3])};
+          __builtin_nontemporal_store(u, reinterpret_cast<ntu2_t*>(C16 + (int64_t)row * p.ldc + c0));
         } else if (row < p.M) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
