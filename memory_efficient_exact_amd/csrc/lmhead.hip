@@ -76,10 +76,12 @@ LmShape lm_shape(int64_t T, int64_t d, int64_t V, int32_t D, int dtype, int G) {
   // dH GEMM: few output tiles, long K = V.  Split K so that the launch has
   // ~256 blocks, one per CU (the ring GEMM holds one block per CU, so more
   // splits only add fp32 partials to write and sum: measured, 8 splits cost
-  // 7% more GEMM time and 4x the partial traffic); a function of the shape
-  // only.
+  // 7% more GEMM time and 4x the partial traffic); no split once the tiles
+  // alone fill three quarters of the CUs (224 tiles at T_c = 4096, d = 3584:
+  // one round of whole-K tiles was 3.8% faster than two rounds of half-K
+  // partials); a function of the shape only.
   const int64_t tiles = cdiv(s.Tcm, 256) * cdiv(d, 256);
-  int64_t S = cdiv(256, tiles);
+  int64_t S = tiles >= 192 ? 1 : cdiv(256, tiles);
   S = std::max<int64_t>(1, std::min<int64_t>(S, 16));
   S = std::min<int64_t>(S, std::max<int64_t>(1, s.Vp / 512));
   s.S = (int)S;
